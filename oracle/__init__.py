@@ -1,0 +1,15 @@
+"""CPU oracle (f64) for the weight-dequantizing linear layer.
+
+TEST INFRASTRUCTURE: only ``tests/``, ``__graft_entry__.smoke()`` and the
+bench's CPU-baseline leg may import this package. The HIP library never calls
+it and shares no code with it.
+
+Pins (what checks the oracle against something other than itself) live in
+``tests/test_oracle_*.py``. Every function here is pinned; none is "parity
+unpinned".
+"""
+from .reference import (  # noqa: F401
+    FLAG_BIAS, FLAG_GELU, FLAG_RESIDUAL, QBLOCK, QBYTES, W_BF16, W_Q4_0, W_Q8_0,
+    bf16_bits_to_f64, decode, decode_bf16, decode_q4_0, decode_q8_0, encode_q8_0,
+    epilogue, f16_bits_to_f64, gelu_erf, linear, moe, weight_nbytes,
+)

@@ -1,0 +1,248 @@
+"""Plain f64 CPU oracle of the weight-dequantizing linear layer.
+
+TEST INFRASTRUCTURE. Only the tests, the package's smoke check and the
+bench's CPU-baseline leg may import or call this module; the product path
+never does. It shares no code with the HIP path and imports nothing from it.
+
+What it computes, written out from the pages it follows:
+
+* ``Y = epilogue(X . W^T + b)`` with X ``[n x k]``, W ``[m x k]``, Y ``[n x m]``
+  -- the kernel contract stated at the top of cortiq-engine
+  ``nemotron_audio.rs`` (``AE_WGSL``, the ``ae_gemm`` comment and its
+  ``GmP`` parameter block), with the epilogue of its ``ae_put``: add the bias
+  (flag 1), then erf-GELU (flag 2), then add the value already in Y (flag 4).
+  wavo ``gpu/mod.rs`` ``Epilogue`` (``Residual``/``GeluResidual``) describes
+  the same accumulate-into-output step.
+* Weights are decoded exactly before the product: bf16 is the upper half of
+  an f32 (``ae_gemm``'s weight-pair unpacking); Q8_0 is ``d * q`` with an f16
+  ``d`` and int8 ``q`` (wavo ``Gpu::upload_linear`` and the test helper
+  ``weights``); Q4_0 is ``d * (q - 8)`` with 4-bit ``q`` (format named by
+  hanzo-ml ``wgpu_backend.rs`` ``matvec_q4_0_gpu``; nibble order: low nibbles
+  are elements 0-15, high nibbles 16-31).
+* The MoE matvec of hanzo-ml ``moe_matvec_gpu``: for routed slot ``s`` and
+  output row ``r``, ``y[s, r] = sum_k W[ids[s], r, k] * x[s, k]`` over one
+  weight bank ``[E, m, k]``; with gate weights the slots of a token are summed,
+  each times its gate.
+
+Every step uses f64 and a plain library primitive (numpy matmul, scipy erf);
+nothing is blocked, fused or reordered. The error scale
+``S[t, j] = sum_k |x[t, k] * w[j, k]|`` that the acceptance bounds use is
+returned beside every result.
+"""
+from __future__ import annotations
+
+import numpy as np
+from scipy.special import erf
+
+W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
+FLAG_BIAS, FLAG_GELU, FLAG_RESIDUAL = 1, 2, 4
+QBLOCK = 32
+QBYTES = {W_Q8_0: 34, W_Q4_0: 18}
+
+
+# ---------------------------------------------------------------------------
+# Scalar formats
+# ---------------------------------------------------------------------------
+
+def f16_bits_to_f64(bits) -> np.ndarray:
+    """Value of IEEE-754 binary16 bit patterns: 1 sign, 5 exponent (bias 15), 10 fraction bits.
+
+    Written from the format's definition: normal numbers are
+    ``(-1)^s * 2^(e-15) * (1 + f/1024)``, subnormals (e = 0) are
+    ``(-1)^s * 2^-14 * f/1024``, e = 31 is infinity (f = 0) or NaN.
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    s = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 10) & 0x1F
+    f = (b & 0x3FF).astype(np.float64)
+    normal = s * np.ldexp(1.0 + f / 1024.0, (e - 15).astype(np.int64))
+    sub = s * np.ldexp(f / 1024.0, -14)
+    special = np.where(f == 0, s * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 31, special, normal))
+
+
+def bf16_bits_to_f64(bits) -> np.ndarray:
+    """Value of bfloat16 bit patterns: 1 sign, 8 exponent (bias 127), 7 fraction bits.
+
+    A bf16 is the upper half of an f32 (the ``ae_gemm`` weight unpack shifts it
+    into the high 16 bits), so it has f32's exponent range: normals are
+    ``(-1)^s * 2^(e-127) * (1 + f/128)``, subnormals ``(-1)^s * 2^-126 * f/128``.
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFFFF
+    s = np.where(b >> 15, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    normal = s * np.ldexp(1.0 + f / 128.0, (e - 127).astype(np.int64))
+    sub = s * np.ldexp(f / 128.0, -126)
+    special = np.where(f == 0, s * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 255, special, normal))
+
+
+# ---------------------------------------------------------------------------
+# Weight decode
+# ---------------------------------------------------------------------------
+
+def weight_nbytes(wtype: int, m: int, k: int) -> int:
+    if wtype == W_BF16:
+        return 2 * m * k
+    return QBYTES[wtype] * m * (k // QBLOCK)
+
+
+def _blocks(raw: np.ndarray, wtype: int, m: int, k: int) -> np.ndarray:
+    if k % QBLOCK:
+        raise ValueError(f"k = {k} is not a multiple of {QBLOCK}")
+    a = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)
+    need = weight_nbytes(wtype, m, k)
+    if a.size < need:
+        raise ValueError(f"weight has {a.size} bytes, needs {need}")
+    return a[:need].reshape(m, k // QBLOCK, QBYTES[wtype])
+
+
+def decode_q8_0(raw: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Q8_0 rows -> ``f64[m][k]``: block = little-endian f16 ``d``, then 32 int8 ``q``; w = d*q."""
+    blk = _blocks(raw, W_Q8_0, m, k)
+    d = f16_bits_to_f64(blk[:, :, 0].astype(np.int64) | (blk[:, :, 1].astype(np.int64) << 8))
+    q = blk[:, :, 2:].view(np.int8).astype(np.float64)
+    return (d[:, :, None] * q).reshape(m, k)
+
+
+def decode_q4_0(raw: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Q4_0 rows -> ``f64[m][k]``: block = LE f16 ``d``, then 16 bytes; w = d*(q-8).
+
+    Byte j of the 16 holds element j in its low nibble and element j+16 in its
+    high nibble.
+    """
+    blk = _blocks(raw, W_Q4_0, m, k)
+    d = f16_bits_to_f64(blk[:, :, 0].astype(np.int64) | (blk[:, :, 1].astype(np.int64) << 8))
+    qs = blk[:, :, 2:].astype(np.int64)
+    q = np.concatenate([qs & 0xF, qs >> 4], axis=2).astype(np.float64)
+    return (d[:, :, None] * (q - 8.0)).reshape(m, k)
+
+
+def decode_bf16(raw: np.ndarray, m: int, k: int) -> np.ndarray:
+    a = np.ascontiguousarray(raw).view(np.uint16).reshape(-1)
+    if a.size < m * k:
+        raise ValueError(f"weight has {a.size} bf16 values, needs {m * k}")
+    return bf16_bits_to_f64(a[: m * k]).reshape(m, k)
+
+
+def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray:
+    """Exact f64 values of an ``m x k`` weight (optionally only the listed rows)."""
+    if wtype == W_BF16:
+        a = np.ascontiguousarray(raw).view(np.uint16).reshape(m, k)
+        if rows is not None:
+            a = a[np.asarray(rows)]
+        return bf16_bits_to_f64(a)
+    per_row = QBYTES.get(wtype)
+    if per_row is None:
+        raise ValueError(f"unknown weight type {wtype}")
+    a = np.ascontiguousarray(raw).view(np.uint8).reshape(m, -1)
+    mm = m
+    if rows is not None:
+        a = a[np.asarray(rows)]
+        mm = a.shape[0]
+    dec = decode_q8_0 if wtype == W_Q8_0 else decode_q4_0
+    return dec(a, mm, k)
+
+
+# ---------------------------------------------------------------------------
+# Epilogue
+# ---------------------------------------------------------------------------
+
+def gelu_erf(v) -> np.ndarray:
+    """erf-GELU: ``0.5 * v * (1 + erf(v / sqrt(2)))`` (``ae_put``'s flag-2 step, exact erf)."""
+    v = np.asarray(v, dtype=np.float64)
+    return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
+
+
+def epilogue(v: np.ndarray, flags: int, bias=None, y_old=None) -> np.ndarray:
+    """bias -> GELU -> +old output, in that order (``ae_put``)."""
+    out = np.array(v, dtype=np.float64, copy=True)
+    if flags & FLAG_BIAS:
+        out = out + np.asarray(bias, dtype=np.float64)[None, :]
+    if flags & FLAG_GELU:
+        out = gelu_erf(out)
+    if flags & FLAG_RESIDUAL:
+        out = out + np.asarray(y_old, dtype=np.float64)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# The layer
+# ---------------------------------------------------------------------------
+
+def linear(x, w_raw, wtype: int, m: int, k: int, bias=None, flags: int = 0, y_old=None,
+           rows=None):
+    """``(Y_ref, S)`` for ``Y = epilogue(X . W^T + b)``; both ``f64[n][len(rows) or m]``.
+
+    ``rows`` restricts the output columns (rows of W) to a subset, so that a
+    sample of a large product can be checked one output at a time; ``bias``
+    and ``y_old`` are then given for the full width and sliced here.
+    """
+    x64 = np.asarray(x, dtype=np.float64).reshape(-1, k)
+    w = decode(w_raw, wtype, m, k, rows)
+    v = x64 @ w.T
+    s = np.abs(x64) @ np.abs(w).T
+    b = None if bias is None else np.asarray(bias, dtype=np.float64)
+    yo = None if y_old is None else np.asarray(y_old, dtype=np.float64).reshape(x64.shape[0], m)
+    if rows is not None:
+        r = np.asarray(rows)
+        b = None if b is None else b[r]
+        yo = None if yo is None else yo[:, r]
+    return epilogue(v, flags, b, yo), s
+
+
+def moe(x, bank_raw, wtype: int, ids, n_exp: int, m: int, k: int, gates=None, rows=None):
+    """MoE matvec over one weight bank ``[E][m][k]``.
+
+    Without ``gates``: ``Y[s] = W[ids[s]] . x[token(s)]`` per routed slot
+    ``s = t*top_k + j`` (``[n_tok*top_k][m]``). With ``gates``:
+    ``Y[t] = sum_j gates[t, j] * W[ids[t, j]] . x[t]`` (``[n_tok][m]``), and
+    ``S[t] = sum_j |gates[t, j]| * (|W[ids[t, j]]| . |x[t]|)``.
+    """
+    ids = np.asarray(ids).astype(np.int64)
+    n_tok, top_k = ids.shape
+    x64 = np.asarray(x, dtype=np.float64).reshape(n_tok, k)
+    nb = weight_nbytes(wtype, m, k)
+    bank = np.ascontiguousarray(bank_raw).view(np.uint8).reshape(-1)
+    width = m if rows is None else len(rows)
+    slot_y = np.zeros((n_tok, top_k, width))
+    slot_s = np.zeros((n_tok, top_k, width))
+    for e in np.unique(ids):
+        if not 0 <= e < n_exp:
+            raise ValueError(f"expert id {e} outside [0, {n_exp})")
+        w = decode(bank[e * nb:(e + 1) * nb], wtype, m, k, rows)
+        t_idx, j_idx = np.nonzero(ids == e)
+        slot_y[t_idx, j_idx] = x64[t_idx] @ w.T
+        slot_s[t_idx, j_idx] = np.abs(x64[t_idx]) @ np.abs(w).T
+    if gates is None:
+        return slot_y.reshape(n_tok * top_k, width), slot_s.reshape(n_tok * top_k, width)
+    g = np.asarray(gates, dtype=np.float64).reshape(n_tok, top_k)
+    return ((g[:, :, None] * slot_y).sum(axis=1),
+            (np.abs(g)[:, :, None] * slot_s).sum(axis=1))
+
+
+# ---------------------------------------------------------------------------
+# Q8_0 test encoder (wavo gpu/mod.rs, test helper ``weights``)
+# ---------------------------------------------------------------------------
+
+def encode_q8_0(w) -> np.ndarray:
+    """Q8_0 bytes of f32 rows, as the wavo test helper builds them.
+
+    Per block of 32: ``d = max|x| / 127`` (in f32), ``q = round(x / d)``
+    (rounded half away from zero) cast to int8, and ``d`` stored as f16.
+    """
+    w = np.asarray(w, dtype=np.float32)
+    m, k = w.shape
+    blocks = w.reshape(m, k // QBLOCK, QBLOCK)
+    d = (np.abs(blocks).max(axis=2) / np.float32(127.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = blocks / d[:, :, None]
+    r = np.where(np.isfinite(r), r, 0.0)
+    q = (np.sign(r) * np.floor(np.abs(r) + np.float32(0.5))).astype(np.int8)
+    dh = d.astype(np.float16).view(np.uint16)
+    out = np.empty((m, k // QBLOCK, 34), np.uint8)
+    out[:, :, 0] = dh & 0xFF
+    out[:, :, 1] = dh >> 8
+    out[:, :, 2:] = q.view(np.uint8)
+    return out.reshape(m, -1)
