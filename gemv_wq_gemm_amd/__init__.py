@@ -1,0 +1,184 @@
+"""Python binding of ``libwq.so``, the weight-dequantizing linear layer for MI355X.
+
+Argument marshalling only: every function checks tensor dtypes, devices and
+sizes, then passes raw device pointers and torch's current HIP stream to the C
+ABI declared in ``include/wq.h``. All arithmetic happens in the HIP kernels;
+there is no fallback. If the library is not built, every call raises.
+
+    import gemv_wq_gemm_amd as wq
+    y = wq.gemm(x, w, wq.W_Q8_0, m=4096, k=4096)              # n <= 16: f32 matvec path
+    y = wq.gemm(x, w, wq.W_BF16, bias=b, gelu=True)           # n > 16: bf16 MFMA path
+    y = wq.moe_matvec(x, bank, wq.W_Q4_0, ids, gates, n_experts=8, m=14336, k=4096)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
+BIAS, GELU, RESIDUAL = 1, 2, 4
+PATH_AUTO, PATH_MATVEC, PATH_MFMA = 0, 1, 2
+MATVEC_MAX_N = 16
+
+STATUS = {
+    0: "WQ_OK", -1: "WQ_ERR_NULL", -2: "WQ_ERR_SHAPE", -3: "WQ_ERR_WTYPE", -4: "WQ_ERR_FLAGS",
+    -5: "WQ_ERR_ALIGN", -6: "WQ_ERR_ALIAS", -7: "WQ_ERR_HIP",
+}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwq.so")
+
+# (name, restype, argtypes) of every function include/wq.h declares.
+_P, _I64, _I, _U = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
+SIGNATURES = [
+    ("wq_gemm", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _P]),
+    ("wq_gemm_ex", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _I, _P]),
+    ("wq_moe_matvec", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    ("wq_dequantize", _I, [_P, _I, _P, _I64, _I64, _P]),
+    ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
+    ("wq_gemm_path", _I, [_I64, _I64, _I64, _I]),
+    ("wq_last_error", ctypes.c_char_p, []),
+    ("wq_version", ctypes.c_char_p, []),
+]
+
+
+class WqError(RuntimeError):
+    """A nonzero status from the C ABI, with the library's message."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded ``libwq.so`` (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m gemv_wq_gemm_amd.build`")
+        # torch ships its own HIP runtime under another file name. Importing it
+        # first makes the library's libamdhip64.so.7 resolve (by soname) to that
+        # same runtime; otherwise the process would hold two HIP runtimes and
+        # the second one sees no device.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, res, args in SIGNATURES:
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise WqError(status, lib().wq_last_error().decode())
+
+
+def version() -> str:
+    return lib().wq_version().decode()
+
+
+def weight_bytes(wtype: int, m: int, k: int) -> int:
+    return int(lib().wq_weight_bytes(wtype, m, k))
+
+
+def gemm_path(n: int, m: int, k: int, wtype: int) -> int:
+    r = lib().wq_gemm_path(n, m, k, wtype)
+    _check(min(r, 0))
+    return r
+
+
+def _stream():
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t, name):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _f32(t, name, numel=None):
+    import torch
+    if t.dtype != torch.float32:
+        raise ValueError(f"{name} must be float32, got {t.dtype}")
+    if numel is not None and t.numel() != numel:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {numel}")
+    return _dev(t, name)
+
+
+def _weight(w, wtype, nbytes, name="w"):
+    if w.numel() * w.element_size() < nbytes:
+        raise ValueError(f"{name} has {w.numel() * w.element_size()} bytes, needs {nbytes}")
+    return _dev(w, name)
+
+
+def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, residual: bool = False,
+         out=None, path: int = PATH_AUTO):
+    """``out[n][m] = epilogue(x[n][k] . W^T + bias)`` via ``wq_gemm_ex``.
+
+    ``w`` holds the weight in its storage format (any dtype; its bytes are
+    used). With ``residual=True``, ``out`` is required and accumulated into.
+    """
+    import torch
+    n = x.numel() // k if k else 0
+    if x.numel() != n * k:
+        raise ValueError("x must hold n*k elements")
+    if out is None:
+        if residual:
+            raise ValueError("residual=True needs out= (the values to accumulate into)")
+        out = torch.empty((n, m), dtype=torch.float32, device=x.device)
+    flags = (BIAS if bias is not None else 0) | (GELU if gelu else 0) | (RESIDUAL if residual else 0)
+    nbytes = weight_bytes(wtype, m, k)
+    if nbytes < 0:
+        _check(lib().wq_gemm_path(n, m, k, wtype))
+    st = lib().wq_gemm_ex(
+        _f32(x, "x"), _weight(w, wtype, nbytes), wtype,
+        None if bias is None else _f32(bias, "bias", m), flags,
+        _f32(out, "out", n * m), n, m, k, path, _stream())
+    _check(st)
+    return out
+
+
+def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: int, k: int, out=None):
+    """Expert-major MoE matvec via ``wq_moe_matvec``.
+
+    ``ids`` int32 ``[n_tok][top_k]``. Without ``gates`` the result is per slot
+    ``[n_tok*top_k][m]``; with ``gates`` (f32 ``[n_tok][top_k]``) it is the
+    gate-weighted sum per token, ``[n_tok][m]``.
+    """
+    import torch
+    if ids.dtype != torch.int32:
+        raise ValueError("ids must be int32")
+    n_tok, top_k = ids.shape
+    rows = n_tok if gates is not None else n_tok * top_k
+    if out is None:
+        out = torch.empty((rows, m), dtype=torch.float32, device=x.device)
+    nbytes = weight_bytes(wtype, m, k)
+    st = lib().wq_moe_matvec(
+        _f32(x, "x", n_tok * k), _weight(w_experts, wtype, max(nbytes, 0) * n_experts, "w_experts"), wtype,
+        _dev(ids, "ids"), None if gates is None else _f32(gates, "gates", n_tok * top_k),
+        _f32(out, "out", rows * m), n_tok, top_k, n_experts, m, k, _stream())
+    _check(st)
+    return out
+
+
+def dequantize(w, wtype: int, *, m: int, k: int, out=None):
+    """``out[m][k]`` = exact f32 values of the weight, via ``wq_dequantize``."""
+    import torch
+    if out is None:
+        out = torch.empty((m, k), dtype=torch.float32, device=w.device)
+    nbytes = weight_bytes(wtype, m, k)
+    st = lib().wq_dequantize(_weight(w, wtype, max(nbytes, 0)), wtype, _f32(out, "out", m * k), m, k, _stream())
+    _check(st)
+    return out

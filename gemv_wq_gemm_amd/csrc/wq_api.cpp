@@ -1,0 +1,268 @@
+// Host side of the C ABI declared in include/wq.h: argument checks, path
+// choice, the MoE combine workspace, and error reporting.
+//
+// The argument checks follow the pages' own: k must be a multiple of 32
+// (wavo src/gpu/mod.rs `Gpu::upload_linear`; hanzo-ml src/wgpu_backend.rs
+// `matvec_q4_0_gpu` / `matvec_q8_0_gpu`), buffers must hold what the sizes
+// say (`moe_matvec_gpu`), and the bias flag follows the presence of a bias
+// (cortiq-engine src/gpu_wgpu/nemotron_audio.rs `AudioEncoder::gemm` sets
+// flag 1 exactly when a bias is given). Every check runs before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "wq.h"
+#include "wq_internal.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return fail(WQ_ERR_HIP, "%s: %s (%s)", what, hipGetErrorName(e), hipGetErrorString(e));
+}
+
+void clear_error() { g_err[0] = '\0'; }
+
+constexpr int64_t kIntMax = 0x7fffffff;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// [a, a+na) and [b, b+nb) overlap (byte ranges; empty ranges never overlap).
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  if (!a || !b || na <= 0 || nb <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + static_cast<uintptr_t>(nb) && b0 < a0 + static_cast<uintptr_t>(na);
+}
+
+int check_wtype(int wtype) {
+  if (wtype != WQ_W_BF16 && wtype != WQ_W_Q8_0 && wtype != WQ_W_Q4_0)
+    return fail(WQ_ERR_WTYPE, "unknown weight type %d (0 = bf16, 1 = Q8_0, 2 = Q4_0)", wtype);
+  return WQ_OK;
+}
+
+int check_k(int64_t k) {
+  if (k <= 0 || k % 32 != 0) return fail(WQ_ERR_SHAPE, "k must be a positive multiple of 32, got %lld", (long long)k);
+  if (k > kIntMax / 4) return fail(WQ_ERR_SHAPE, "k = %lld is too large", (long long)k);
+  return WQ_OK;
+}
+
+// ---- MoE combine workspace: per (device, stream), grown on demand, kept for the process ----
+struct Workspace {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+};
+std::mutex g_ws_mu;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int workspace(hipStream_t stream, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace& w = g_ws[{dev, stream}];
+  if (w.bytes < bytes) {
+    if (w.ptr) {
+      // The old buffer may still be read by work queued on this stream.
+      e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      e = hipFree(w.ptr);
+      if (e != hipSuccess) return hip_fail(e, "hipFree");
+      w.ptr = nullptr;
+      w.bytes = 0;
+    }
+    size_t want = bytes < (size_t(1) << 20) ? (size_t(1) << 20) : bytes;
+    e = hipMalloc(&w.ptr, want);
+    if (e != hipSuccess) return hip_fail(e, "hipMalloc (MoE workspace)");
+    w.bytes = want;
+  }
+  *out = w.ptr;
+  return WQ_OK;
+}
+
+int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y,
+                 int64_t n, int64_t m, int64_t k, int path, void* stream) {
+  clear_error();
+  if (int r = check_wtype(wtype)) return r;
+  if (flags & ~(WQ_BIAS | WQ_GELU | WQ_RESIDUAL)) return fail(WQ_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+  if (((flags & WQ_BIAS) != 0) != (bias != nullptr))
+    return fail(WQ_ERR_FLAGS, "WQ_BIAS must be set exactly when a bias pointer is given");
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_MATVEC && path != WQ_PATH_MFMA)
+    return fail(WQ_ERR_SHAPE, "unknown path %d", path);
+  if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size n = %lld, m = %lld", (long long)n, (long long)m);
+  if (int r = check_k(k)) return r;
+  if (n > kIntMax || m > kIntMax) return fail(WQ_ERR_SHAPE, "n or m exceeds 2^31 - 1");
+  if (path == WQ_PATH_AUTO) path = n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
+  if (path == WQ_PATH_MATVEC && n > WQ_MATVEC_MAX_N)
+    return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
+  if (path == WQ_PATH_MFMA && n > 65535LL * 128)
+    return fail(WQ_ERR_SHAPE, "n = %lld exceeds the GEMM grid (65535 x 128 rows)", (long long)n);
+  if (n == 0 || m == 0) return WQ_OK;
+  if (!x || !w || !y) return fail(WQ_ERR_NULL, "x, w and y must not be NULL");
+  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
+    return fail(WQ_ERR_ALIGN, "x, w and y must be 16-byte aligned");
+  if (bias && !aligned(bias, 4)) return fail(WQ_ERR_ALIGN, "bias must be 4-byte aligned");
+  const int64_t wbytes = wq_weight_bytes(wtype, m, k);
+  const int64_t ybytes = n * m * 4;
+  if (overlap(y, ybytes, x, n * k * 4) || overlap(y, ybytes, w, wbytes) || overlap(y, ybytes, bias, m * 4))
+    return fail(WQ_ERR_ALIAS, "y overlaps x, w or bias");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  const long long rowbytes = static_cast<long long>(wbytes / m);
+  if (path == WQ_PATH_MATVEC) {
+    wq::MatvecParams p{};
+    p.x = x;
+    p.w = static_cast<const uint8_t*>(w);
+    p.expert_bytes = 0;
+    p.bias = bias;
+    p.y = y;
+    p.ids = nullptr;
+    p.n_slots = static_cast<int>(n);
+    p.top_k = 1;
+    p.n_exp = 1;
+    p.m = static_cast<int>(m);
+    p.k = static_cast<int>(k);
+    p.rowbytes = rowbytes;
+    p.flags = flags;
+    e = wq::launch_matvec(wtype, p, static_cast<int>(n), s);
+  } else {
+    wq::GemmParams p{};
+    p.x = x;
+    p.w = static_cast<const uint8_t*>(w);
+    p.bias = bias;
+    p.y = y;
+    p.n = static_cast<int>(n);
+    p.m = static_cast<int>(m);
+    p.k = static_cast<int>(k);
+    p.rowbytes = rowbytes;
+    p.flags = flags;
+    e = wq::launch_gemm(wtype, p, s);
+  }
+  if (e != hipSuccess) return hip_fail(e, "kernel launch");
+  return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k) {
+  if (m < 0 || k < 0 || k % 32 != 0) return -1;
+  switch (wtype) {
+    case WQ_W_BF16: return 2 * m * k;
+    case WQ_W_Q8_0: return 34 * m * (k / 32);
+    case WQ_W_Q4_0: return 18 * m * (k / 32);
+    default: return -1;
+  }
+}
+
+int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype) {
+  clear_error();
+  if (int r = check_wtype(wtype)) return r;
+  if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size");
+  if (int r = check_k(k)) return r;
+  return n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
+}
+
+int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
+            int64_t m, int64_t k, void* stream) {
+  return gemm_checked(x, w, wtype, bias, flags, y, n, m, k, WQ_PATH_AUTO, stream);
+}
+
+int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
+               int64_t m, int64_t k, int path, void* stream) {
+  return gemm_checked(x, w, wtype, bias, flags, y, n, m, k, path, stream);
+}
+
+int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                  const float* gate_w, float* y, int64_t n_tok, int64_t top_k, int64_t n_experts, int64_t m,
+                  int64_t k, void* stream) {
+  clear_error();
+  if (int r = check_wtype(wtype)) return r;
+  if (n_tok < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size");
+  if (n_experts < 1 || n_experts > 65534) return fail(WQ_ERR_SHAPE, "n_experts must be in [1, 65534]");
+  if (top_k < 1 || top_k > n_experts) return fail(WQ_ERR_SHAPE, "top_k must be in [1, n_experts]");
+  if (int r = check_k(k)) return r;
+  if (m > kIntMax) return fail(WQ_ERR_SHAPE, "m exceeds 2^31 - 1");
+  if (n_tok * top_k > 4096) return fail(WQ_ERR_SHAPE, "n_tok * top_k must be <= 4096");
+  if (n_tok == 0 || m == 0) return WQ_OK;
+  if (!x || !w_experts || !expert_ids || !y) return fail(WQ_ERR_NULL, "x, w_experts, expert_ids and y must not be NULL");
+  if (!aligned(x, 16) || !aligned(w_experts, 16) || !aligned(y, 16))
+    return fail(WQ_ERR_ALIGN, "x, w_experts and y must be 16-byte aligned");
+  if (!aligned(expert_ids, 4) || (gate_w && !aligned(gate_w, 4)))
+    return fail(WQ_ERR_ALIGN, "expert_ids and gate_w must be 4-byte aligned");
+  const int64_t n_slots = n_tok * top_k;
+  const int64_t ebytes = wq_weight_bytes(wtype, m, k);
+  const int64_t ybytes = (gate_w ? n_tok : n_slots) * m * 4;
+  if (overlap(y, ybytes, x, n_tok * k * 4) || overlap(y, ybytes, w_experts, ebytes * n_experts) ||
+      overlap(y, ybytes, expert_ids, n_slots * 4) || overlap(y, ybytes, gate_w, n_slots * 4))
+    return fail(WQ_ERR_ALIAS, "y overlaps x, w_experts, expert_ids or gate_w");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* slots = y;
+  if (gate_w) {
+    void* ws = nullptr;
+    if (int r = workspace(s, static_cast<size_t>(n_slots * m * 4), &ws)) return r;
+    slots = static_cast<float*>(ws);
+  }
+  wq::MatvecParams p{};
+  p.x = x;
+  p.w = static_cast<const uint8_t*>(w_experts);
+  p.expert_bytes = ebytes;
+  p.bias = nullptr;
+  p.y = slots;
+  p.ids = expert_ids;
+  p.n_slots = static_cast<int>(n_slots);
+  p.top_k = static_cast<int>(top_k);
+  p.n_exp = static_cast<int>(n_experts);
+  p.m = static_cast<int>(m);
+  p.k = static_cast<int>(k);
+  p.rowbytes = ebytes / m;
+  p.flags = 0;
+  // Expected slots per expert picks the tokens-per-pass variant; more per expert is still exact.
+  const int64_t per_expert = (n_slots + n_experts - 1) / n_experts;
+  hipError_t e = wq::launch_matvec(wtype, p, static_cast<int>(per_expert < n_tok ? per_expert : n_tok), s);
+  if (e != hipSuccess) return hip_fail(e, "MoE matvec launch");
+  if (gate_w) {
+    e = wq::launch_moe_combine(slots, gate_w, y, static_cast<int>(n_tok), static_cast<int>(top_k),
+                               static_cast<int>(m), s);
+    if (e != hipSuccess) return hip_fail(e, "MoE combine launch");
+  }
+  return WQ_OK;
+}
+
+int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream) {
+  clear_error();
+  if (int r = check_wtype(wtype)) return r;
+  if (m < 0) return fail(WQ_ERR_SHAPE, "negative m");
+  if (int r = check_k(k)) return r;
+  if (m > kIntMax || m * (k / 32) > kIntMax * 128LL) return fail(WQ_ERR_SHAPE, "m * k too large");
+  if (m == 0) return WQ_OK;
+  if (!w || !out) return fail(WQ_ERR_NULL, "w and out must not be NULL");
+  if (!aligned(w, 16) || !aligned(out, 16)) return fail(WQ_ERR_ALIGN, "w and out must be 16-byte aligned");
+  if (overlap(out, m * k * 4, w, wq_weight_bytes(wtype, m, k))) return fail(WQ_ERR_ALIAS, "out overlaps w");
+  hipError_t e = wq::launch_dequantize(wtype, static_cast<const uint8_t*>(w), out, static_cast<int>(m),
+                                       static_cast<int>(k), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return WQ_OK;
+}
+
+const char* wq_last_error(void) { return g_err; }
+
+const char* wq_version(void) { return "wq 0.1.0 (gfx950)"; }
+
+}  // extern "C"

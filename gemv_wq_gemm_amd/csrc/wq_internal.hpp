@@ -1,0 +1,58 @@
+// Internal interface between the host API (wq_api.cpp) and the kernel files.
+// Not installed; the public ABI is include/wq.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wq {
+
+enum WType : int { kBF16 = 0, kQ8_0 = 1, kQ4_0 = 2 };
+
+// Bytes of one 32-element block in each storage type (bf16: 32 x 2 bytes).
+__host__ __device__ constexpr int block_bytes(int wt) { return wt == kBF16 ? 64 : wt == kQ8_0 ? 34 : 18; }
+
+// ---- matvec / MoE (f32 FMA path) ---------------------------------------------------------------
+struct MatvecParams {
+  const float* x;           // activations, rows of k floats
+  const uint8_t* w;         // weight, or the first expert of a bank
+  long long expert_bytes;   // byte distance between experts (0 for a single weight)
+  const float* bias;        // [m] or null
+  float* y;                 // outputs, rows of m floats
+  const int32_t* ids;       // MoE: expert of each slot; null for the plain layer
+  int n_slots;              // plain: rows of x (<= 16); MoE: n_tok * top_k
+  int top_k;                // MoE: slots per token (x row of slot s = s / top_k); plain: 1
+  int n_exp;                // experts in the bank (plain: 1)
+  int m, k;
+  long long rowbytes;       // bytes of one weight row
+  unsigned flags;           // epilogue flags (plain layer only)
+};
+
+// Picks the kernel variant (tokens per pass, rows per wave) and launches it.
+// For MoE (ids != null) the grid has one extra expert row that writes NaN for
+// slots whose id is out of range.
+hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tokens_per_expert,
+                         hipStream_t stream);
+
+// y[t][j] = sum_s gate[t*top_k + s] * slots[(t*top_k + s)][j], summed in s order.
+hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, int n_tok,
+                              int top_k, int m, hipStream_t stream);
+
+// out[m][k] = exact f32 value of every weight.
+hipError_t launch_dequantize(int wtype, const uint8_t* w, float* out, int m, int k,
+                             hipStream_t stream);
+
+// ---- MFMA GEMM ---------------------------------------------------------------------------------
+struct GemmParams {
+  const float* x;     // [n][k]
+  const uint8_t* w;   // [m][k] in storage type
+  const float* bias;  // [m] or null
+  float* y;           // [n][m]
+  int n, m, k;
+  long long rowbytes;
+  unsigned flags;
+};
+
+hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream);
+
+}  // namespace wq

@@ -1,0 +1,150 @@
+/*
+ * wq.h -- C ABI of the weight-dequantizing linear layer for AMD MI355X (gfx950).
+ *
+ *   Y[n x m] = epilogue( X[n x k] . W[m x k]^T + bias )
+ *
+ * X is f32, W is stored as bf16 or as GGML-style 32-element Q8_0 / Q4_0
+ * blocks, accumulation is f32, and the epilogue adds a bias, applies erf-GELU
+ * and/or accumulates into Y. The operation and its flag bits are those of the
+ * GEMM kernel on the cortiq-engine 0.8.49 page src/gpu_wgpu/nemotron_audio.rs
+ * (the `AE_WGSL` source: `ae_gemm`, its `GmP` parameter block and `ae_put`);
+ * the quantized weight formats and the MoE matvec are those of the hanzo-ml
+ * 0.11.13 page src/wgpu_backend.rs (`upload_qweight`, `matvec_q8_0_gpu`,
+ * `matvec_q4_0_gpu`, `moe_matvec_gpu`); wavo 0.3.0 src/gpu/mod.rs describes
+ * the same layer (`Linear`, `Epilogue`, `Pass::gemm`, `Pass::gemv`) and the
+ * requirement k % 32 == 0 (`Gpu::upload_linear`).
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers, owned by the caller. The
+ *     library keeps no reference to them after the call returns; the caller
+ *     keeps them alive until the work enqueued on `stream` has completed.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call is asynchronous on it; nothing synchronizes the host.
+ *   - Tensors are contiguous and row-major; there are no strides.
+ *   - Arguments are checked on the host before any HIP call; a failed check
+ *     returns a negative status, enqueues nothing and leaves the outputs
+ *     untouched. `wq_last_error()` then describes it (per thread).
+ *   - Faults of the enqueued work itself surface at the caller's next
+ *     synchronization, as for any HIP kernel.
+ *   - The library allocates device memory only for the MoE gate combine
+ *     (a per-device, per-stream workspace, grown on demand and kept until
+ *     the process ends).
+ */
+#ifndef WQ_H
+#define WQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- weight storage types ------------------------------------------------
+ * WQ_W_BF16: uint16[m][k]; each value is the upper 16 bits of an f32
+ *            (little-endian), decoded exactly by a 16-bit shift -- the weight
+ *            pairs of `ae_gemm` on the cortiq-engine page.
+ * WQ_W_Q8_0: m rows of k/32 blocks of 34 bytes: a little-endian f16 scale d,
+ *            then 32 int8 quants q; value = d*q (wavo `Gpu::upload_linear`,
+ *            hanzo-ml `matvec_q8_0_gpu`).
+ * WQ_W_Q4_0: m rows of k/32 blocks of 18 bytes: a little-endian f16 scale d,
+ *            then 16 bytes; byte j holds element j in its low nibble and
+ *            element j+16 in its high nibble; value = d*(q-8) (hanzo-ml
+ *            `matvec_q4_0_gpu`). Rows follow each other with no padding. */
+#define WQ_W_BF16 0
+#define WQ_W_Q8_0 1
+#define WQ_W_Q4_0 2
+
+/* ---- epilogue flags (the bit values of `GmP.flags` / `ae_put`) ------------
+ * Applied to each output in this order: + bias[j] (WQ_BIAS), then erf-GELU
+ * 0.5*v*(1+erf(v/sqrt 2)) (WQ_GELU), then + the value Y held before the call
+ * (WQ_RESIDUAL; Y is read and written in place). */
+#define WQ_BIAS 1u
+#define WQ_GELU 2u
+#define WQ_RESIDUAL 4u
+
+/* ---- contraction paths ----------------------------------------------------
+ * WQ_PATH_MATVEC: all-f32 FMA path for n <= 16 (weights streamed once for all
+ *   n rows of X). Error: |y - y_ref| <= 1e-5 * sum_k |x_k * w_k|.
+ * WQ_PATH_MFMA: bf16 matrix-core path for any n: X rounded to bf16 (to
+ *   nearest even), W fed exactly (bf16 as stored; Q8_0/Q4_0 as their integer
+ *   quants, with the f16 scale applied in f32 per 32-element block), f32
+ *   accumulation. Error: |y - y_ref| <= 2^-8 * sum_k |x_k * w_k|.
+ * WQ_PATH_AUTO: MATVEC when n <= 16, else MFMA (`wq_gemm_path` tells which). */
+#define WQ_PATH_AUTO 0
+#define WQ_PATH_MATVEC 1
+#define WQ_PATH_MFMA 2
+#define WQ_MATVEC_MAX_N 16
+
+/* ---- status codes ---------------------------------------------------------- */
+#define WQ_OK 0
+#define WQ_ERR_NULL (-1)   /* a required pointer is NULL */
+#define WQ_ERR_SHAPE (-2)  /* negative size, k % 32 != 0, n too large for the path, ... */
+#define WQ_ERR_WTYPE (-3)  /* unknown weight type */
+#define WQ_ERR_FLAGS (-4)  /* unknown flag bits, or WQ_BIAS set without a bias (or a bias without WQ_BIAS) */
+#define WQ_ERR_ALIGN (-5)  /* x, w or y not 16-byte aligned; bias, ids or gates not 4-byte aligned */
+#define WQ_ERR_ALIAS (-6)  /* y overlaps x, w, bias, ids or gates */
+#define WQ_ERR_HIP (-7)    /* a HIP call failed (launch, allocation, device query) */
+
+/*
+ * wq_gemm: Y = epilogue(X . W^T + bias) on `stream`, path chosen by n.
+ *   x     f32 [n][k], 16-byte aligned.
+ *   w     weight [m][k] in `wtype` storage (wq_weight_bytes bytes), 16-byte aligned.
+ *   bias  f32 [m] when flags & WQ_BIAS, else NULL.
+ *   y     f32 [n][m], 16-byte aligned; read first when flags & WQ_RESIDUAL.
+ *   n, m  >= 0 (n == 0 or m == 0: nothing to do, WQ_OK); k > 0, k % 32 == 0.
+ * Returns WQ_OK or a WQ_ERR_* code.
+ */
+int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
+            float* y, int64_t n, int64_t m, int64_t k, void* stream);
+
+/* wq_gemm with the path forced (WQ_PATH_*). WQ_PATH_MATVEC requires n <= 16. */
+int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
+               float* y, int64_t n, int64_t m, int64_t k, int path, void* stream);
+
+/*
+ * wq_moe_matvec: the MoE matvec of hanzo-ml `moe_matvec_gpu`, expert-major.
+ *   x          f32 [n_tok][k], 16-byte aligned.
+ *   w_experts  one bank of n_experts weights, expert e at byte offset
+ *              e * wq_weight_bytes(wtype, m, k); 16-byte aligned.
+ *   expert_ids int32 [n_tok][top_k]: expert of slot s = t*top_k + j.
+ *              Precondition 0 <= id < n_experts (not checked on the host:
+ *              the ids live on the device). A slot with an id outside that
+ *              range is never read from the bank; its output is NaN.
+ *   gate_w     f32 [n_tok][top_k] or NULL.
+ *   y          gate_w == NULL: f32 [n_tok*top_k][m], y[s] = W[ids[s]] . x[t].
+ *              gate_w != NULL: f32 [n_tok][m], y[t] = sum_j gate_w[t][j] * W[ids[t][j]] . x[t],
+ *              summed in j order.
+ *   1 <= top_k <= n_experts; n_tok*top_k <= 4096; k % 32 == 0.
+ * Each expert's weights are streamed once per call for all tokens routed to
+ * it; all arithmetic is f32 (the WQ_PATH_MATVEC bound per slot).
+ */
+int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                  const float* gate_w, float* y, int64_t n_tok, int64_t top_k,
+                  int64_t n_experts, int64_t m, int64_t k, void* stream);
+
+/*
+ * wq_dequantize: out[m][k] = the exact f32 value of every weight (bf16: the
+ * upper-half bit pattern; Q8_0: d*q; Q4_0: d*(q-8), all exact in f32).
+ *   w    weight in `wtype` storage, 16-byte aligned; out f32 [m][k], 16-byte aligned.
+ */
+int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream);
+
+/* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32);
+ * -1 for an unknown type, negative sizes or k % 32 != 0. */
+int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k);
+
+/* The path wq_gemm takes for these sizes: WQ_PATH_MATVEC or WQ_PATH_MFMA
+ * (negative WQ_ERR_* for invalid sizes or type). */
+int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype);
+
+/* Message of the last failed call on this thread ("" when none). */
+const char* wq_last_error(void);
+
+/* Library version string. */
+const char* wq_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WQ_H */

@@ -1,0 +1,230 @@
+"""GPU parity: the HIP path (through the C ABI) against the f64 oracle.
+
+Small shapes span several tiles and ragged tails; every weight type, both
+paths, the epilogue flags, NaN-prefilled outputs (every element must be
+written) and a canary region after the output (nothing written past it).
+"""
+import numpy as np
+import pytest
+
+import gemv_wq_gemm_amd as wq
+import oracle
+import synth
+from tests.parity import (B_F32, B_MFMA, assert_within, dev, guarded_out, oracle_with_tol,
+                          read_guarded)
+
+pytestmark = pytest.mark.gpu
+
+WTYPES = [wq.W_BF16, wq.W_Q8_0, wq.W_Q4_0]
+
+
+def _inputs(seed, wtype, n, m, k, flags):
+    g = synth.rng(seed, wtype, n, m, k, flags)
+    x = synth.normal_f32(g, (n, k), 1.0)
+    w = synth.weight(g, wtype, m, k, sigma=0.05, dsigma=0.01)
+    bias = synth.normal_f32(g, (m,), 0.1) if flags & wq.BIAS else None
+    y_old = synth.normal_f32(g, (n, m), 1.0) if flags & wq.RESIDUAL else None
+    return x, w, bias, y_old
+
+
+def _run(x, w, wtype, m, k, bias, flags, y_old, path):
+    n = x.shape[0]
+    buf, out = guarded_out(n, m, y_old if flags & wq.RESIDUAL else None)
+    wq.gemm(dev(x), dev(w), wtype, m=m, k=k, bias=None if bias is None else dev(bias),
+            gelu=bool(flags & wq.GELU), residual=bool(flags & wq.RESIDUAL), out=out, path=path)
+    return read_guarded(buf, n, m)
+
+
+# ---------------------------------------------------------------- dequantize
+
+def _random_weight_bytes(g, wtype, m, k):
+    """Random weights over every finite f16 scale (subnormals, zeros, signs included)."""
+    if wtype == wq.W_BF16:
+        bits = g.integers(0, 1 << 16, (m, k), dtype=np.uint16)
+        exp = (bits >> 7) & 0xFF
+        return np.where(exp == 0xFF, bits & 0x807F, bits).astype(np.uint16)
+    raw = synth.weight(g, wtype, m, k).reshape(m, k // 32, -1).copy()
+    raw[:, :, 2:] = g.integers(0, 256, raw[:, :, 2:].shape, dtype=np.uint8)
+    d = g.integers(0, 1 << 16, (m, k // 32), dtype=np.uint16)
+    d = np.where(((d >> 10) & 0x1F) == 0x1F, d & 0x83FF, d).astype(np.uint16)
+    d[0, 0] = 0x0000
+    if d.size > 1:
+        d.flat[1] = 0x8000
+    raw[:, :, 0] = d & 0xFF
+    raw[:, :, 1] = d >> 8
+    return raw.reshape(m, -1)
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("m,k", [(1, 32), (3, 32), (37, 96), (64, 4096), (5, 4128)])
+def test_dequantize_is_bit_exact(wtype, m, k):
+    g = synth.rng(7, wtype, m, k)
+    raw = _random_weight_bytes(g, wtype, m, k)
+    buf, out = guarded_out(m, k)
+    wq.dequantize(dev(raw), wtype, m=m, k=k, out=out)
+    got = read_guarded(buf, m, k)
+    want = oracle.decode(raw, wtype, m, k).astype(np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+# ---------------------------------------------------------------- matvec path (f32)
+
+MV_SHAPES = [(1, 32), (37, 96), (130, 4096), (67, 4128), (21, 8224)]
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 7, 16])
+@pytest.mark.parametrize("m,k", MV_SHAPES)
+def test_matvec_parity(wtype, n, m, k):
+    flags = [0, 1, 3, 7, 4, 6][(n + m) % 6]
+    x, w, bias, y_old = _inputs(1, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_MATVEC)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_F32)
+    assert_within(got, y_ref, tol, f"matvec wtype={wtype} n={n} m={m} k={k} flags={flags}")
+
+
+@pytest.mark.parametrize("flags", range(8))
+def test_matvec_every_flag_combination(flags):
+    wtype, n, m, k = wq.W_Q8_0, 3, 70, 256
+    x, w, bias, y_old = _inputs(2, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_F32)
+    assert_within(got, y_ref, tol, f"flags={flags}")
+
+
+# ---------------------------------------------------------------- MFMA path (bf16 x, exact w)
+
+GEMM_SHAPES = [(17, 1, 32), (64, 37, 96), (130, 128, 256), (200, 288, 160), (257, 130, 1024)]
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n,m,k", GEMM_SHAPES)
+def test_gemm_parity(wtype, n, m, k):
+    flags = [0, 3, 5, 7, 2][(n + m + wtype) % 5]
+    x, w, bias, y_old = _inputs(3, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_MFMA)
+    assert_within(got, y_ref, tol, f"gemm wtype={wtype} n={n} m={m} k={k} flags={flags}")
+
+
+@pytest.mark.parametrize("flags", range(8))
+def test_gemm_every_flag_combination(flags):
+    wtype, n, m, k = wq.W_Q4_0, 70, 140, 192
+    x, w, bias, y_old = _inputs(4, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_MFMA)
+    assert_within(got, y_ref, tol, f"flags={flags}")
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n", [1, 5, 16])
+def test_mfma_path_forced_at_small_n(wtype, n):
+    m, k = 45, 320
+    x, w, bias, y_old = _inputs(5, wtype, n, m, k, 1)
+    got = _run(x, w, wtype, m, k, bias, 1, y_old, wq.PATH_MFMA)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, 1, y_old, B_MFMA)
+    assert_within(got, y_ref, tol)
+
+
+# ---------------------------------------------------------------- exact cases
+
+def _probe(wtype, n=130, m=64, k=32):
+    r = np.arange(n)[:, None]
+    a = (np.arange(k)[None, :] + r % 32).astype(np.float32)
+    ones = np.arange(k)[None, :] == (np.arange(m) % 32)[:, None]
+    if wtype == wq.W_BF16:
+        w = np.where(ones, 0x3F80, 0).astype(np.uint16)
+    elif wtype == wq.W_Q8_0:
+        w = np.zeros((m, 34), np.uint8)
+        w[:, 1] = 0x3C
+        w[:, 2:] = ones
+    else:
+        q = np.where(ones, 9, 8)
+        w = np.zeros((m, 18), np.uint8)
+        w[:, 1] = 0x3C
+        w[:, 2:] = q[:, :16] | (q[:, 16:] << 4)
+    return a, w
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("path,n", [(wq.PATH_MFMA, 130), (wq.PATH_MATVEC, 16), (wq.PATH_MATVEC, 1)])
+def test_closed_form_probe_is_exact(wtype, path, n):
+    m, k = 64, 32
+    a, w = _probe(wtype, n, m, k)
+    got = _run(a, w, wtype, m, k, None, 0, None, path)
+    want, _ = oracle.linear(a, w, wtype, m, k)
+    assert np.array_equal(got, want)
+
+
+def test_identity_weight():
+    import torch
+    k, n = 96, 40
+    x = synth.normal_f32(synth.rng(8), (n, k), 1.0)
+    w = np.where(np.eye(k, dtype=bool), 0x3F80, 0).astype(np.uint16)
+    got = _run(x, w, wq.W_BF16, k, k, None, 0, None, wq.PATH_MFMA)
+    assert np.array_equal(got, torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+    got = _run(x[:16], w, wq.W_BF16, k, k, None, 0, None, wq.PATH_MATVEC)
+    assert np.array_equal(got, x[:16])
+
+
+def test_zero_sized_calls_leave_output_alone():
+    import torch
+    x = torch.zeros(0, 32, device="cuda")
+    w = torch.zeros(8, 32, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros(0, 8, device="cuda")
+    assert wq.gemm(x, w, wq.W_BF16, m=8, k=32, out=out).shape == (0, 8)
+
+
+# ---------------------------------------------------------------- MoE
+
+def _moe_inputs(seed, wtype, n_tok, n_exp, top_k, m, k):
+    g = synth.rng(seed, wtype, n_tok, n_exp, top_k, m, k)
+    x = synth.normal_f32(g, (n_tok, k), 1.0)
+    bank = np.stack([synth.weight(g, wtype, m, k, sigma=0.05) for _ in range(n_exp)])
+    ids, gates = synth.moe_routing(g, n_tok, n_exp, top_k)
+    return x, bank, ids, gates
+
+
+def _run_moe(x, bank, wtype, ids, gates, n_exp, m, k):
+    n_tok, top_k = ids.shape
+    rows = n_tok if gates is not None else n_tok * top_k
+    buf, out = guarded_out(rows, m)
+    wq.moe_matvec(dev(x), dev(bank), wtype, dev(ids.astype(np.int32)),
+                  None if gates is None else dev(gates), n_experts=n_exp, m=m, k=k, out=out)
+    return read_guarded(buf, rows, m)
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n_tok,n_exp,top_k", [(1, 8, 2), (16, 4, 2), (5, 6, 3), (40, 8, 1), (64, 3, 3)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_moe_parity(wtype, n_tok, n_exp, top_k, gated):
+    m, k = 75, 160
+    x, bank, ids, gates = _moe_inputs(9, wtype, n_tok, n_exp, top_k, m, k)
+    got = _run_moe(x, bank, wtype, ids, gates if gated else None, n_exp, m, k)
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k, gates if gated else None)
+    assert_within(got, y_ref, B_F32 * S + 8 * 2.0 ** -24 * np.abs(y_ref), "moe")
+
+
+def test_moe_out_of_range_ids_give_nan_and_leave_other_slots_right():
+    wtype, n_tok, n_exp, top_k, m, k = wq.W_Q4_0, 6, 4, 2, 50, 64
+    x, bank, ids, gates = _moe_inputs(10, wtype, n_tok, n_exp, top_k, m, k)
+    bad = ids.copy()
+    bad[2, 1] = 7
+    bad[4, 0] = -1
+    got = _run_moe(x, bank, wtype, bad, None, n_exp, m, k)
+    assert np.isnan(got[2 * 2 + 1]).all() and np.isnan(got[4 * 2 + 0]).all()
+    ok = [s for s in range(n_tok * top_k) if s not in (5, 8)]
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k)
+    assert_within(got[ok], y_ref[ok], B_F32 * S[ok] + 1e-12, "moe valid slots")
+    gated = _run_moe(x, bank, wtype, bad, gates, n_exp, m, k)
+    assert np.isnan(gated[2]).all() and np.isnan(gated[4]).all()
+    assert np.isfinite(gated[[0, 1, 3, 5]]).all()
+
+
+def test_moe_all_tokens_on_one_expert_equals_the_16_row_layer():
+    wtype, n_tok, n_exp, m, k = wq.W_Q8_0, 16, 4, 90, 128
+    x, bank, _, _ = _moe_inputs(11, wtype, n_tok, n_exp, 1, m, k)
+    ids = np.full((n_tok, 1), 3, np.int32)
+    got = _run_moe(x, bank, wtype, ids, None, n_exp, m, k)
+    y_ref, S = oracle.linear(x, bank[3], wtype, m, k)
+    assert_within(got, y_ref, B_F32 * S + 1e-12)
