@@ -42,6 +42,9 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run an elementwise copy of 256 MiB (reads and writes that many bytes), "
+                         "the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
@@ -89,6 +92,14 @@ def main():
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     props = torch.cuda.get_device_properties(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
 
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)

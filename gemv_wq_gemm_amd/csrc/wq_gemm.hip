@@ -7,20 +7,28 @@
 // (`Pass::gemm`, one pipeline per weight type).
 //
 // Design for gfx950:
-//  * Workgroup tile 128 (rows of X) x 128 (rows of W), k step 64; four waves,
-//    each owning a 64x64 quarter as 2x2 v_mfma_f32_32x32x16_bf16 tiles.
-//  * X is read as f32 and rounded to bf16 (nearest even, v_cvt_pk_bf16_f32)
-//    on its way into LDS. bf16 weights go to LDS as stored.
-//  * Q8_0 / Q4_0 weights are decoded on the way into LDS to their integer
-//    quants q (Q8_0) or q-8 (Q4_0), which bf16 holds exactly; the matrix cores
-//    sum each 32-element block into a fresh accumulator and the f16 scale of
-//    that (row, block) multiplies it in f32. The weights thus enter the
-//    product exactly and only the bf16 rounding of X (2^-9 relative) and the
-//    f32 sums contribute error: |y - y_ref| <= 2^-8 * sum|x*w|.
-//  * The next k step's global loads are issued before the current step's
-//    matrix-core work, so their latency hides behind it.
-//  * LDS rows are padded to 144 bytes so the 16-byte fragment reads of 16
-//    consecutive lanes fall in distinct banks.
+//  * Workgroup tile BM (rows of X) x BN (rows of W), k step 64; WM x WN waves,
+//    each owning a (BM/WM) x (BN/WN) piece as v_mfma_f32_32x32x16_bf16 tiles.
+//    The wide tile along W keeps the per-FLOP traffic from L2 low: X arrives as
+//    f32 (4 bytes per element), W as 2 bytes or less.
+//  * X is rounded to bf16 (nearest even, v_cvt_pk_bf16_f32) on its way into
+//    LDS; bf16 weights go to LDS as stored. Q8_0 / Q4_0 weights are decoded on
+//    the way to their integer quants q (Q8_0) or q-8 (Q4_0), exact in bf16; the
+//    matrix cores sum each 32-element block into a fresh accumulator and the f16
+//    scale of that (row, block) multiplies it in f32. The weights thus enter
+//    exactly; only the bf16 rounding of X (2^-9 relative) and the f32 sums
+//    contribute error: |y - y_ref| <= 2^-8 * sum|x*w|.
+//  * Two LDS buffers: while the matrix cores work on one k step, the next step
+//    is loaded from global memory into registers and then written to the other
+//    buffer; one workgroup barrier per k step. LDS rows are padded to 144 bytes
+//    so 16-byte fragment reads of consecutive lanes spread over the banks.
+//  * Tiles are numbered so that consecutive tiles share W rows, and the tile
+//    numbers are dealt to the 8 XCDs in contiguous ranges (workgroup i runs on
+//    XCD i % 8), so an XCD's L2 holds the panels its tiles reuse.
+//  * Split-K: when the output has too few tiles to fill the chip and the
+//    epilogue is linear in the product (no GELU, accumulate into Y), gridDim.z
+//    workgroups share a tile's k range and add their partial sums into Y with
+//    f32 atomics; the first one adds the bias.
 #include <hip/hip_runtime.h>
 
 #include "wq_decode.hpp"
@@ -32,11 +40,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int BM = 128;         // tile rows (X rows, output rows)
-constexpr int BN = 128;         // tile cols (W rows, output cols)
 constexpr int BK = 64;          // k per step: two 32-element blocks
 constexpr int LDS_STRIDE = 72;  // bf16 per LDS row (64 + 8 padding)
-constexpr int kThreads = 256;
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   // Exact for the small integers fed here (at most 8 significant bits).
@@ -53,137 +58,171 @@ __device__ __forceinline__ uint2 round_bf16x4(float4 v) {
   return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
+// Decoded block -> 16 dwords of bf16 pairs in element order.
 template <int WT>
-struct WStage;  // registers holding one k step of this thread's share of the W tile
+__device__ __forceinline__ void quants_to_bf16(const uint32_t* q, uint32_t* o) {
+  if constexpr (WT == kQ8_0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      o[2 * i] = pack_bf16x2(q8_at(q[i], 0), q8_at(q[i], 1));
+      o[2 * i + 1] = pack_bf16x2(q8_at(q[i], 2), q8_at(q[i], 3));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t qx = q[i] ^ 0x88888888u;
+      // elements 4i..4i+3 (low nibbles) and 16+4i..16+4i+3 (high nibbles)
+      o[2 * i] = pack_bf16x2(q4_at(qx, 0), q4_at(qx, 2));
+      o[2 * i + 1] = pack_bf16x2(q4_at(qx, 4), q4_at(qx, 6));
+      o[8 + 2 * i] = pack_bf16x2(q4_at(qx, 1), q4_at(qx, 3));
+      o[8 + 2 * i + 1] = pack_bf16x2(q4_at(qx, 5), q4_at(qx, 7));
+    }
+  }
+}
 
-template <>
-struct WStage<kBF16> {
-  uint4 v[4];
-};
-template <>
-struct WStage<kQ8_0> {
-  uint32_t q[8];
-  uint32_t s;
-  bool ok;
-};
-template <>
-struct WStage<kQ4_0> {
-  uint32_t q[4];
-  uint32_t s;
-  bool ok;
+template <int WT, int BM, int BN, int WM, int WN>
+struct GemmCfg {
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int TM = BM / WM;  // wave tile rows (X rows)
+  static constexpr int TN = BN / WN;  // wave tile cols (W rows)
+  static constexpr int FM = TM / 32;  // 32x32 fragments per wave
+  static constexpr int FN = TN / 32;
+  // X: BM rows x 16 float4 per step
+  static constexpr int kXLoads = BM * 16 / kThreads;
+  // W bf16: BN rows x 8 16-byte chunks per step
+  static constexpr int kWLoads = BN * 8 / kThreads;
+  // W quantized: BN rows x 2 blocks per step
+  static constexpr int kQLoads = (BN * 2 + kThreads - 1) / kThreads;
+  static_assert(BM * 16 % kThreads == 0 && BN * 8 % kThreads == 0, "tile/threads mismatch");
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
 };
 
-template <int WT>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
-  __shared__ __attribute__((aligned(16))) __bf16 sA[BM * LDS_STRIDE];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[BN * LDS_STRIDE];
-  __shared__ float sS[BN * 2];
+template <int WT, int NQ>
+struct QStage {
+  uint32_t q[NQ][BlockWords<WT>::NW];
+  uint32_t s[NQ];
+  bool ok[NQ];
+};
+
+template <int WT, int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
+  using C = GemmCfg<WT, BM, BN, WM, WN>;
+  constexpr bool kQuant = WT != kBF16;
+  __shared__ __attribute__((aligned(16))) __bf16 sA[2][BM * LDS_STRIDE];
+  __shared__ __attribute__((aligned(16))) __bf16 sB[2][BN * LDS_STRIDE];
+  __shared__ float sS[2][kQuant ? BN * 2 : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  const int wm = wave >> 1;  // 64-row half of the tile (X rows)
-  const int wn = wave & 1;   // 64-col half of the tile (W rows)
-  const int n0 = blockIdx.y * BM;
-  const int m0 = blockIdx.x * BN;
-  const int nk = (p.k + BK - 1) / BK;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // ---- tile of this workgroup: contiguous ranges of tile numbers per XCD ----
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + 7) / 8;
+  const int bid = blockIdx.x;
+  const int t = (bid & 7) * per_xcd + (bid >> 3);
+  if (t >= tiles) return;  // workgroup-uniform
+  const int tile_n = t / tiles_m;  // W-row tile (varies slowest: neighbours share W)
+  const int tile_m = t - tile_n * tiles_m;
+  const int n0 = tile_m * BM;  // first X row
+  const int m0 = tile_n * BN;  // first W row
+
+  // ---- k range of this split ----
+  const int nk_total = (p.k + BK - 1) / BK;
+  const int per_split = (nk_total + gridDim.z - 1) / gridDim.z;
+  const int s_begin = blockIdx.z * per_split;
+  const int s_end = min(nk_total, s_begin + per_split);
+  const bool split = gridDim.z > 1;
 
   // ---- per-thread load assignments ----
-  // X: 8 float4 per thread; row = tid/16 + 16 i, float4 column tid%16.
-  const int xc4 = tid & 15;
-  const int xr0 = tid >> 4;
-  // W bf16: 4 x 16 bytes per thread; row = tid/8 + 32 i, 16-byte chunk tid%8.
-  const int wc16 = tid & 7;
-  const int wr0 = tid >> 3;
-  // W quantized: one (row, block) per thread.
-  const int qrow = tid >> 1;
-  const int qblk = tid & 1;
+  const int xc4 = tid & 15;   // float4 column of X
+  const int xr0 = tid >> 4;   // first X row; rows xr0 + i * (threads / 16)
+  const int wc16 = tid & 7;   // 16-byte chunk of a bf16 W row
+  const int wr0 = tid >> 3;   // first W row; rows wr0 + i * (threads / 8)
 
-  float4 xs[8];
-  WStage<WT> ws;
+  float4 xs[C::kXLoads];
+  uint4 wsb[kQuant ? 1 : C::kWLoads];
+  QStage<WT == kBF16 ? kQ8_0 : WT, C::kQLoads> wsq;
 
   auto load_stage = [&](int s) {
     const int k0 = s * BK;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = n0 + xr0 + 16 * i;
+    for (int i = 0; i < C::kXLoads; ++i) {
+      const int r = n0 + xr0 + i * (C::kThreads / 16);
       const int kk = k0 + 4 * xc4;
-      if (r < p.n && kk < p.k)
-        xs[i] = *reinterpret_cast<const float4*>(p.x + static_cast<long long>(r) * p.k + kk);
-      else
-        xs[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (r < p.n && kk < p.k) v = *reinterpret_cast<const float4*>(p.x + static_cast<long long>(r) * p.k + kk);
+      xs[i] = v;
     }
-    if constexpr (WT == kBF16) {
+    if constexpr (!kQuant) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = m0 + wr0 + 32 * i;
+      for (int i = 0; i < C::kWLoads; ++i) {
+        const int r = m0 + wr0 + i * (C::kThreads / 8);
         const int kk = k0 + 8 * wc16;
+        uint4 v = make_uint4(0u, 0u, 0u, 0u);
         if (r < p.m && kk < p.k)
-          ws.v[i] = *reinterpret_cast<const uint4*>(p.w + static_cast<long long>(r) * p.rowbytes + 2LL * kk);
-        else
-          ws.v[i] = make_uint4(0, 0, 0, 0);
+          v = *reinterpret_cast<const uint4*>(p.w + static_cast<long long>(r) * p.rowbytes + 2LL * kk);
+        wsb[i] = v;
       }
     } else {
-      const int r = m0 + qrow;
-      const int blk = s * 2 + qblk;
-      ws.ok = r < p.m && blk * 32 < p.k;
-      if (ws.ok) {
-        read_block<WT>(reinterpret_cast<const uint32_t*>(p.w),
-                       static_cast<long long>(r) * p.rowbytes + static_cast<long long>(blk) * block_bytes(WT),
-                       ws.q, &ws.s);
+#pragma unroll
+      for (int i = 0; i < C::kQLoads; ++i) {
+        const int e = tid + i * C::kThreads;  // (row, block) pair of the step
+        const int rr = e >> 1;
+        const int blk = s * 2 + (e & 1);
+        const bool ok = e < BN * 2 && m0 + rr < p.m && blk * 32 < p.k;
+        wsq.ok[i] = ok;
+        if (ok)
+          read_block<WT>(reinterpret_cast<const uint32_t*>(p.w),
+                         static_cast<long long>(m0 + rr) * p.rowbytes + static_cast<long long>(blk) * block_bytes(WT),
+                         wsq.q[i], &wsq.s[i]);
       }
     }
   };
 
-  auto store_stage = [&]() {
+  auto store_stage = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int r = xr0 + 16 * i;
-      *reinterpret_cast<uint2*>(&sA[r * LDS_STRIDE + 4 * xc4]) = round_bf16x4(xs[i]);
+    for (int i = 0; i < C::kXLoads; ++i) {
+      const int r = xr0 + i * (C::kThreads / 16);
+      *reinterpret_cast<uint2*>(&sA[buf][r * LDS_STRIDE + 4 * xc4]) = round_bf16x4(xs[i]);
     }
-    if constexpr (WT == kBF16) {
+    if constexpr (!kQuant) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = wr0 + 32 * i;
-        *reinterpret_cast<uint4*>(&sB[r * LDS_STRIDE + 8 * wc16]) = ws.v[i];
+      for (int i = 0; i < C::kWLoads; ++i) {
+        const int r = wr0 + i * (C::kThreads / 8);
+        *reinterpret_cast<uint4*>(&sB[buf][r * LDS_STRIDE + 8 * wc16]) = wsb[i];
       }
     } else {
-      uint32_t o[16];
-      if (ws.ok) {
-        if constexpr (WT == kQ8_0) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            o[2 * i] = pack_bf16x2(q8_at(ws.q[i], 0), q8_at(ws.q[i], 1));
-            o[2 * i + 1] = pack_bf16x2(q8_at(ws.q[i], 2), q8_at(ws.q[i], 3));
-          }
-        } else {
+      for (int i = 0; i < C::kQLoads; ++i) {
+        const int e = tid + i * C::kThreads;
+        if (e < BN * 2) {
+          const int rr = e >> 1;
+          const int half = e & 1;
+          uint32_t o[16];
+          if (wsq.ok[i]) {
+            quants_to_bf16<WT>(wsq.q[i], o);
+            sS[buf][rr * 2 + half] = f16_to_f32(wsq.s[i]);
+          } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const uint32_t qx = ws.q[i] ^ 0x88888888u;
-            // elements 4i..4i+3 (low nibbles) and 16+4i..16+4i+3 (high nibbles)
-            o[2 * i] = pack_bf16x2(q4_at(qx, 0), q4_at(qx, 2));
-            o[2 * i + 1] = pack_bf16x2(q4_at(qx, 4), q4_at(qx, 6));
-            o[8 + 2 * i] = pack_bf16x2(q4_at(qx, 1), q4_at(qx, 3));
-            o[8 + 2 * i + 1] = pack_bf16x2(q4_at(qx, 5), q4_at(qx, 7));
+            for (int j = 0; j < 16; ++j) o[j] = 0u;
+            sS[buf][rr * 2 + half] = 0.f;
           }
+          uint4* dst = reinterpret_cast<uint4*>(&sB[buf][rr * LDS_STRIDE + 32 * half]);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) dst[j] = make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
         }
-        sS[qrow * 2 + qblk] = f16_to_f32(ws.s);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o[i] = 0u;
-        sS[qrow * 2 + qblk] = 0.f;
       }
-      uint4* dst = reinterpret_cast<uint4*>(&sB[qrow * LDS_STRIDE + 32 * qblk]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) dst[i] = make_uint4(o[4 * i], o[4 * i + 1], o[4 * i + 2], o[4 * i + 3]);
     }
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[C::FM][C::FN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < C::FN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
@@ -191,84 +230,280 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   const int frow = lane & 31;
   const int fk = 8 * (lane >> 5);
 
-  load_stage(0);
-  for (int s = 0; s < nk; ++s) {
-    __syncthreads();  // the previous step's fragment reads are done
-    store_stage();
-    __syncthreads();
-    if (s + 1 < nk) load_stage(s + 1);
+  auto mfma_step = [&](int buf, int ks, f32x16 (&c)[C::FM][C::FN]) {
+    bf16x8 a[C::FM], b[C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * C::TM + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+      b[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * C::TN + j * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
+  };
 
-    if constexpr (WT == kBF16) {
+  if (s_begin < s_end) {
+    load_stage(s_begin);
+    store_stage(0);
+    __syncthreads();
+    for (int s = s_begin; s < s_end; ++s) {
+      const int buf = (s - s_begin) & 1;
+      if (s + 1 < s_end) load_stage(s + 1);
+      if constexpr (!kQuant) {
 #pragma unroll
-      for (int ks = 0; ks < BK / 16; ++ks) {
-        bf16x8 a[2], b[2];
+        for (int ks = 0; ks < BK / 16; ++ks) mfma_step(buf, ks, acc);
+      } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+        for (int blk = 0; blk < 2; ++blk) {
+          f32x16 part[C::FM][C::FN];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          b[j] = *reinterpret_cast<const bf16x8*>(&sB[(wn * 64 + j * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+          for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < C::FN; ++j)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-      }
-    } else {
+              for (int v = 0; v < 16; ++v) part[i][j][v] = 0.f;
+          mfma_step(buf, 2 * blk, part);
+          mfma_step(buf, 2 * blk + 1, part);
+          // Output column of this lane in fragment j is W row wn*TN + j*32 + lane%32.
 #pragma unroll
-      for (int blk = 0; blk < 2; ++blk) {
-        f32x16 part[2][2];
+          for (int j = 0; j < C::FN; ++j) {
+            const float d = sS[buf][(wn * C::TN + j * 32 + frow) * 2 + blk];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < C::FM; ++i)
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) part[i][j][v] = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int ks = blk * 2 + h;
-          bf16x8 a[2], b[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-            a[i] = *reinterpret_cast<const bf16x8*>(&sA[(wm * 64 + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            b[j] = *reinterpret_cast<const bf16x8*>(&sB[(wn * 64 + j * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-              part[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], part[i][j], 0, 0, 0);
+              for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(d, part[i][j][v], acc[i][j][v]);
+          }
         }
-        // Output column of this lane in tile j is W row wn*64 + j*32 + lane%32.
+      }
+      if (s + 1 < s_end) store_stage(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4 of each fragment ----
+  const bool first = blockIdx.z == 0;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const float d = sS[(wn * 64 + j * 32 + frow) * 2 + blk];
+  for (int j = 0; j < C::FN; ++j) {
+    const int col = m0 + wn * C::TN + j * 32 + frow;
+    if (col >= p.m) continue;
+    const float b = (p.flags & 1u) && first ? p.bias[col] : 0.f;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[i][j][v] = __builtin_fmaf(d, part[i][j][v], acc[i][j][v]);
+      for (int v = 0; v < 16; ++v) {
+        const int row = n0 + wm * C::TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        if (row < p.n) {
+          float* yp = p.y + static_cast<long long>(row) * p.m + col;
+          float o = acc[i][j][v] + b;
+          if (split) {
+            unsafeAtomicAdd(yp, o);  // Y already holds the old values (residual, no GELU)
+          } else {
+            if (p.flags & 2u) o = gelu_erf(o);
+            if (p.flags & 4u) o += *yp;
+            *yp = o;
+          }
         }
       }
     }
   }
+}
 
-  // ---- epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4 of each tile ----
+// ---------------------------------------------------------------------------------------------
+// bf16 weights: a deeper pipeline (k step 32, NSTAGE LDS slots, NSTAGE-1 steps in flight).
+//  * Both operands stream from global memory straight into LDS with global_load_lds_dwordx4, so
+//    the loads in flight hold no registers; X stays f32 in LDS and is rounded to bf16 (nearest
+//    even) as its fragments are read.
+//  * The loads are issued through inline assembly and waited for with explicit vmcnt counts; the
+//    compiler cannot tell which LDS bytes such a load writes and would otherwise wait for all of
+//    them before every LDS read. Their destinations are LDS only, so no register is ever live
+//    across an unfinished load. Waits the compiler inserts for its own loads can only over-wait,
+//    since vector memory loads complete in issue order.
+//  * LDS rows are XOR-swizzled by row so that the 16 lanes served per LDS cycle read 16 distinct
+//    groups of four banks: X rows (32 f32 = 8 chunks of 16 bytes) keep chunk c at
+//    c ^ ((r >> 1) & 7), W rows (32 bf16 = 4 chunks) at c ^ ((r >> 2) & 3).
+//  * A direct-to-LDS load writes lane l's 16 bytes at (LDS base + 16 l); each lane fetches the
+//    global chunk that belongs at its LDS position. Rows past the end of X or W are clamped to the
+//    last row (their products land only in outputs that are never stored).
+
+// M0 is listed as clobbered for the reader; the compiler treats it as reserved and does not
+// otherwise use it in these kernels (checked in the generated code).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint32_t lds_addr) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt out of range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_address(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const void __attribute__((address_space(3)))*)p));
+}
+
+__device__ __forceinline__ int x_swizzle(int r) { return (r >> 1) & 7; }
+__device__ __forceinline__ int w_swizzle(int r) { return (r >> 2) & 3; }
+
+template <int BM, int BN, int WM, int WN, int NSTAGE>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n) {
+  constexpr int BK = 32;
+  constexpr int kWaves = WM * WN;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int kABytes = BM * BK * 4;  // f32
+  constexpr int kBBytes = BN * BK * 2;  // bf16
+  constexpr int kStageBytes = kABytes + kBBytes;
+  constexpr int kAInst = kABytes / 1024 / kWaves;  // direct-to-LDS loads per wave per step
+  constexpr int kBInst = kBBytes / 1024 / kWaves;
+  constexpr int kInst = kAInst + kBInst;
+  constexpr int P = NSTAGE - 1;  // steps in flight
+  static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "step must split evenly");
+  static_assert(kInst * (P - 1) < 64, "vmcnt range");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE * kStageBytes];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: keeps addresses in SGPRs
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  const int tiles = tiles_m * tiles_n;
+  const int per_xcd = (tiles + 7) / 8;
+  const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (t >= tiles) return;  // workgroup-uniform
+  const int tile_n = t / tiles_m;
+  const int tile_m = t - tile_n * tiles_m;
+  const int n0 = tile_m * BM;
+  const int m0 = tile_n * BN;
+  const int nk = p.k / BK;
+
+  // Per-lane source offsets (bytes) of this wave's direct-to-LDS loads, for k step 0.
+  uint32_t aoff[kAInst], boff[kBInst];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int col = m0 + wn * 64 + j * 32 + frow;
+  for (int i = 0; i < kAInst; ++i) {
+    const int L = (wave * kAInst + i) * 64 + lane;  // 16-byte chunk index in a step's X region
+    const int r = L >> 3, pos = L & 7;
+    const int c = pos ^ x_swizzle(r);
+    aoff[i] = static_cast<uint32_t>(min(n0 + r, p.n - 1)) * static_cast<uint32_t>(p.k) * 4u + c * 16u;
+  }
+#pragma unroll
+  for (int i = 0; i < kBInst; ++i) {
+    const int L = (wave * kBInst + i) * 64 + lane;
+    const int r = L >> 2, pos = L & 3;
+    const int c = pos ^ w_swizzle(r);
+    boff[i] = static_cast<uint32_t>(min(m0 + r, p.m - 1)) * static_cast<uint32_t>(p.rowbytes) + c * 16u;
+  }
+  const uint32_t ring_lds = lds_address(ring);
+
+  auto issue = [&](int s) {
+    const uint32_t lst = ring_lds + (s % NSTAGE) * kStageBytes;
+#pragma unroll
+    for (int i = 0; i < kAInst; ++i) load_lds16(p.x, aoff[i] + s * (BK * 4u), lst + (wave * kAInst + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < kBInst; ++i)
+      load_lds16(p.w, boff[i] + s * (BK * 2u), lst + kABytes + (wave * kBInst + i) * 1024);
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+  const int frow = lane & 31;
+  const int khalf = lane >> 5;  // which 8 of the 16 k of an MFMA step
+
+  // The epilogue's bias is fetched now, long before it is needed.
+  float bias_v[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = min(m0 + wn * TN + j * 32 + frow, p.m - 1);
+    bias_v[j] = (p.flags & 1u) ? p.bias[col] : 0.f;
+  }
+
+  // Prologue: steps 0..P-1 in flight.
+#pragma unroll
+  for (int s = 0; s < P; ++s)
+    if (s < nk) issue(s);
+
+  for (int s = 0; s < nk; ++s) {
+    // Wait for this wave's loads of step s: those of the later steps issued so far stay outstanding.
+    const int later = min(P - 1, nk - 1 - s);
+    if constexpr (P >= 3) {
+      if (later >= 2) wait_vmcnt<2 * kInst>();
+      else if (later == 1) wait_vmcnt<kInst>();
+      else wait_vmcnt<0>();
+    } else {
+      if (later >= 1) wait_vmcnt<kInst>();
+      else wait_vmcnt<0>();
+    }
+    __syncthreads();  // every wave's step-s data is in LDS; the slot of step s-1 is free
+    if (s + P < nk) issue(s + P);
+
+    const uint8_t* st = ring + (s % NSTAGE) * kStageBytes;
+    const float* sa = reinterpret_cast<const float*>(st);
+    const __bf16* sb = reinterpret_cast<const __bf16*>(st + kABytes);
+    float4 ra[2][FM][2];
+    bf16x8 fb[2][FN];
+    auto read_frags = [&](int ks, int slot) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int r = wm * TM + i * 32 + frow;
+        const int c0 = 4 * ks + 2 * khalf;  // two f32 chunks: k = 16 ks + 8 khalf .. +8
+        const int sw = x_swizzle(r);
+        ra[slot][i][0] = *reinterpret_cast<const float4*>(sa + r * BK + ((c0 ^ sw) << 2));
+        ra[slot][i][1] = *reinterpret_cast<const float4*>(sa + r * BK + (((c0 + 1) ^ sw) << 2));
+      }
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int r = wn * TN + j * 32 + frow;
+        const int c = 2 * ks + khalf;
+        fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + r * BK + ((c ^ w_swizzle(r)) << 3));
+      }
+    };
+    read_frags(0, 0);
+    read_frags(1, 1);
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 a[FM];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const uint2 l2 = round_bf16x4(ra[ks][i][0]), h2 = round_bf16x4(ra[ks][i][1]);
+        a[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], fb[ks][j], acc[i][j], 0, 0, 0);
+    }
+  }
+
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const int col = m0 + wn * TN + j * 32 + frow;
     if (col >= p.m) continue;
-    const float b = (p.flags & 1u) ? p.bias[col] : 0.f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = n0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int row = n0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < p.n) {
-          float o = acc[i][j][v];
-          if (p.flags & 1u) o += b;
-          if (p.flags & 2u) o = gelu_erf(o);
           float* yp = p.y + static_cast<long long>(row) * p.m + col;
+          float o = acc[i][j][v] + bias_v[j];
+          if (p.flags & 2u) o = gelu_erf(o);
           if (p.flags & 4u) o += *yp;
           *yp = o;
         }
@@ -277,17 +512,76 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(GemmParams p) {
   }
 }
 
+int device_cus() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] <= 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cus[dev] = v;
+  }
+  return cus[dev];
+}
+
+template <int WT, int BM, int BN, int WM, int WN>
+hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
+  const int tiles_m = (p.n + BM - 1) / BM;
+  const int tiles_n = (p.m + BN - 1) / BN;
+  const int tiles = tiles_m * tiles_n;
+  int splits = 1;
+  // Split the k range when the tiles alone leave most CUs idle and the
+  // epilogue allows adding partial sums into Y (accumulate, no GELU).
+  const int nk = (p.k + BK - 1) / BK;
+  if ((p.flags & 4u) && !(p.flags & 2u)) {
+    const int cus = device_cus();
+    while (tiles * splits * 2 <= cus * 3 / 2 && nk / (splits * 2) >= 4) splits *= 2;
+  }
+  const int per_xcd = (tiles + 7) / 8;
+  dim3 grid(per_xcd * 8, 1, splits);
+  hipLaunchKernelGGL((gemm_kernel<WT, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NSTAGE>
+hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
+  const int tiles_m = (p.n + BM - 1) / BM;
+  const int tiles_n = (p.m + BN - 1) / BN;
+  const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE>), dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream,
+                     p, tiles_m, tiles_n);
+  return hipGetLastError();
+}
+
+template <int WT>
+hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
+  // The pipelined bf16 kernel addresses operands with 32-bit byte offsets.
+  const bool small_enough = static_cast<long long>(p.n) * p.k * 4 < (1LL << 32) &&
+                            static_cast<long long>(p.m) * p.rowbytes < (1LL << 32);
+  if constexpr (WT == kBF16) {
+    if (!small_enough) return launch_tile<WT, 128, 128, 2, 2>(p, stream);
+    const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
+    // Measured on MI355X at n = 1500: 128 x 256 tiles win once they give at least half the CUs
+    // a tile; below that, 128 x 128 tiles (more of them) do. Both use 8 waves.
+    if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 4>(p, stream);
+    return launch_bf16<128, 128, 2, 4, 4>(p, stream);
+  }
+  // Wide tiles (128 X rows x 256 W rows) when they still give every CU work,
+  // 128 x 128 otherwise.
+  const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
+  if (wide_tiles >= device_cus() / 2) return launch_tile<WT, 128, 256, 2, 2>(p, stream);
+  return launch_tile<WT, 128, 128, 2, 2>(p, stream);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream) {
-  dim3 grid((p.m + BN - 1) / BN, (p.n + BM - 1) / BM);
   switch (wtype) {
-    case kBF16: hipLaunchKernelGGL(gemm_kernel<kBF16>, grid, dim3(kThreads), 0, stream, p); break;
-    case kQ8_0: hipLaunchKernelGGL(gemm_kernel<kQ8_0>, grid, dim3(kThreads), 0, stream, p); break;
-    case kQ4_0: hipLaunchKernelGGL(gemm_kernel<kQ4_0>, grid, dim3(kThreads), 0, stream, p); break;
+    case kBF16: return launch_wt<kBF16>(p, stream);
+    case kQ8_0: return launch_wt<kQ8_0>(p, stream);
+    case kQ4_0: return launch_wt<kQ4_0>(p, stream);
     default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 }  // namespace wq

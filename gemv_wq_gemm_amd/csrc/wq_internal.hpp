@@ -34,6 +34,12 @@ struct MatvecParams {
 hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tokens_per_expert,
                          hipStream_t stream);
 
+// The sliced kernel (k a multiple of 1024, at most 8192), which launch_matvec
+// prefers when it applies; the general kernel takes every other k.
+bool matvec_sliced_supports(int k);
+hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tokens_per_expert,
+                                hipStream_t stream);
+
 // y[t][j] = sum_s gate[t*top_k + s] * slots[(t*top_k + s)][j], summed in s order.
 hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, int n_tok,
                               int top_k, int m, hipStream_t stream);

@@ -58,7 +58,7 @@ struct Geometry {
 };
 
 template <int WT, int NTC, int KB, int RW>
-__global__ __launch_bounds__(kThreads) void matvec_kernel(MatvecParams p) {
+__global__ __launch_bounds__(kThreads) void matvec_general_kernel(MatvecParams p) {
   using G = Geometry<WT, KB>;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves * RW * G::kRowLds];
 
@@ -265,7 +265,7 @@ template <int WT, int NTC, int KB, int RW>
 hipError_t launch_variant(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   const int rows_per_wg = kWaves * RW;
   dim3 grid((p.m + rows_per_wg - 1) / rows_per_wg, n_exp_rows);
-  hipLaunchKernelGGL((matvec_kernel<WT, NTC, KB, RW>), grid, dim3(kThreads), 0, stream, p);
+  hipLaunchKernelGGL((matvec_general_kernel<WT, NTC, KB, RW>), grid, dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -350,6 +350,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* w, float
 }  // namespace
 
 hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStream_t stream) {
+  if (matvec_sliced_supports(p.k)) return launch_matvec_sliced(wtype, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;
   switch (wtype) {
     case kBF16: return launch_wt<kBF16>(p, max_tok, n_exp_rows, stream);

@@ -228,3 +228,42 @@ def test_moe_all_tokens_on_one_expert_equals_the_16_row_layer():
     got = _run_moe(x, bank, wtype, ids, None, n_exp, m, k)
     y_ref, S = oracle.linear(x, bank[3], wtype, m, k)
     assert_within(got, y_ref, B_F32 * S + 1e-12)
+
+
+# ---------------------------------------------------------------- sliced matvec kernel (k % 1024 == 0)
+
+SLICED_SHAPES = [(1, 1024), (17, 2048), (100, 3072), (33, 8192), (530, 4096)]
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 16])
+@pytest.mark.parametrize("m,k", SLICED_SHAPES)
+def test_matvec_sliced_parity(wtype, n, m, k):
+    flags = [0, 1, 3, 7, 4, 6][(n + m + wtype) % 6]
+    x, w, bias, y_old = _inputs(12, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_MATVEC)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_F32)
+    assert_within(got, y_ref, tol, f"sliced wtype={wtype} n={n} m={m} k={k} flags={flags}")
+
+
+@pytest.mark.parametrize("wtype", WTYPES)
+@pytest.mark.parametrize("n_tok,n_exp,top_k,m,k", [(16, 4, 2, 75, 1024), (1, 8, 2, 300, 4096),
+                                                   (40, 3, 1, 64, 2048), (7, 5, 3, 129, 8192)])
+@pytest.mark.parametrize("gated", [False, True])
+def test_moe_sliced_parity(wtype, n_tok, n_exp, top_k, m, k, gated):
+    x, bank, ids, gates = _moe_inputs(13, wtype, n_tok, n_exp, top_k, m, k)
+    got = _run_moe(x, bank, wtype, ids, gates if gated else None, n_exp, m, k)
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k, gates if gated else None)
+    assert_within(got, y_ref, B_F32 * S + 8 * 2.0 ** -24 * np.abs(y_ref), "moe sliced")
+
+
+def test_moe_sliced_out_of_range_ids():
+    wtype, n_tok, n_exp, top_k, m, k = wq.W_Q8_0, 6, 4, 2, 50, 1024
+    x, bank, ids, gates = _moe_inputs(14, wtype, n_tok, n_exp, top_k, m, k)
+    bad = ids.copy()
+    bad[1, 0] = 4
+    got = _run_moe(x, bank, wtype, bad, None, n_exp, m, k)
+    assert np.isnan(got[2]).all()
+    ok = [s for s in range(n_tok * top_k) if s != 2]
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k)
+    assert_within(got[ok], y_ref[ok], B_F32 * S[ok] + 1e-12, "moe sliced valid slots")
