@@ -233,8 +233,9 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
   p.k = static_cast<int>(k);
   p.rowbytes = ebytes / m;
   p.flags = 0;
-  // Expected slots per expert picks the tokens-per-pass variant; more per expert is still exact.
-  const int64_t per_expert = (n_slots + n_experts - 1) / n_experts;
+  // Twice the mean count of slots per expert picks the tokens-per-pass variant: an expert
+  // holding more than that is rare, and is still served exactly by a further pass over its rows.
+  const int64_t per_expert = 2 * ((n_slots + n_experts - 1) / n_experts);
   hipError_t e = wq::launch_matvec(wtype, p, static_cast<int>(per_expert < n_tok ? per_expert : n_tok), s);
   if (e != hipSuccess) return hip_fail(e, "MoE matvec launch");
   if (gate_w) {

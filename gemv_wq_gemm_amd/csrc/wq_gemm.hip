@@ -33,6 +33,7 @@
 
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
+#include "wq_lds_dma.hpp"
 
 namespace wq {
 namespace {
@@ -315,41 +316,13 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 //  * Both operands stream from global memory straight into LDS with global_load_lds_dwordx4, so
 //    the loads in flight hold no registers; X stays f32 in LDS and is rounded to bf16 (nearest
 //    even) as its fragments are read.
-//  * The loads are issued through inline assembly and waited for with explicit vmcnt counts; the
-//    compiler cannot tell which LDS bytes such a load writes and would otherwise wait for all of
-//    them before every LDS read. Their destinations are LDS only, so no register is ever live
-//    across an unfinished load. Waits the compiler inserts for its own loads can only over-wait,
-//    since vector memory loads complete in issue order.
+//  * The loads are waited for with explicit vmcnt counts (wq_lds_dma.hpp).
 //  * LDS rows are XOR-swizzled by row so that the 16 lanes served per LDS cycle read 16 distinct
 //    groups of four banks: X rows (32 f32 = 8 chunks of 16 bytes) keep chunk c at
 //    c ^ ((r >> 1) & 7), W rows (32 bf16 = 4 chunks) at c ^ ((r >> 2) & 3).
 //  * A direct-to-LDS load writes lane l's 16 bytes at (LDS base + 16 l); each lane fetches the
 //    global chunk that belongs at its LDS position. Rows past the end of X or W are clamped to the
 //    last row (their products land only in outputs that are never stored).
-
-// M0 is listed as clobbered for the reader; the compiler treats it as reserved and does not
-// otherwise use it in these kernels (checked in the generated code).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(base), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt out of range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ uint32_t lds_address(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const void __attribute__((address_space(3)))*)p));
-}
 
 __device__ __forceinline__ int x_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int w_swizzle(int r) { return (r >> 2) & 3; }

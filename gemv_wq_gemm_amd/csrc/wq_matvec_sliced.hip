@@ -8,25 +8,39 @@
 //
 // Layout of the work (gfx950, wave64):
 //  * A workgroup has k/1024 waves; wave w owns the k-slice [1024 w, 1024 w + 1024)
-//    of every row, and lane l owns 16 elements of it: half h = l & 1 of block
-//    32 w + l/2. Its activations for up to NTC tokens sit in 16*NTC VGPRs and
-//    are loaded once per workgroup, then reused for every row it visits.
-//  * The workgroup walks a run of row tiles (R rows each). For a tile, each wave
-//    copies its slice of the R rows (R contiguous segments of 32 blocks) into
-//    its LDS region with 16-byte loads spread evenly over the 64 lanes; the next
-//    tile's loads are in flight while the current tile is computed.
+//    of every row, and each lane owns 16 elements of it, in 2 lanes per 32-element
+//    block. Its activations for up to NTC tokens sit in 16*NTC VGPRs, loaded once
+//    per workgroup and reused for every row it visits.
+//  * The workgroup walks a run of row tiles (R rows each). Each wave streams its
+//    slice of a tile (R contiguous segments of 32 blocks) straight into its own
+//    ring of NSTAGE LDS slots with direct-to-LDS loads, NSTAGE-1 tiles ahead of
+//    the one it computes. Only the wave that loads a slot reads it, so the ring
+//    needs no barrier; the loads hold no registers while in flight.
+//  * Element ownership per 32-element block (half h = lane & 1):
+//      bf16, Q8_0: elements 16h .. 16h+15;
+//      Q4_0:       bytes 8h .. 8h+7 of the quants, i.e. elements 8h .. 8h+7 (low
+//                  nibbles) and 16+8h .. 16+8h+7 (high nibbles). A byte select
+//                  (SDWA) feeds each nibble to v_cvt_off_f32_i4, which yields
+//                  (q-8)/16 exactly once the nibble is XOR-ed with 8; the block
+//                  scale is taken as 16 d to compensate.
 //  * A lane's 16 products per row and token are summed in f32 and scaled once by
-//    the block's f16 scale. The 64 lane partials of the R rows are then summed
-//    by a register transpose (v_permlane32_swap, v_permlane16_swap, DPP): each
-//    step halves the values a lane holds, so R rows cost about R adds per lane
-//    instead of 6 R. The k-slices of the waves are added in wave order through
-//    LDS, and one lane per (row, token) applies the epilogue and stores.
+//    the block scale. The 64 lane partials of the R rows are then summed by a
+//    register transpose (v_permlane32_swap, v_permlane16_swap, DPP): each step
+//    halves the values a lane holds, so R rows cost about R adds per lane instead
+//    of 6 R.
+//  * A wave leaves its per-row partial sums in LDS and goes on to its next tile
+//    without waiting for the other waves. Every kFlushRows rows the workgroup
+//    synchronizes once, adds the k-slices of each row in wave order, applies the
+//    epilogue and stores. An epilogue that reads memory (bias, residual) would make
+//    the compiler wait for every ring load in flight, so such launches give each
+//    workgroup at most one flush of rows.
 //  * Rounding: a 16-term chain, one scale, a 6-level tree and at most 8 slice
 //    additions per output -- far inside 1e-5 * sum |x w|.
 #include <hip/hip_runtime.h>
 
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
+#include "wq_lds_dma.hpp"
 
 namespace wq {
 namespace {
@@ -37,8 +51,6 @@ struct Slice {
   static constexpr int kSegBytes = 32 * BB;          // one wave's 1024-element slice of a row
   static constexpr int kSegPieces = kSegBytes / 16;  // 68 (Q8_0), 36 (Q4_0), 128 (bf16)
 };
-
-__device__ __forceinline__ void wave_lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v) {
@@ -59,13 +71,17 @@ __device__ __forceinline__ void transpose_sum(float (&v)[R], int lane) {
       v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
   }
-  // xor 16: the same per pair of 16-lane groups.
+  // xor 16: the same per pair of 16-lane groups (with one row left, both operands are that
+  // row, and the sum is its total over each 32-lane half).
   if constexpr (R >= 4) {
 #pragma unroll
     for (int i = 0; i < R / 4; ++i) {
       auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + R / 4]), false, false);
       v[i] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
     }
+  } else {
+    auto s = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[0]), __float_as_uint(v[0]), false, false);
+    v[0] = __uint_as_float(s[0]) + __uint_as_float(s[1]);
   }
   // xor 8 (rotate by 8 inside 16 lanes): lanes with bit 3 clear keep the lower
   // half of their values and send the upper half, the others the reverse.
@@ -93,19 +109,88 @@ __device__ __forceinline__ void transpose_sum(float (&v)[R], int lane) {
   v[0] += dpp<0xB1>(v[0]);  // xor 1 inside quads
 }
 
-template <int WT, int NTC, int R, int MAXW>
+// Rows whose per-wave partial sums a workgroup holds in LDS before it adds them up.
+constexpr int kFlushRows = 128;
+
+// Decodes this lane's 16 weights of one block held in LDS at byte `boff` from `lds`
+// (element order as described above) and returns the factor that scales their sum.
+template <int WT>
+__device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int h, float (&wv)[16]) {
+  if constexpr (WT == kBF16) {
+    const uint4 a = *reinterpret_cast<const uint4*>(lds + boff + 32 * h);
+    const uint4 b = *reinterpret_cast<const uint4*>(lds + boff + 32 * h + 16);
+    const uint32_t q[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      wv[2 * i] = bf16_lo(q[i]);
+      wv[2 * i + 1] = bf16_hi(q[i]);
+    }
+    return 1.f;
+  } else if constexpr (WT == kQ8_0) {
+    const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + boff));
+    const int qo = boff + 2 + 16 * h;  // quants 16h .. 16h+15
+    const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(lds) + (qo >> 2);
+    uint32_t dw[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) dw[i] = a[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t q = realign(dw[i + 1], dw[i], sh);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) wv[4 * i + b] = q8_at(q, b);
+    }
+    return d;
+  } else {
+    const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + boff));
+    const int qo = boff + 2 + 8 * h;  // quant bytes 8h .. 8h+7
+    const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(lds) + (qo >> 2);
+    uint32_t dw[3];
+#pragma unroll
+    for (int i = 0; i < 3; ++i) dw[i] = a[i];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const uint32_t lo = realign(dw[i + 1], dw[i], sh) ^ 0x88888888u;
+      const uint32_t hi = __builtin_amdgcn_alignbit(lo, lo, 4);  // high nibbles into the low ones
+      wv[4 * i] = __builtin_amdgcn_cvt_off_f32_i4(lo);
+      wv[8 + 4 * i] = __builtin_amdgcn_cvt_off_f32_i4(hi);
+#pragma unroll
+      for (int b = 1; b < 4; ++b) {
+        wv[4 * i + b] = __builtin_amdgcn_cvt_off_f32_i4((lo >> (8 * b)) & 0xFFu);
+        wv[8 + 4 * i + b] = __builtin_amdgcn_cvt_off_f32_i4((hi >> (8 * b)) & 0xFFu);
+      }
+    }
+    return 16.f * d;
+  }
+}
+
+// First element, within the lane's 1024-element k-slice, of each run of 8 activations the
+// lane multiplies (two runs per block; see the ownership above).
+template <int WT>
+__device__ __forceinline__ int x_run(int lane, int run) {
+  const int bl = lane >> 1, h = lane & 1;
+  if constexpr (WT == kQ4_0) return bl * 32 + 8 * h + 16 * run;
+  return bl * 32 + 16 * h + 8 * run;
+}
+
+template <int WT, int NTC, int R, int NSTAGE, int MAXW>
 __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p, int tiles_per_wg) {
   using S = Slice<WT>;
   constexpr int kTilePieces = R * S::kSegPieces;
-  constexpr int NL = (kTilePieces + 63) / 64;  // 16-byte loads per lane per tile
+  constexpr int NL = (kTilePieces + 63) / 64;  // direct-to-LDS loads per lane per tile
+  // +16: the covering dwords of the slot's last block may reach 4 bytes past the tile.
+  constexpr int kSlotBytes = NL * 1024 + 16;
   constexpr int kLanesPerRow = 64 / R;
+  constexpr int kFlushTiles = kFlushRows / R;
+  static_assert(NSTAGE >= 2 && NL * (NSTAGE - 2) < 64, "vmcnt range");
+  static_assert(R >= 2 && R <= 16 && (R & (R - 1)) == 0, "rows per tile: a power of two in 2..16");
 
-  // +16: the covering dwords of a wave's last block may reach 4 bytes past its region.
-  __shared__ __attribute__((aligned(16))) uint8_t seg_lds[MAXW * R * S::kSegBytes + 16];
-  __shared__ float cw[2][MAXW * R * NTC];
+  __shared__ __attribute__((aligned(16))) uint8_t ring_lds[MAXW * NSTAGE * kSlotBytes];
+  __shared__ float part[kFlushRows * NTC * MAXW];  // [row][token][wave]
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int e = blockIdx.y;
   const bool moe = p.ids != nullptr;
@@ -131,38 +216,37 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
     return;
   }
 
-  uint8_t* seg = seg_lds + wave * (R * S::kSegBytes);
   const uint8_t* wexp = p.w + static_cast<long long>(e) * p.expert_bytes;
+  const int ring_off = wave * (NSTAGE * kSlotBytes);
+  const uint32_t ring_addr = lds_address(ring_lds) + ring_off;
 
-  // Loop-invariant part of this lane's load addresses: piece q = lane + 64 i of
-  // the tile is 16 bytes of row q / P at slice offset 16 (q % P).
-  int off[NL];
+  // Piece q = lane + 64 i of a tile is 16 bytes of tile row q / P at slice offset 16 (q % P).
+  // Lanes past the tile's last piece fetch that piece again (same cache line) into the slot's
+  // spare bytes; rows past the end of W read its last row (their sums are never stored).
   int prow[NL];
+  uint32_t pcol[NL];
 #pragma unroll
   for (int i = 0; i < NL; ++i) {
-    const int q = lane + 64 * i;
+    const int q = min(lane + 64 * i, kTilePieces - 1);
     const int r = q / S::kSegPieces;
-    prow[i] = q < kTilePieces ? r : R;  // R marks a lane with no piece here
-    off[i] = r * static_cast<int>(p.rowbytes) + wave * S::kSegBytes + (q - r * S::kSegPieces) * 16;
+    prow[i] = r;
+    pcol[i] = static_cast<uint32_t>(wave * S::kSegBytes + (q - r * S::kSegPieces) * 16);
   }
+  const uint32_t rowbytes = static_cast<uint32_t>(p.rowbytes);
 
-  // This lane's share of a row: half h of block bl of the wave's slice.
-  const int bl = lane >> 1;
-  const int h = lane & 1;
-  const int kofs = wave * 1024 + lane * 16;  // first of its 16 elements
-
-  auto issue = [&](int tile, uint4 (&st)[NL]) {
+  auto issue = [&](int tile) {
     const int row0 = tile * R;
     const uint8_t* base = wexp + static_cast<long long>(row0) * p.rowbytes;
+    const int last = p.m - 1 - row0;
+    const uint32_t dst = ring_addr + static_cast<uint32_t>((tile % NSTAGE) * kSlotBytes);
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (prow[i] < R && row0 + prow[i] < p.m) v = *reinterpret_cast<const uint4*>(base + off[i]);
-      st[i] = v;
-    }
+    for (int i = 0; i < NL; ++i)
+      load_lds16(base, static_cast<uint32_t>(min(prow[i], last)) * rowbytes + pcol[i], dst + i * 1024);
   };
 
-  int parity = 0;
+  const int h = lane & 1;
+  const int blk_off = (lane >> 1) * S::BB;  // this lane's block within a row segment
+
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
     if (moe) {
@@ -186,22 +270,23 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
         }
       }
 
-      uint4 st[NL];
-      issue(t_begin, st);
-
       float xr[NTC][16];
 #pragma unroll
       for (int t = 0; t < NTC; ++t) {
         if (slot[t] >= 0) {
-          const float4* xp = reinterpret_cast<const float4*>(
-              p.x + static_cast<long long>(slot[t] / p.top_k) * p.k + kofs);
+          const float* xs = p.x + static_cast<long long>(slot[t] / p.top_k) * p.k + wave * 1024;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float4 v = xp[i];
-            xr[t][4 * i] = v.x;
-            xr[t][4 * i + 1] = v.y;
-            xr[t][4 * i + 2] = v.z;
-            xr[t][4 * i + 3] = v.w;
+          for (int run = 0; run < 2; ++run) {
+            const float4* xp = reinterpret_cast<const float4*>(xs + x_run<WT>(lane, run));
+            const float4 v0 = xp[0], v1 = xp[1];
+            xr[t][8 * run + 0] = v0.x;
+            xr[t][8 * run + 1] = v0.y;
+            xr[t][8 * run + 2] = v0.z;
+            xr[t][8 * run + 3] = v0.w;
+            xr[t][8 * run + 4] = v1.x;
+            xr[t][8 * run + 5] = v1.y;
+            xr[t][8 * run + 6] = v1.z;
+            xr[t][8 * run + 7] = v1.w;
           }
         } else {
 #pragma unroll
@@ -209,86 +294,59 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
         }
       }
 
-      for (int tile = t_begin; tile < t_end; ++tile) {
-        // Stage this tile's slice into LDS, then start the next tile's loads.
-        wave_lds_sync();
+      // Prologue: the first NSTAGE-1 tiles in flight.
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-          if (prow[i] < R) reinterpret_cast<uint4*>(seg)[lane + 64 * i] = st[i];
-        wave_lds_sync();
-        if (tile + 1 < t_end) issue(tile + 1, st);
+      for (int s = 0; s < NSTAGE - 1; ++s)
+        if (t_begin + s < t_end) issue(t_begin + s);
 
-        float acc[NTC][R];
+      for (int f0 = t_begin; f0 < t_end; f0 += kFlushTiles) {
+        const int f1 = min(t_end, f0 + kFlushTiles);
+        // Each wave runs through the tiles of this flush on its own: no barrier per tile.
+        for (int tile = f0; tile < f1; ++tile) {
+          // This wave's loads of `tile` have landed once only those of later tiles are pending.
+          wait_groups<NL, NSTAGE - 2>(min(NSTAGE - 2, t_end - 1 - tile));
+          // The slot of tile-1 is free (its reads were consumed last iteration): refill it.
+          if (tile + NSTAGE - 1 < t_end) issue(tile + NSTAGE - 1);
+
+          const int seg = ring_off + (tile % NSTAGE) * kSlotBytes;
+          float acc[NTC][R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) {
-          const uint8_t* blk = seg + r * S::kSegBytes + bl * S::BB;
-          float wv[16];
-          float d = 1.f;
-          if constexpr (WT == kBF16) {
-            const uint4 a = *reinterpret_cast<const uint4*>(blk + 32 * h);
-            const uint4 b = *reinterpret_cast<const uint4*>(blk + 32 * h + 16);
-            const uint32_t q[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+          for (int r = 0; r < R; ++r) {
+            float wv[16];
+            const float d = decode_lane<WT>(ring_lds, seg + r * S::kSegBytes + blk_off, h, wv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-              wv[2 * i] = bf16_lo(q[i]);
-              wv[2 * i + 1] = bf16_hi(q[i]);
-            }
-          } else {
-            d = f16_to_f32(*reinterpret_cast<const uint16_t*>(blk));
-            // The 16 bytes this lane needs: Q8_0 quants 16h..16h+15; Q4_0 all 16.
-            const int qo = static_cast<int>(blk - seg_lds) + 2 + (WT == kQ8_0 ? 16 * h : 0);
-            const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
-            const uint32_t* a = reinterpret_cast<const uint32_t*>(seg_lds) + (qo >> 2);
-            uint32_t dw[5];
+            for (int t = 0; t < NTC; ++t) {
+              float s = 0.f;
 #pragma unroll
-            for (int i = 0; i < 5; ++i) dw[i] = a[i];
-            uint32_t q[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) q[i] = realign(dw[i + 1], dw[i], sh);
-            if constexpr (WT == kQ8_0) {
-#pragma unroll
-              for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int b = 0; b < 4; ++b) wv[4 * i + b] = q8_at(q[i], b);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                const uint32_t qx = (q[i] ^ 0x88888888u) >> (4 * h);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) wv[4 * i + b] = q4_at(qx, 2 * b);
-              }
+              for (int j = 0; j < 16; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
+              acc[t][r] = d * s;
             }
           }
 #pragma unroll
-          for (int t = 0; t < NTC; ++t) {
-            float s = 0.f;
+          for (int t = 0; t < NTC; ++t) transpose_sum<R>(acc[t], lane);
+          if ((lane & (kLanesPerRow - 1)) == 0) {
+            const int rr = (tile - f0) * R + lane / kLanesPerRow;
 #pragma unroll
-            for (int j = 0; j < 16; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
-            acc[t][r] = d * s;
+            for (int t = 0; t < NTC; ++t) part[(rr * NTC + t) * MAXW + wave] = acc[t][0];
           }
         }
 
-#pragma unroll
-        for (int t = 0; t < NTC; ++t) transpose_sum<R>(acc[t], lane);
-
-        float* cwb = cw[parity];
-        if ((lane & (kLanesPerRow - 1)) == 0) {
-          const int rho = lane / kLanesPerRow;
-#pragma unroll
-          for (int t = 0; t < NTC; ++t) cwb[(wave * R + rho) * NTC + t] = acc[t][0];
-        }
+        // The k-slices of the waves, added in wave order; then the epilogue and the store.
         __syncthreads();
-        if (threadIdx.x < R * NTC) {
-          const int rho = threadIdx.x / NTC;
-          const int t = threadIdx.x - rho * NTC;
-          const int row = tile * R + rho;
+        const int n_out = (f1 - f0) * R * NTC;
+        for (int i = threadIdx.x; i < n_out; i += blockDim.x) {
+          const int rr = i / NTC;
+          const int t = i - rr * NTC;
+          const int row = f0 * R + rr;
           int st_slot = -1;
 #pragma unroll
           for (int u = 0; u < NTC; ++u)
             if (u == t) st_slot = slot[u];
           if (row < p.m && st_slot >= 0) {
             float v = 0.f;
-            for (int w = 0; w < nw; ++w) v += cwb[(w * R + rho) * NTC + t];
+#pragma unroll
+            for (int w = 0; w < MAXW; ++w)
+              if (w < nw) v += part[i * MAXW + w];
             float* yp = p.y + static_cast<long long>(st_slot) * p.m + row;
             if (!moe) {
               if (p.flags & 1u) v += p.bias[row];
@@ -298,7 +356,7 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
             *yp = v;
           }
         }
-        parity ^= 1;
+        __syncthreads();  // part is refilled by the next flush
       }
     }
   }
@@ -327,47 +385,46 @@ int groups_per_cu(void (*kernel)(MatvecParams, int), int threads, int* cache) {
   return *cache;
 }
 
-template <int WT, int NTC, int R>
+template <int WT, int NTC, int R, int NSTAGE>
 hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   const int nw = p.k / 1024;
   const int ntiles = (p.m + R - 1) / R;
-  auto kernel = nw <= 4 ? matvec_sliced_kernel<WT, NTC, R, 4> : matvec_sliced_kernel<WT, NTC, R, 8>;
-  // As many workgroups as are resident at once (no thin second round), split
-  // over the experts; each walks a run of tiles with the next tile in flight.
+  auto kernel = nw <= 4 ? matvec_sliced_kernel<WT, NTC, R, NSTAGE, 4> : matvec_sliced_kernel<WT, NTC, R, NSTAGE, 8>;
+  // As many workgroups as are resident at once (no thin second round), split over the
+  // experts; each walks a run of tiles with NSTAGE-1 of them in flight.
   const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
   static int per_cu[9];  // per variant and wave count
   int groups = groups_per_cu(kernel, 64 * nw, &per_cu[nw]) * device_cus() / experts;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
-  const int tpw = (ntiles + groups - 1) / groups;
+  int tpw = (ntiles + groups - 1) / groups;
+  // An epilogue that reads memory (bias, residual) makes the compiler wait for every load in
+  // flight, so such launches give each workgroup no more rows than one flush holds.
+  if (p.ids == nullptr && (p.flags & 5u) != 0 && tpw * R > kFlushRows) tpw = kFlushRows / R;
   dim3 grid((ntiles + tpw - 1) / tpw, n_exp_rows);
   hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, stream, p, tpw);
   return hipGetLastError();
 }
 
-// Rows per tile: the largest that compiles without spills for this weight type
-// and token count (more rows per tile = fewer, wider reductions).
+// Rows per tile and ring depth for each weight type and token count.
 template <int WT, int NTC>
-constexpr int rows_big() {
-  if constexpr (WT == kBF16) return NTC >= 4 ? 4 : 8;
-  if constexpr (WT == kQ8_0) return NTC >= 2 ? 8 : 16;
-  return NTC >= 4 ? 8 : 16;
-}
+struct SlicedShape {
+  static constexpr int R = WT == kBF16 ? 2 : 4;
+  static constexpr int NSTAGE = 3;
+};
 
 template <int WT, int NTC>
 hipError_t launch_ntc(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
-  constexpr int RBIG = rows_big<WT, NTC>();
-  constexpr int RSMALL = RBIG > 4 ? RBIG / 2 : 4;
-  const long long tiles_big = (static_cast<long long>(p.m) + RBIG - 1) / RBIG * (n_exp_rows > 1 ? n_exp_rows - 1 : 1);
-  if (tiles_big >= 512) return launch_r<WT, NTC, RBIG>(p, n_exp_rows, stream);
-  return launch_r<WT, NTC, RSMALL>(p, n_exp_rows, stream);
+  using C = SlicedShape<WT, NTC>;
+  return launch_r<WT, NTC, C::R, C::NSTAGE>(p, n_exp_rows, stream);
 }
 
 template <int WT>
 hipError_t launch_wt(const MatvecParams& p, int max_tok, int n_exp_rows, hipStream_t stream) {
   if (max_tok <= 1) return launch_ntc<WT, 1>(p, n_exp_rows, stream);
   if (max_tok <= 2) return launch_ntc<WT, 2>(p, n_exp_rows, stream);
-  return launch_ntc<WT, 4>(p, n_exp_rows, stream);
+  if (max_tok <= 4) return launch_ntc<WT, 4>(p, n_exp_rows, stream);
+  return launch_ntc<WT, 8>(p, n_exp_rows, stream);
 }
 
 }  // namespace
