@@ -9,10 +9,19 @@ the step's time, with every input resident in HBM. To keep the 256 MB
 Infinity Cache from serving the weights, the calls rotate over 36 distinct
 copies of W (641 MB), so every call streams its weight from HBM.
 
+The timed region runs the K steps' calls as two back-to-back phases on one
+stream (the K n=1 calls, then the K n=4 calls), with a HIP event at the start,
+between the phases and at the end. No event sits between two launches, so each
+phase's time over K is that kernel's mean launch duration (as a kernel trace
+sees it, plus the gap between back-to-back dispatches). Calls go through
+bound calls (argument conversion done once), so the host keeps ahead of the GPU.
+
 The same JSON line carries:
   roofline      the dominant kernel's weight bytes per launch over its mean
-                launch time (HIP events around every launch on the stream the
-                kernel runs on), against the 8 TB/s HBM peak;
+                launch time, against the 8 TB/s HBM peak; `traffic` is the HBM
+                bytes per launch that FETCH_SIZE / WRITE_SIZE counted for that
+                kernel (profiles/, scaled by a copy kernel of known size), or
+                null when the kernel sources changed since they were counted;
   cpu_baseline  the f64 oracle (decode + product, numpy/OpenBLAS) on a
                 bounded sample of the same workload, on the host's cores;
   others        the remaining workloads (bf16 GEMM 64x256x256, Q4_0 matvec
@@ -29,6 +38,7 @@ import time
 
 import numpy as np
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 ROTATE_BYTES = 600 * 2 ** 20
@@ -46,30 +56,6 @@ def _parse():
                     help="first run an elementwise copy of 256 MiB (reads and writes that many bytes), "
                          "the reference for scaling HBM byte counters")
     return ap.parse_args()
-
-
-class Timeline:
-    """HIP events recorded on one stream around every launch of a timed region."""
-
-    def __init__(self, torch, stream):
-        self.torch, self.stream, self.events, self.tags = torch, stream, [], []
-
-    def mark(self, tag=None):
-        ev = self.torch.cuda.Event(enable_timing=True)
-        ev.record(self.stream)
-        self.events.append(ev)
-        self.tags.append(tag)
-
-    def spans(self):
-        """{tag: [ms, ...]} of each span that starts at a mark with that tag."""
-        out = {}
-        for i in range(len(self.events) - 1):
-            if self.tags[i] is not None:
-                out.setdefault(self.tags[i], []).append(self.events[i].elapsed_time(self.events[i + 1]))
-        return out
-
-    def total_ms(self):
-        return self.events[0].elapsed_time(self.events[-1])
 
 
 def _copies(make, nbytes):
@@ -117,34 +103,32 @@ def main():
     xs = {n: to_dev(synth.config_q8_matvec(n)["x"]) for n in (1, 4)}
     ys = {n: torch.empty((n, m), dtype=torch.float32, device=dev) for n in (1, 4)}
 
-    call = [0]
+    binds = {n: [wq.bind_gemm(xs[n], W[c], wq.W_Q8_0, m=m, k=k, out=ys[n]) for c in range(ncopy)]
+             for n in (1, 4)}
 
-    def step(tl=None):
+    for i in range(args.warmup):
         for n in (1, 4):
-            c = call[0] % ncopy
-            call[0] += 1
-            if tl is not None:
-                tl.mark(f"n{n}")
-            wq.gemm(xs[n], W[c], wq.W_Q8_0, m=m, k=k, out=ys[n])
-
-    for _ in range(args.warmup):
-        step()
+            binds[n][i % ncopy]()
     torch.cuda.synchronize()
-    tl = Timeline(torch, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
     t0 = time.perf_counter()
-    tl.mark()
-    for _ in range(args.steps):
-        step(tl)
-    tl.mark()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        binds[1][i % ncopy]()
+    ev[1].record(stream)
+    for i in range(args.steps):
+        binds[4][i % ncopy]()
+    ev[2].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_total = tl.total_ms()
+    ms_total = ev[0].elapsed_time(ev[2])
     ms_step = ms_total / args.steps
     value = 2 * wbytes / (ms_step * 1e-3) / 1e9
-    spans = tl.spans()
-    kern = {tag: float(np.mean(v)) for tag, v in spans.items()}
-    dom = max(kern, key=lambda t: kern[t] * len(spans[t]))
+    kern = {"n1": ev[0].elapsed_time(ev[1]) / args.steps, "n4": ev[1].elapsed_time(ev[2]) / args.steps}
+    dom = max(kern, key=kern.get)
     achieved = wbytes / (kern[dom] * 1e-3) / 1e9
+    from gemv_wq_gemm_amd.rocprof_summary import read_traffic
+    traffic = read_traffic(os.path.join(ROOT, "profiles", "matvec_q8_0_4096x4096_hbm_counters.md"), dom)
 
     line = {
         "metric": "matvec weight GB/s (Q8_0 decode, 1 MI355X)",
@@ -173,7 +157,7 @@ def main():
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": None if traffic is None else round(traffic),
             "mean_launch_us": {t: round(v * 1e3, 3) for t, v in kern.items()},
         },
         "device": props.name,
@@ -190,17 +174,17 @@ def main():
 
 
 def _time_calls(torch, stream, fn, reps, warm=3):
+    """Mean ms per call of `reps` back-to-back calls (events only around the whole run)."""
     for i in range(warm):
         fn(i)
     torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(reps):
         fn(i)
-        ev[i + 1].record(stream)
+    e1.record(stream)
     torch.cuda.synchronize()
-    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
-    return float(np.median(per)), float(np.mean(per))
+    return e0.elapsed_time(e1) / reps
 
 
 def _others(torch, wq, synth, dev, stream, to_dev):
@@ -209,8 +193,8 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     c = synth.config_gemm_small()
     x, w, b = to_dev(c["x"]), to_dev(c["w"]), to_dev(c["bias"])
     y = torch.empty((64, 256), device=dev)
-    med, mean = _time_calls(torch, stream, lambda i: wq.gemm(x, w, wq.W_BF16, m=256, k=256, bias=b, gelu=True,
-                                                             out=y), 200)
+    g = wq.bind_gemm(x, w, wq.W_BF16, m=256, k=256, bias=b, gelu=True, out=y)
+    med = _time_calls(torch, stream, lambda i: g(), 200)
     fl = 2 * 64 * 256 * 256
     out["gemm_bf16_64x256x256"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 3),
                                    "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}
@@ -223,7 +207,8 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     Wc = torch.stack([torch.roll(base.view(m, -1), shifts=7 * i, dims=0).reshape(-1) for i in range(nc)])
     x = to_dev(synth.config_q4_matvec()["x"])
     y = torch.empty((1, m), device=dev)
-    med, mean = _time_calls(torch, stream, lambda i: wq.gemm(x, Wc[i % nc], wq.W_Q4_0, m=m, k=k, out=y), 100)
+    gs = [wq.bind_gemm(x, Wc[i], wq.W_Q4_0, m=m, k=k, out=y) for i in range(nc)]
+    med = _time_calls(torch, stream, lambda i: gs[i % nc](), 100)
     out["matvec_q4_0_14336x4096_n1"] = {"us": round(med * 1e3, 3), "GB/s": round(wb / (med * 1e-3) / 1e9, 1),
                                         "frac_hbm": round(wb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                                         "copies": nc}
@@ -238,8 +223,8 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     x, ids, gates = to_dev(cm["x"]), to_dev(cm["ids"]), to_dev(cm["gates"])
     y = torch.empty((16, m), device=dev)
     touched = len(np.unique(cm["ids"]))
-    med, mean = _time_calls(torch, stream, lambda i: wq.moe_matvec(x, banks[i % 3], wq.W_Q4_0, ids, gates,
-                                                                   n_experts=8, m=m, k=k, out=y), 60)
+    med = _time_calls(torch, stream, lambda i: wq.moe_matvec(x, banks[i % 3], wq.W_Q4_0, ids, gates,
+                                                             n_experts=8, m=m, k=k, out=y), 60)
     mb = touched * wb
     out["moe_q4_0_16tok_top2_of_8"] = {"us": round(med * 1e3, 3), "GB/s": round(mb / (med * 1e-3) / 1e9, 1),
                                        "frac_hbm": round(mb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -258,14 +243,18 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     qkv = torch.empty((n, 3 * d), device=dev)
     f = torch.empty((n, ff), device=dev)
 
-    def chain(_):
-        for W_ in layers:
-            wq.gemm(a1, W_["qkv"][0], wq.W_BF16, m=3 * d, k=d, bias=W_["qkv"][1], out=qkv)
-            wq.gemm(a2, W_["out"][0], wq.W_BF16, m=d, k=d, bias=W_["out"][1], residual=True, out=h)
-            wq.gemm(a3, W_["fc1"][0], wq.W_BF16, m=ff, k=d, bias=W_["fc1"][1], gelu=True, out=f)
-            wq.gemm(f, W_["fc2"][0], wq.W_BF16, m=d, k=ff, bias=W_["fc2"][1], residual=True, out=h)
+    calls = []
+    for W_ in layers:
+        calls.append(wq.bind_gemm(a1, W_["qkv"][0], wq.W_BF16, m=3 * d, k=d, bias=W_["qkv"][1], out=qkv))
+        calls.append(wq.bind_gemm(a2, W_["out"][0], wq.W_BF16, m=d, k=d, bias=W_["out"][1], residual=True, out=h))
+        calls.append(wq.bind_gemm(a3, W_["fc1"][0], wq.W_BF16, m=ff, k=d, bias=W_["fc1"][1], gelu=True, out=f))
+        calls.append(wq.bind_gemm(f, W_["fc2"][0], wq.W_BF16, m=d, k=ff, bias=W_["fc2"][1], residual=True, out=h))
 
-    med, mean = _time_calls(torch, stream, chain, 10, warm=2)
+    def chain(_):
+        for c in calls:
+            c()
+
+    med = _time_calls(torch, stream, chain, 10, warm=2)
     fl = 24 * 2 * n * (3 * d * d + d * d + ff * d + d * ff)
     out["encoder_chain_bf16_24x4_n1500"] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
                                             "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}

@@ -150,6 +150,38 @@ def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, res
     return out
 
 
+class BoundGemm:
+    """One ``wq_gemm_ex`` call with every argument resolved up front.
+
+    For loops that call the same layer on the same buffers again and again (a
+    timing loop, a decode step): calling the object costs one ctypes call, with
+    no tensor inspection. The tensors given to :func:`bind_gemm` must stay alive
+    and in place for as long as the object is used, and the stream it was bound
+    to must still be the one to launch on.
+    """
+
+    def __init__(self, fn, args):
+        self._fn, self._args = fn, args
+
+    def __call__(self) -> None:
+        _check(self._fn(*self._args))
+
+
+def bind_gemm(x, w, wtype: int, *, m: int, k: int, out, bias=None, gelu: bool = False,
+              residual: bool = False, path: int = PATH_AUTO) -> BoundGemm:
+    """Checks the arguments as :func:`gemm` does and returns a :class:`BoundGemm`."""
+    n = x.numel() // k if k else 0
+    if x.numel() != n * k:
+        raise ValueError("x must hold n*k elements")
+    flags = (BIAS if bias is not None else 0) | (GELU if gelu else 0) | (RESIDUAL if residual else 0)
+    nbytes = weight_bytes(wtype, m, k)
+    if nbytes < 0:
+        _check(lib().wq_gemm_path(n, m, k, wtype))
+    args = (_f32(x, "x"), _weight(w, wtype, nbytes), wtype, None if bias is None else _f32(bias, "bias", m),
+            flags, _f32(out, "out", n * m), n, m, k, path, _stream())
+    return BoundGemm(lib().wq_gemm_ex, args)
+
+
 def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: int, k: int, out=None):
     """Expert-major MoE matvec via ``wq_moe_matvec``.
 

@@ -6,7 +6,10 @@
 // register-tiled f32 kernel with bf16 weights) and wavo src/gpu/mod.rs
 // (`Pass::gemm`, one pipeline per weight type).
 //
-// Design for gfx950:
+// Two kernels: `gemm_bf16_kernel` for bf16 weights (a deeper direct-to-LDS pipeline, described
+// where it is defined) and `gemm_kernel` for Q8_0 / Q4_0 weights, described here.
+//
+// Design for gfx950 (quantized weights):
 //  * Workgroup tile BM (rows of X) x BN (rows of W), k step 64; WM x WN waves,
 //    each owning a (BM/WM) x (BN/WN) piece as v_mfma_f32_32x32x16_bf16 tiles.
 //    The wide tile along W keeps the per-FLOP traffic from L2 low: X arrives as

@@ -11,11 +11,12 @@
 //    of every row, and each lane owns 16 elements of it, in 2 lanes per 32-element
 //    block. Its activations for up to NTC tokens sit in 16*NTC VGPRs, loaded once
 //    per workgroup and reused for every row it visits.
-//  * The workgroup walks a run of row tiles (R rows each). Each wave streams its
-//    slice of a tile (R contiguous segments of 32 blocks) straight into its own
-//    ring of NSTAGE LDS slots with direct-to-LDS loads, NSTAGE-1 tiles ahead of
-//    the one it computes. Only the wave that loads a slot reads it, so the ring
-//    needs no barrier; the loads hold no registers while in flight.
+//  * The workgroup walks a run of row tiles (R consecutive rows each, i.e. one
+//    contiguous run of bytes). The waves stream each tile straight into a shared
+//    ring of NSTAGE LDS slots with direct-to-LDS loads, each wave a contiguous
+//    share of the tile's 1024-byte loads, NSTAGE-1 tiles ahead of the one being
+//    computed; one barrier per tile publishes it to all waves. The loads hold no
+//    registers while in flight.
 //  * Element ownership per 32-element block (half h = lane & 1):
 //      bf16, Q8_0: elements 16h .. 16h+15;
 //      Q4_0:       bytes 8h .. 8h+7 of the quants, i.e. elements 8h .. 8h+7 (low
@@ -28,10 +29,9 @@
 //    register transpose (v_permlane32_swap, v_permlane16_swap, DPP): each step
 //    halves the values a lane holds, so R rows cost about R adds per lane instead
 //    of 6 R.
-//  * A wave leaves its per-row partial sums in LDS and goes on to its next tile
-//    without waiting for the other waves. Every kFlushRows rows the workgroup
-//    synchronizes once, adds the k-slices of each row in wave order, applies the
-//    epilogue and stores. An epilogue that reads memory (bias, residual) would make
+//  * A wave leaves its per-row partial sums in LDS. Every kFlushRows rows the
+//    workgroup adds the k-slices of each row in wave order, applies the epilogue
+//    and stores. An epilogue that reads memory (bias, residual) would make
 //    the compiler wait for every ring load in flight, so such launches give each
 //    workgroup at most one flush of rows.
 //  * Rounding: a 16-term chain, one scale, a 6-level tree and at most 8 slice
@@ -177,16 +177,19 @@ __device__ __forceinline__ int x_run(int lane, int run) {
 template <int WT, int NTC, int R, int NSTAGE, int MAXW>
 __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p, int tiles_per_wg) {
   using S = Slice<WT>;
-  constexpr int kTilePieces = R * S::kSegPieces;
-  constexpr int NL = (kTilePieces + 63) / 64;  // direct-to-LDS loads per lane per tile
-  // +16: the covering dwords of the slot's last block may reach 4 bytes past the tile.
-  constexpr int kSlotBytes = NL * 1024 + 16;
+  // A tile is R consecutive rows: R * rowbytes contiguous bytes, moved by 1024-byte loads.
+  constexpr int kMaxLoads = (R * MAXW * S::kSegBytes + 1023) / 1024;
+  // +16: the covering dwords of the tile's last block may reach 4 bytes past it.
+  constexpr int kSlotBytes = kMaxLoads * 1024 + 16;
+  // Every wave issues at least this many of a tile's loads (at most one more).
+  constexpr int kMinPerWave = R * S::BB / 32;
   constexpr int kLanesPerRow = 64 / R;
   constexpr int kFlushTiles = kFlushRows / R;
-  static_assert(NSTAGE >= 2 && NL * (NSTAGE - 2) < 64, "vmcnt range");
+  static_assert(NSTAGE >= 2 && (kMinPerWave + 1) * (NSTAGE - 2) < 64, "vmcnt range");
+  static_assert(kMinPerWave >= 1, "tile too small");
   static_assert(R >= 2 && R <= 16 && (R & (R - 1)) == 0, "rows per tile: a power of two in 2..16");
 
-  __shared__ __attribute__((aligned(16))) uint8_t ring_lds[MAXW * NSTAGE * kSlotBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t ring_lds[NSTAGE * kSlotBytes];
   __shared__ float part[kFlushRows * NTC * MAXW];  // [row][token][wave]
 
   const int lane = threadIdx.x & 63;
@@ -217,35 +220,26 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
   }
 
   const uint8_t* wexp = p.w + static_cast<long long>(e) * p.expert_bytes;
-  const int ring_off = wave * (NSTAGE * kSlotBytes);
-  const uint32_t ring_addr = lds_address(ring_lds) + ring_off;
-
-  // Piece q = lane + 64 i of a tile is 16 bytes of tile row q / P at slice offset 16 (q % P).
-  // Lanes past the tile's last piece fetch that piece again (same cache line) into the slot's
-  // spare bytes; rows past the end of W read its last row (their sums are never stored).
-  int prow[NL];
-  uint32_t pcol[NL];
-#pragma unroll
-  for (int i = 0; i < NL; ++i) {
-    const int q = min(lane + 64 * i, kTilePieces - 1);
-    const int r = q / S::kSegPieces;
-    prow[i] = r;
-    pcol[i] = static_cast<uint32_t>(wave * S::kSegBytes + (q - r * S::kSegPieces) * 16);
-  }
-  const uint32_t rowbytes = static_cast<uint32_t>(p.rowbytes);
+  const uint32_t ring_addr = lds_address(ring_lds);
+  const int rowbytes = static_cast<int>(p.rowbytes);
+  const int tile_bytes = R * rowbytes;
+  const int n_loads = (tile_bytes + 1023) / 1024;
+  // This wave's share of a tile's loads: [ld0, ld1), contiguous bytes of the tile.
+  const int ld0 = wave * n_loads / nw;
+  const int ld1 = (wave + 1) * n_loads / nw;
 
   auto issue = [&](int tile) {
     const int row0 = tile * R;
     const uint8_t* base = wexp + static_cast<long long>(row0) * p.rowbytes;
-    const int last = p.m - 1 - row0;
+    // Bytes past the end of W (last tile) re-read W's last 16 bytes; never stored.
+    const int last = min(tile_bytes, (p.m - row0) * rowbytes) - 16;
     const uint32_t dst = ring_addr + static_cast<uint32_t>((tile % NSTAGE) * kSlotBytes);
-#pragma unroll
-    for (int i = 0; i < NL; ++i)
-      load_lds16(base, static_cast<uint32_t>(min(prow[i], last)) * rowbytes + pcol[i], dst + i * 1024);
+    for (int i = ld0; i < ld1; ++i)
+      load_lds16(base, static_cast<uint32_t>(min(i * 1024 + lane * 16, last)), dst + i * 1024);
   };
 
   const int h = lane & 1;
-  const int blk_off = (lane >> 1) * S::BB;  // this lane's block within a row segment
+  const int blk_off = wave * S::kSegBytes + (lane >> 1) * S::BB;  // this lane's block in a row
 
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
@@ -301,19 +295,19 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
 
       for (int f0 = t_begin; f0 < t_end; f0 += kFlushTiles) {
         const int f1 = min(t_end, f0 + kFlushTiles);
-        // Each wave runs through the tiles of this flush on its own: no barrier per tile.
         for (int tile = f0; tile < f1; ++tile) {
-          // This wave's loads of `tile` have landed once only those of later tiles are pending.
-          wait_groups<NL, NSTAGE - 2>(min(NSTAGE - 2, t_end - 1 - tile));
-          // The slot of tile-1 is free (its reads were consumed last iteration): refill it.
+          // This wave's loads of `tile` have landed once at most those of the later tiles in
+          // flight are pending (counted with the smaller per-wave share: may over-wait).
+          wait_groups<kMinPerWave, NSTAGE - 2>(min(NSTAGE - 2, t_end - 1 - tile));
+          __syncthreads();  // every wave's share of the tile is in; the slot of tile-1 is free
           if (tile + NSTAGE - 1 < t_end) issue(tile + NSTAGE - 1);
 
-          const int seg = ring_off + (tile % NSTAGE) * kSlotBytes;
+          const int seg = (tile % NSTAGE) * kSlotBytes + blk_off;
           float acc[NTC][R];
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float wv[16];
-            const float d = decode_lane<WT>(ring_lds, seg + r * S::kSegBytes + blk_off, h, wv);
+            const float d = decode_lane<WT>(ring_lds, seg + r * rowbytes, h, wv);
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
               float s = 0.f;
@@ -385,11 +379,11 @@ int groups_per_cu(void (*kernel)(MatvecParams, int), int threads, int* cache) {
   return *cache;
 }
 
-template <int WT, int NTC, int R, int NSTAGE>
+template <int WT, int NTC, int R, int NSTAGE, int MAXW>
 hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   const int nw = p.k / 1024;
   const int ntiles = (p.m + R - 1) / R;
-  auto kernel = nw <= 4 ? matvec_sliced_kernel<WT, NTC, R, NSTAGE, 4> : matvec_sliced_kernel<WT, NTC, R, NSTAGE, 8>;
+  auto kernel = matvec_sliced_kernel<WT, NTC, R, NSTAGE, MAXW>;
   // As many workgroups as are resident at once (no thin second round), split over the
   // experts; each walks a run of tiles with NSTAGE-1 of them in flight.
   const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
@@ -406,17 +400,30 @@ hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows per tile and ring depth for each weight type and token count.
-template <int WT, int NTC>
+// Rows per tile and ring depth for each weight type, token count and wave count, from sweeps on
+// MI355X (Q8_0 4096x4096 at n = 1 and 4, Q4_0 14336x4096 at n = 1, bf16 4096x4096 at n = 1, and
+// the 16-token top-2-of-8 Q4_0 MoE): one tile in flight per workgroup with several workgroups per
+// CU beat deeper rings, and taller tiles pay off once several tokens share each decoded weight.
+// Eight-wave variants (k above 4096) halve the tile to stay inside the LDS.
+template <int WT, int NTC, int MAXW>
 struct SlicedShape {
-  static constexpr int R = WT == kBF16 ? 2 : 4;
-  static constexpr int NSTAGE = 3;
+  static constexpr int R0 = WT == kBF16 ? (NTC >= 8 ? 2 : 4) : (NTC >= 4 ? 8 : 4);
+  static constexpr int R = MAXW > 4 && R0 > 2 ? R0 / 2 : R0;
+  static constexpr int NSTAGE = 2;
 };
+
+template <int WT, int NTC, int R4, int R8, int NSTAGE>
+hipError_t launch_shape(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
+  if (p.k <= 4096) return launch_r<WT, NTC, R4, NSTAGE, 4>(p, n_exp_rows, stream);
+  return launch_r<WT, NTC, R8, NSTAGE, 8>(p, n_exp_rows, stream);
+}
 
 template <int WT, int NTC>
 hipError_t launch_ntc(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
-  using C = SlicedShape<WT, NTC>;
-  return launch_r<WT, NTC, C::R, C::NSTAGE>(p, n_exp_rows, stream);
+  using C4 = SlicedShape<WT, NTC, 4>;
+  using C8 = SlicedShape<WT, NTC, 8>;
+  static_assert(C4::NSTAGE == C8::NSTAGE, "one ring depth per token count");
+  return launch_shape<WT, NTC, C4::R, C8::R, C4::NSTAGE>(p, n_exp_rows, stream);
 }
 
 template <int WT>
