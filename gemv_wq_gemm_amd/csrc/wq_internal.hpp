@@ -40,6 +40,11 @@ bool matvec_sliced_supports(int k);
 hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tokens_per_expert,
                                 hipStream_t stream);
 
+// The matrix-core kernel for 2..16 tokens per pass and MoE (Q8_0 / Q4_0, k a multiple of 512
+// in 2048..4096), which launch_matvec prefers when it applies.
+bool matvec_mfma_supports(int wtype, int k);
+hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream);
+
 // y[t][j] = sum_s gate[t*top_k + s] * slots[(t*top_k + s)][j], summed in s order.
 hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, int n_tok,
                               int top_k, int m, hipStream_t stream);

@@ -350,6 +350,10 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* w, float
 }  // namespace
 
 hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStream_t stream) {
+  // MoE: matrix cores (each workgroup walks many tiles, which repays building the activation
+  // operands once). The plain layer at n <= 16 has too few rows per workgroup for that; it takes
+  // the f32 FMA kernels.
+  if (p.ids != nullptr && matvec_mfma_supports(wtype, p.k)) return launch_matvec_mfma(wtype, p, stream);
   if (matvec_sliced_supports(p.k)) return launch_matvec_sliced(wtype, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;
   switch (wtype) {

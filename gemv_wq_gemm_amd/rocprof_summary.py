@@ -27,7 +27,7 @@ from collections import defaultdict
 PKG = os.path.dirname(os.path.abspath(__file__))
 
 # The files the matvec kernels are built from (and the flags they are built with).
-KERNEL_SOURCES = ["csrc/wq_matvec_sliced.hip", "csrc/wq_matvec.hip", "csrc/wq_decode.hpp",
+KERNEL_SOURCES = ["csrc/wq_matvec_sliced.hip", "csrc/wq_matvec_mfma.hip", "csrc/wq_matvec.hip", "csrc/wq_decode.hpp",
                   "csrc/wq_internal.hpp", "csrc/wq_lds_dma.hpp", "build.py"]
 
 

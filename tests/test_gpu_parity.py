@@ -267,3 +267,37 @@ def test_moe_sliced_out_of_range_ids():
     ok = [s for s in range(n_tok * top_k) if s != 2]
     y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k)
     assert_within(got[ok], y_ref[ok], B_F32 * S[ok] + 1e-12, "moe sliced valid slots")
+
+
+# ---------------------------------------------------------------- MoE on matrix cores (Q8_0 / Q4_0, k in 2048..4096)
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("wtype", [wq.W_Q8_0, wq.W_Q4_0])
+@pytest.mark.parametrize("n_tok,n_exp,top_k,m,k", [
+    (16, 8, 2, 75, 4096),   # the C4 routing shape at a ragged m
+    (64, 2, 1, 33, 2048),   # ~32 slots per expert: several passes of 16
+    (20, 3, 2, 129, 3072),  # six waves: uneven rows per wave
+    (5, 6, 3, 1, 4096),     # one row
+    (3, 4, 1, 16, 2560),    # five waves, one full tile
+])
+@pytest.mark.parametrize("gated", [False, True])
+def test_moe_mfma_parity(wtype, n_tok, n_exp, top_k, m, k, gated):
+    print(f"moe mfma wtype={wtype} n_tok={n_tok} n_exp={n_exp} top_k={top_k} m={m} k={k} gated={gated}", flush=True)
+    x, bank, ids, gates = _moe_inputs(15, wtype, n_tok, n_exp, top_k, m, k)
+    got = _run_moe(x, bank, wtype, ids, gates if gated else None, n_exp, m, k)
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k, gates if gated else None)
+    assert_within(got, y_ref, B_F32 * S + 8 * 2.0 ** -24 * np.abs(y_ref), "moe mfma")
+
+
+@pytest.mark.gpu
+def test_moe_mfma_out_of_range_ids():
+    wtype, n_tok, n_exp, top_k, m, k = wq.W_Q4_0, 6, 4, 2, 70, 4096
+    x, bank, ids, gates = _moe_inputs(16, wtype, n_tok, n_exp, top_k, m, k)
+    bad = ids.copy()
+    bad[0, 1] = 9
+    bad[3, 0] = -2
+    got = _run_moe(x, bank, wtype, bad, None, n_exp, m, k)
+    assert np.isnan(got[1]).all() and np.isnan(got[6]).all()
+    ok = [s for s in range(n_tok * top_k) if s not in (1, 6)]
+    y_ref, S = oracle.moe(x, bank, wtype, ids, n_exp, m, k)
+    assert_within(got[ok], y_ref[ok], B_F32 * S[ok] + 1e-12, "moe mfma valid slots")
