@@ -57,6 +57,18 @@ __device__ __forceinline__ void wait_groups(int later) {
   }
 }
 
+// Waits until at most n (wave-uniform, 0 <= n) of this wave's loads are outstanding, for n known
+// only at run time: takes the largest immediate not above n (n above MAX waits for MAX).
+template <int MAX>
+__device__ __forceinline__ void wait_at_most(int n) {
+  if constexpr (MAX == 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (n >= MAX) wait_vmcnt<MAX>();
+    else wait_at_most<MAX - 1>(n);
+  }
+}
+
 __device__ __forceinline__ uint32_t lds_address(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const void __attribute__((address_space(3)))*)p));
 }

@@ -1,13 +1,11 @@
-// Matrix-core matvec for 2..16 tokens per pass and the MoE matvec, with f32 accuracy.
+// The MoE matvec on matrix cores, with f32 accuracy (Q8_0 and Q4_0 weights).
 //
-// Same contract as the other matvec kernels: y[t][j] = epilogue(sum_k x[t][k] w[j][k]) for the
-// plain layer (cortiq-engine src/gpu_wgpu/nemotron_audio.rs `ae_gemm`/`ae_put`; wavo
-// src/gpu/mod.rs `Pass::gemv`) and y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k] for MoE slots
-// (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), for Q8_0 and Q4_0 weights.
+// Contract: per routed slot s and output row j, y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k]
+// (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), the same as the f32 matvec kernels.
 //
-// Why matrix cores: with f32 FMAs every weight costs one instruction per token, so a few tokens
-// (or a MoE expert's routed tokens) make the kernel bound by the vector ALU, not by HBM. Here each
-// weight is decoded once and v_mfma_f32_16x16x32_bf16 applies it to up to 16 tokens.
+// Why matrix cores: with f32 FMAs every weight costs one instruction per routed slot, so an
+// expert's several slots make the kernel bound by the vector ALU, not by HBM. Here each weight
+// is decoded once and v_mfma_f32_16x16x32_bf16 applies it to up to 16 slots.
 //
 // Exactness:
 //  * Each activation is split into three bf16 parts, x = x1 + x2 + x3, with x1 = bf16(x),
@@ -23,24 +21,25 @@
 //
 // Layout of the work (gfx950, wave64):
 //  * A workgroup has k/512 waves; wave w owns the k-slice [512 w, 512 w + 512), i.e. 16 blocks of
-//    every row. MFMA roles: A = activations (16 token rows x 32 k), B = weights (32 k x 16 weight
+//    every row. MFMA roles: A = activations (16 slots x 32 k), B = weights (32 k x 16 weight
 //    rows), D[t][j] in lane 16 (t / 4) + j, value t % 4.
 //  * Lane l = 16 o + j: weight row j of the tile and k-octet o of each block (elements 8o..8o+7);
-//    as A it holds token l % 16 at the same octet. Its three activation parts for the 16 blocks of
-//    its slice (192 VGPRs) are built once per group of tokens and reused for every tile.
+//    as A it holds slot j at the same octet. Its three activation parts for the 16 blocks of its
+//    slice (192 VGPRs) are built once per group of slots and reused for every tile.
 //  * A tile is 16 consecutive weight rows, streamed by the workgroup into a ring of NSTAGE LDS
 //    slots with direct-to-LDS loads (each wave a share of the rows, 1024 bytes per load, the last
 //    load of a row on the lanes with bytes left), NSTAGE-1 tiles ahead; one barrier per tile
-//    publishes it. Rows sit at a stride of their length + 16 bytes, so the 16 rows one operand
-//    read touches spread over the LDS banks (at most two lanes of a half-wave per bank).
+//    publishes it. Rows sit at a stride of their length + 16 bytes: row strides that are
+//    multiples of 128 bytes would put the 16 rows one operand read touches into one LDS bank.
+//    From a 4-byte aligned per-lane base, every block's LDS offsets are compile-time constants.
 //  * Each wave writes its 16x16 partial sums to LDS; after the next tile's barrier the workgroup
-//    adds the k-slices in wave order, applies the epilogue and stores. An epilogue that reads
-//    memory (bias, residual) would make the compiler wait for every ring load in flight, so such
-//    launches park the sums in LDS and finish them after the last tile.
-//  * MoE: blockIdx.y is the expert; a ballot over the ids picks its slots, 16 per pass, so each
+//    adds the k-slices in wave order and stores.
+//  * blockIdx.y is the expert; a ballot over the ids picks its slots, 16 per pass, so each
 //    touched expert's rows stream once per 16 of its slots. One extra grid row writes NaN for
 //    slots whose id is out of range.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
@@ -52,11 +51,11 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kTileRows = 16;    // weight rows per tile: the MFMA's N
+constexpr int kTileRows = 16;     // weight rows per tile: the MFMA's N
 constexpr int kSliceBlocks = 16;  // blocks per wave: 512 of k
 constexpr int kMaxWaves = 8;      // k <= 4096
-constexpr int kTokens = 16;       // slots per pass: the MFMA's M
-constexpr int kParkTiles = 4;     // tiles whose sums a memory-reading epilogue parks in LDS
+constexpr int kSlots = 16;        // routed slots per pass: the MFMA's M
+constexpr int kSchedBlocks = 2;   // blocks the scheduler may interleave
 
 // bf16 bit patterns of two f32 values that bf16 holds exactly, packed low | high << 16.
 __device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
@@ -69,16 +68,26 @@ __device__ __forceinline__ float q4_byte(uint32_t word, int b) {
   return __builtin_amdgcn_cvt_off_f32_i4(b == 0 ? word : (word >> (8 * b)) & 0xFFu);
 }
 
-// The 8 weights of k-octet o of the block at LDS byte offset `off`, as MFMA B operand, and the
-// factor that scales their products.
-template <int WT>
-__device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int off, int o, float& scale) {
-  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + off));
-  const int qo = off + 2 + (WT == kQ8_0 ? 8 * o : 8 * (o & 1));
-  const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
-  const uint32_t* a = reinterpret_cast<const uint32_t*>(lds) + (qo >> 2);
-  const uint32_t d0 = a[0], d1 = a[1], d2 = a[2];
-  const uint32_t q0 = realign(d1, d0, sh), q1 = realign(d2, d1, sh);
+// The 8 weights of k-octet o of block BLK of this lane's row slice, as MFMA B operand, and the
+// factor that scales their products. `q_base` (4-byte aligned) is the LDS byte offset of the
+// slice's first block plus the lane's quant offset (8 o for Q8_0, 8 (o & 1) for Q4_0); `s_base`
+// is the slice's first block. Every other offset is a compile-time constant.
+template <int WT, int BLK>
+__device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int q_base, int s_base, int o, float& scale) {
+  constexpr int BB = block_bytes(WT);
+  constexpr int kQ = BLK * BB + 2;  // first quant byte of the block, from an aligned base
+  constexpr int kSh = kQ & 3;       // 0 or 2
+  const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + s_base + BLK * BB));
+  const uint32_t* a = reinterpret_cast<const uint32_t*>(lds + q_base) + (kQ >> 2);
+  uint32_t q0, q1;
+  if constexpr (kSh == 0) {
+    q0 = a[0];
+    q1 = a[1];
+  } else {
+    const uint32_t d0 = a[0], d1 = a[1], d2 = a[2];
+    q0 = realign(d1, d0, kSh);
+    q1 = realign(d2, d1, kSh);
+  }
   uint4 u;
   if constexpr (WT == kQ8_0) {
     u.x = bf16_pair(q8_at(q0, 0), q8_at(q0, 1));
@@ -99,47 +108,52 @@ __device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int off, int 
   return __builtin_bit_cast(bf16x8, u);
 }
 
-// Three bf16 parts of 8 activations (see the exactness note above).
+// The three bf16 parts of 8 activations (see the exactness note above).
 __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p1, bf16x8& p2, bf16x8& p3) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const __bf16 h1 = static_cast<__bf16>(x[i]);
     const float r1 = x[i] - static_cast<float>(h1);
     const __bf16 h2 = static_cast<__bf16>(r1);
-    const float r2 = r1 - static_cast<float>(h2);
     p1[i] = h1;
     p2[i] = h2;
-    p3[i] = static_cast<__bf16>(r2);
+    p3[i] = static_cast<__bf16>(r1 - static_cast<float>(h2));
+  }
+}
+
+// Calls f(integral_constant<int, I>) for I = 0 .. N-1, in order.
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
   }
 }
 
 template <int WT, int NSTAGE>
 __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParams p, int tiles_per_wg) {
   constexpr int BB = block_bytes(WT);
-  // A row sits in LDS at a stride of its byte length + 16: row strides that are multiples of
-  // 128 bytes would put the 16 rows an MFMA operand reads at once into one LDS bank.
   constexpr int kMaxRowBytes = kMaxWaves * kSliceBlocks * BB;
   constexpr int kSlotBytes = kTileRows * (kMaxRowBytes + 16);
-  // Loads per wave per tile, at least (rows per wave x loads per row, over the supported k).
-  constexpr int kMinPerWave = WT == kQ8_0 ? 8 : 4;
-  static_assert(NSTAGE >= 2 && 2 * kMinPerWave * (NSTAGE - 2) < 64, "vmcnt range");
+  constexpr int kPartWave = kSlots * kTileRows;  // one wave's partials: [slot][weight row]
+  // A wave issues at most 4 rows x 5 loads per tile (k <= 4096); vmcnt holds up to 63.
+  constexpr int kMaxPending = 20 * (NSTAGE - 2);
+  static_assert(NSTAGE >= 2 && kMaxPending < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE * kSlotBytes];
-  __shared__ float part[2][kMaxWaves * kTileRows * kTokens];  // [buffer][wave][token][row]
-  __shared__ float park[kParkTiles * kTileRows * kTokens];     // [tile][token][row]
-  __shared__ int slot_lds[kTokens];                            // slot of each token row
+  __shared__ float part[2][kMaxWaves * kPartWave];
+  __shared__ int slot_lds[kSlots];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int e = blockIdx.y;
-  const bool moe = p.ids != nullptr;
   const int ntiles = (p.m + kTileRows - 1) / kTileRows;
   const int t_begin = blockIdx.x * tiles_per_wg;
   const int t_end = min(ntiles, t_begin + tiles_per_wg);
   if (t_begin >= ntiles) return;  // workgroup-uniform
 
-  if (moe && e == p.n_exp) {
+  if (e == p.n_exp) {
     // Slots routed outside the bank: their outputs in this run of rows become NaN.
     for (int win = 0; win < p.n_slots; win += 64) {
       const int s = win + lane;
@@ -156,7 +170,6 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
     return;
   }
 
-  const bool parked = !moe && (p.flags & 5u) != 0;
   const uint8_t* wexp = p.w + static_cast<long long>(e) * p.expert_bytes;
   const uint32_t ring_addr = lds_address(ring);
   const int rowbytes = static_cast<int>(p.rowbytes);
@@ -165,6 +178,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
   // This wave's rows of every tile.
   const int r0 = wave * kTileRows / nw;
   const int r1 = (wave + 1) * kTileRows / nw;
+  const int per_tile = (r1 - r0) * per_row;  // this wave's loads per tile (wave-uniform)
 
   auto issue = [&](int tile) {
     const int row0 = tile * kTileRows;
@@ -180,47 +194,42 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
     }
   };
 
-  const int j = lane & 15;  // weight row in the tile (B, D column); token row as A
+  const int j = lane & 15;  // weight row in the tile (B, D column); slot as A
   const int o = lane >> 4;  // k-octet of each block; D rows 4o .. 4o+3
-  const int row_off = j * stride + wave * kSliceBlocks * BB;
+  const int s_off = j * stride + wave * kSliceBlocks * BB;         // the lane's row slice
+  const int q_off = s_off + (WT == kQ8_0 ? 8 * o : 8 * (o & 1));  // and its quant octet
 
-  // Finishes tile `tile` from the wave partials in part[buf]: the sums of all waves, in wave order.
+  // Finishes tile `tile` from the wave partials in part[buf]: the k-slices of all waves, added in
+  // wave order.
   auto finish = [&](int tile, int buf) {
-    for (int i = threadIdx.x; i < kTileRows * kTokens; i += blockDim.x) {
-      const int t = i >> 4;
-      const int r = i & 15;
-      float v = 0.f;
-#pragma unroll
-      for (int w = 0; w < kMaxWaves; ++w)
-        if (w < nw) v += part[buf][w * kTileRows * kTokens + i];
-      if (parked) {
-        park[(tile - t_begin) * kTileRows * kTokens + i] = v;
-      } else {
-        const int row = tile * kTileRows + r;
-        const int slot = slot_lds[t];
-        if (row < p.m && slot >= 0) {
-          if (!moe && (p.flags & 2u)) v = gelu_erf(v);
-          p.y[static_cast<long long>(slot) * p.m + row] = v;
-        }
+    for (int i = threadIdx.x; i < kSlots * kTileRows; i += blockDim.x) {
+      const int t = i >> 4;  // slot within the pass
+      const int r = i & 15;  // weight row within the tile
+      const int row = tile * kTileRows + r;
+      const int slot = slot_lds[t];
+      if (row < p.m && slot >= 0) {
+        float v = 0.f;
+        // Not unrolled: this runs inside the tile loop, where registers are scarce.
+#pragma unroll 1
+        for (int w = 0; w < nw; ++w) v += part[buf][w * kPartWave + i];
+        p.y[static_cast<long long>(slot) * p.m + row] = v;
       }
     }
   };
 
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
-    if (moe) {
+    {
       const int s = win + lane;
       int id = -1;
       if (s < p.n_slots) id = p.ids[s];
       mask = __ballot(id == e);
-    } else {
-      const int left = p.n_slots - win;
-      mask = left >= 64 ? ~0ull : ((1ull << left) - 1ull);
     }
     while (mask) {
-      int slot_of[kTokens];
+      // This pass's slots, in order: A row (and D row) t is slot_of[t].
+      int slot_of[kSlots];
 #pragma unroll
-      for (int t = 0; t < kTokens; ++t) {
+      for (int t = 0; t < kSlots; ++t) {
         if (mask) {
           slot_of[t] = win + __builtin_ctzll(mask);
           mask &= mask - 1;
@@ -230,11 +239,11 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
       }
       int my_slot = -1;
 #pragma unroll
-      for (int t = 0; t < kTokens; ++t)
+      for (int t = 0; t < kSlots; ++t)
         if (t == j) my_slot = slot_of[t];
-      if (threadIdx.x < kTokens) slot_lds[threadIdx.x] = my_slot;  // read after the next barrier
+      if (threadIdx.x < kSlots) slot_lds[threadIdx.x] = my_slot;  // read after the next barrier
 
-      // Prologue: the first NSTAGE-1 tiles in flight, then the activation parts.
+      // Prologue: the first NSTAGE-1 tiles in flight, then the activation operands.
 #pragma unroll
       for (int s = 0; s < NSTAGE - 1; ++s)
         if (t_begin + s < t_end) issue(t_begin + s);
@@ -255,55 +264,43 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
             for (int i = 0; i < 8; ++i) xv[i] = 0.f;
           }
           split3(xv, xa[0][bb], xa[1][bb], xa[2][bb]);
+          // Load and split a few blocks at a time: hoisting every load first runs out of registers.
+          if (bb % 4 == 3) __builtin_amdgcn_sched_barrier(0);
         }
       }
 
       for (int tile = t_begin; tile < t_end; ++tile) {
-        wait_groups<kMinPerWave, NSTAGE - 2>(min(NSTAGE - 2, t_end - 1 - tile));
+        // This wave's loads of `tile` have landed once only those of the later tiles in flight
+        // are pending (the exact count: a smaller one would also wait for part of the next tile).
+        wait_at_most<kMaxPending>(per_tile * min(NSTAGE - 2, t_end - 1 - tile));
         __syncthreads();  // the tile is in; the slot of tile-1 and part[(tile-1)&1] are complete
-        if (tile + NSTAGE - 1 < t_end) issue(tile + NSTAGE - 1);
+        // Stores count in vmcnt too: issued before the next tile's loads, they are never among the
+        // most recent operations a wait leaves in flight, so they cannot stretch it.
         if (tile > t_begin) finish(tile - 1, (tile - 1) & 1);
+        if (tile + NSTAGE - 1 < t_end) issue(tile + NSTAGE - 1);
 
-        const int seg = (tile % NSTAGE) * kSlotBytes + row_off;
+        const int slot_base = (tile % NSTAGE) * kSlotBytes;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int bb = 0; bb < kSliceBlocks; ++bb) {
+        static_for<0, kSliceBlocks>([&](auto bb) {
+          constexpr int B = decltype(bb)::value;
           float scale;
-          const bf16x8 wb = decode_octet<WT>(ring, seg + bb * BB, o, scale);
+          const bf16x8 wb = decode_octet<WT, B>(ring, slot_base + q_off, slot_base + s_off, o, scale);
           f32x4 blk = {0.f, 0.f, 0.f, 0.f};
-          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][bb], wb, blk, 0, 0, 0);
-          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][bb], wb, blk, 0, 0, 0);
-          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2][bb], wb, blk, 0, 0, 0);
+          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][B], wb, blk, 0, 0, 0);
+          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][B], wb, blk, 0, 0, 0);
+          blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2][B], wb, blk, 0, 0, 0);
 #pragma unroll
           for (int v = 0; v < 4; ++v) acc[v] = __builtin_fmaf(scale, blk[v], acc[v]);
-        }
-        float* pw = part[tile & 1] + wave * kTileRows * kTokens;
+          // Keep the scheduler within a few blocks: hoisting many decodes runs out of registers.
+          if constexpr (B % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
+        });
+        float* pw = part[tile & 1] + wave * kPartWave;
 #pragma unroll
         for (int v = 0; v < 4; ++v) pw[(4 * o + v) * kTileRows + j] = acc[v];
       }
       __syncthreads();
       finish(t_end - 1, (t_end - 1) & 1);
-
-      if (parked) {
-        // Every ring load has landed (the last tile waited for all of them).
-        __syncthreads();
-        const int n = (t_end - t_begin) * kTileRows * kTokens;
-        for (int i = threadIdx.x; i < n; i += blockDim.x) {
-          const int tl = i / (kTileRows * kTokens);
-          const int t = (i >> 4) & (kTokens - 1);
-          const int row = (t_begin + tl) * kTileRows + (i & 15);
-          const int slot = slot_lds[t];
-          if (row < p.m && slot >= 0) {
-            float* yp = p.y + static_cast<long long>(slot) * p.m + row;
-            float v = park[i];
-            if (p.flags & 1u) v += p.bias[row];
-            if (p.flags & 2u) v = gelu_erf(v);
-            if (p.flags & 4u) v += *yp;
-            *yp = v;
-          }
-        }
-      }
-      __syncthreads();  // part, park and the ring are reused by the next group of slots
+      __syncthreads();  // part, slot_lds and the ring are reused by the next group of slots
     }
   }
 }
@@ -323,8 +320,6 @@ int mfma_device_cus() {
 template <int WT, int NSTAGE>
 hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
   const int nw = p.k / 512;
-  const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;
-  const int experts = p.ids ? p.n_exp : 1;
   const int ntiles = (p.m + kTileRows - 1) / kTileRows;
   auto kernel = matvec_mfma_kernel<WT, NSTAGE>;
   static int per_cu = 0;
@@ -333,12 +328,12 @@ hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, 64 * kMaxWaves, 0) != hipSuccess || v <= 0) v = 1;
     per_cu = v;
   }
-  int groups = per_cu * mfma_device_cus() / experts;
+  // As many workgroups as are resident at once, split over the experts.
+  int groups = per_cu * mfma_device_cus() / p.n_exp;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
-  int tpw = (ntiles + groups - 1) / groups;
-  if (p.ids == nullptr && (p.flags & 5u) != 0 && tpw > kParkTiles) tpw = kParkTiles;
-  dim3 grid((ntiles + tpw - 1) / tpw, n_exp_rows);
+  const int tpw = (ntiles + groups - 1) / groups;
+  dim3 grid((ntiles + tpw - 1) / tpw, p.n_exp + 1);
   hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, stream, p, tpw);
   return hipGetLastError();
 }
@@ -350,7 +345,8 @@ bool matvec_mfma_supports(int wtype, int k) {
 }
 
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream) {
-  if (!matvec_mfma_supports(wtype, p.k)) return hipErrorInvalidValue;
+  if (!matvec_mfma_supports(wtype, p.k) || p.ids == nullptr) return hipErrorInvalidValue;
+  // LDS: a Q8_0 tile is twice a Q4_0 one, so Q8_0 runs a shallower ring.
   if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2>(p, stream);
   return launch_mfma<kQ4_0, 3>(p, stream);
 }
