@@ -416,15 +416,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 
   for (int s = 0; s < nk; ++s) {
     // Wait for this wave's loads of step s: those of the later steps issued so far stay outstanding.
-    const int later = min(P - 1, nk - 1 - s);
-    if constexpr (P >= 3) {
-      if (later >= 2) wait_vmcnt<2 * kInst>();
-      else if (later == 1) wait_vmcnt<kInst>();
-      else wait_vmcnt<0>();
-    } else {
-      if (later >= 1) wait_vmcnt<kInst>();
-      else wait_vmcnt<0>();
-    }
+    wait_groups<kInst, P - 1>(min(P - 1, nk - 1 - s));
     __syncthreads();  // every wave's step-s data is in LDS; the slot of step s-1 is free
     if (s + P < nk) issue(s + P);
 
@@ -540,7 +532,10 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
     // Measured on MI355X at n = 1500: 128 x 256 tiles win once they give at least half the CUs
     // a tile; below that, 128 x 128 tiles (more of them) do. Both use 8 waves.
     if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 4>(p, stream);
-    return launch_bf16<128, 128, 2, 4, 4>(p, stream);
+    const long long mid_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 127) / 128);
+    if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 4>(p, stream);
+    // Few output tiles: 64 x 128 tiles keep more CUs streaming operands, with a deeper ring.
+    return launch_bf16<64, 128, 2, 4, 8>(p, stream);
   }
   // Wide tiles (128 X rows x 256 W rows) when they still give every CU work,
   // 128 x 128 otherwise.
