@@ -34,6 +34,8 @@
 //    f32 atomics; the first one adds the bias.
 #include <hip/hip_runtime.h>
 
+#include <cstdlib>
+
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
 #include "wq_lds_dma.hpp"
@@ -331,7 +333,7 @@ __device__ __forceinline__ int x_swizzle(int r) { return (r >> 1) & 7; }
 __device__ __forceinline__ int w_swizzle(int r) { return (r >> 2) & 3; }
 
 template <int BM, int BN, int WM, int WN, int NSTAGE>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n, int band) {
   constexpr int BK = 32;
   constexpr int kWaves = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -357,8 +359,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
   const int per_xcd = (tiles + 7) / 8;
   const int t = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
   if (t >= tiles) return;  // workgroup-uniform
-  const int tile_n = t / tiles_m;
-  const int tile_m = t - tile_n * tiles_m;
+  // Tiles are numbered in bands of `band` X-tile rows, down each band's rows first: an XCD's
+  // contiguous range of tile numbers is then a band x (range / band) block, which reads fewer
+  // distinct X and W panels than whole columns of tiles would.
+  const int band_tiles = band * tiles_n;
+  const int b = t / band_tiles;
+  const int r = t - b * band_tiles;
+  const int rows = min(band, tiles_m - b * band);
+  const int tile_m = b * band + r % rows;
+  const int tile_n = r / rows;
   const int n0 = tile_m * BM;
   const int m0 = tile_n * BN;
   const int nk = p.k / BK;
@@ -511,13 +520,22 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Band height for the tile order: the divisor of an XCD's tile count closest to its square
+// root (no taller than the tile grid), so each XCD works on a near-square block of tiles.
+int tile_band(int tiles_m, int per_xcd) {
+  int best = 1;
+  for (int d = 1; d <= per_xcd && d <= tiles_m; ++d)
+    if (per_xcd % d == 0 && std::abs(d * d - per_xcd) < std::abs(best * best - per_xcd)) best = d;
+  return best;
+}
+
 template <int BM, int BN, int WM, int WN, int NSTAGE>
 hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
   const int tiles_m = (p.n + BM - 1) / BM;
   const int tiles_n = (p.m + BN - 1) / BN;
   const int per_xcd = (tiles_m * tiles_n + 7) / 8;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE>), dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream,
-                     p, tiles_m, tiles_n);
+                     p, tiles_m, tiles_n, tile_band(tiles_m, per_xcd));
   return hipGetLastError();
 }
 
