@@ -29,13 +29,26 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
 
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+// kStream marks bytes read once per launch (a matvec's weights): the load carries the nt
+// (non-temporal) hint, so the caches favour keeping the data workgroups re-read, such as the
+// activations.
+template <bool kStream = false>
 __device__ __forceinline__ void load_lds16(const void* base, uint32_t voff, uint32_t lds_addr) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
-      : "memory", "m0");
+  if constexpr (kStream) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1 nt"
+        :
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+  } else {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(uniform_ptr(base)), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+        : "memory", "m0");
+  }
 }
 #pragma clang diagnostic pop
 

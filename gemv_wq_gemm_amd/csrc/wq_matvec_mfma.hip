@@ -189,7 +189,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
       for (int c = 0; c < per_row; ++c) {
         const int b = c * 1024 + lane * 16;
         if (b < rowbytes)  // the last load of a row runs on the lanes that have bytes left
-          load_lds16(base, static_cast<uint32_t>(rr * rowbytes + b), dst + r * stride + c * 1024);
+          load_lds16<true>(base, static_cast<uint32_t>(rr * rowbytes + b), dst + r * stride + c * 1024);
       }
     }
   };

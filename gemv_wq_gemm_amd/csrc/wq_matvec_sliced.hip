@@ -7,34 +7,38 @@
 // `moe_matvec_gpu`), all in f32.
 //
 // Layout of the work (gfx950, wave64):
-//  * A workgroup has k/1024 waves; wave w owns the k-slice [1024 w, 1024 w + 1024)
-//    of every row, and each lane owns 16 elements of it, in 2 lanes per 32-element
-//    block. Its activations for up to NTC tokens sit in 16*NTC VGPRs, loaded once
-//    per workgroup and reused for every row it visits.
+//  * A workgroup has k/SLICE waves (SLICE = 1024 or 512 elements of k); wave w owns
+//    the k-slice [SLICE w, SLICE w + SLICE) of every row, and each lane owns
+//    E = SLICE/64 elements of it (16 or 8), in 32/E lanes per 32-element block.
+//    Its activations for up to NTC tokens sit in E*NTC VGPRs, loaded once per
+//    workgroup and reused for every row it visits. Narrower slices spread a
+//    tile's arithmetic over more waves, so fewer workgroups per CU (each of which
+//    loads the whole activation rows) keep the same bytes in flight.
 //  * The workgroup walks a run of row tiles (R consecutive rows each, i.e. one
 //    contiguous run of bytes). The waves stream each tile straight into a shared
 //    ring of NSTAGE LDS slots with direct-to-LDS loads, each wave a contiguous
 //    share of the tile's 1024-byte loads, NSTAGE-1 tiles ahead of the one being
 //    computed; one barrier per tile publishes it to all waves. The loads hold no
 //    registers while in flight.
-//  * Element ownership per 32-element block (half h = lane & 1):
-//      bf16, Q8_0: elements 16h .. 16h+15;
-//      Q4_0:       bytes 8h .. 8h+7 of the quants, i.e. elements 8h .. 8h+7 (low
-//                  nibbles) and 16+8h .. 16+8h+7 (high nibbles). A byte select
-//                  (SDWA) feeds each nibble to v_cvt_off_f32_i4, which yields
-//                  (q-8)/16 exactly once the nibble is XOR-ed with 8; the block
-//                  scale is taken as 16 d to compensate.
-//  * A lane's 16 products per row and token are summed in f32 and scaled once by
+//  * Element ownership per 32-element block (q = lane's index among the block's
+//    32/E lanes):
+//      bf16, Q8_0: elements E q .. E q + E-1;
+//      Q4_0:       quant bytes (E/2) q .. (E/2) q + E/2-1, i.e. those elements
+//                  (low nibbles) and the same 16 further on (high nibbles). A
+//                  byte select (SDWA) feeds each nibble to v_cvt_off_f32_i4,
+//                  which yields (q-8)/16 exactly once the nibble is XOR-ed with
+//                  8; the block scale is taken as 16 d to compensate.
+//  * A lane's E products per row and token are summed in f32 and scaled once by
 //    the block scale. The 64 lane partials of the R rows are then summed by a
 //    register transpose (v_permlane32_swap, v_permlane16_swap, DPP): each step
 //    halves the values a lane holds, so R rows cost about R adds per lane instead
 //    of 6 R.
-//  * A wave leaves its per-row partial sums in LDS. Every kFlushRows rows the
+//  * A wave leaves its per-row partial sums in LDS. Every flush_rows rows the
 //    workgroup adds the k-slices of each row in wave order, applies the epilogue
 //    and stores. An epilogue that reads memory (bias, residual) would make
 //    the compiler wait for every ring load in flight, so such launches give each
 //    workgroup at most one flush of rows.
-//  * Rounding: a 16-term chain, one scale, a 6-level tree and at most 8 slice
+//  * Rounding: an E-term chain, one scale, a 6-level tree and at most 16 slice
 //    additions per output -- far inside 1e-5 * sum |x w|.
 #include <hip/hip_runtime.h>
 
@@ -45,11 +49,13 @@
 namespace wq {
 namespace {
 
-template <int WT>
+template <int WT, int SLICE>
 struct Slice {
+  static_assert(SLICE == 1024 || SLICE == 512, "k elements per wave: 1024 or 512");
   static constexpr int BB = block_bytes(WT);
-  static constexpr int kSegBytes = 32 * BB;          // one wave's 1024-element slice of a row
-  static constexpr int kSegPieces = kSegBytes / 16;  // 68 (Q8_0), 36 (Q4_0), 128 (bf16)
+  static constexpr int E = SLICE / 64;                  // elements per lane and row
+  static constexpr int kLanesPerBlock = 32 / E;         // 2 or 4
+  static constexpr int kSegBytes = SLICE / 32 * BB;     // one wave's slice of a row
 };
 
 template <int CTRL>
@@ -109,80 +115,90 @@ __device__ __forceinline__ void transpose_sum(float (&v)[R], int lane) {
   v[0] += dpp<0xB1>(v[0]);  // xor 1 inside quads
 }
 
-// Rows whose per-wave partial sums a workgroup holds in LDS before it adds them up.
-constexpr int kFlushRows = 128;
+// Rows whose per-wave partial sums a workgroup holds in LDS before it adds them up: 128, or
+// fewer where NTC * MAXW partials per row would take more than 16 KB.
+constexpr int flush_rows(int ntc, int maxw) { return 4096 / (ntc * maxw) < 128 ? 4096 / (ntc * maxw) : 128; }
 
-// Decodes this lane's 16 weights of one block held in LDS at byte `boff` from `lds`
+// Decodes this lane's E weights of one block held in LDS at byte `boff` from `lds`
 // (element order as described above) and returns the factor that scales their sum.
-template <int WT>
-__device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int h, float (&wv)[16]) {
+template <int WT, int E>
+__device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int q, float (&wv)[E]) {
   if constexpr (WT == kBF16) {
-    const uint4 a = *reinterpret_cast<const uint4*>(lds + boff + 32 * h);
-    const uint4 b = *reinterpret_cast<const uint4*>(lds + boff + 32 * h + 16);
-    const uint32_t q[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    const uint32_t* a = reinterpret_cast<const uint32_t*>(lds + boff + 2 * E * q);
+    uint32_t w[E / 2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      wv[2 * i] = bf16_lo(q[i]);
-      wv[2 * i + 1] = bf16_hi(q[i]);
+    for (int i = 0; i < E / 8; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(a)[i];
+      w[4 * i] = v.x;
+      w[4 * i + 1] = v.y;
+      w[4 * i + 2] = v.z;
+      w[4 * i + 3] = v.w;
+    }
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) {
+      wv[2 * i] = bf16_lo(w[i]);
+      wv[2 * i + 1] = bf16_hi(w[i]);
     }
     return 1.f;
   } else if constexpr (WT == kQ8_0) {
     const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + boff));
-    const int qo = boff + 2 + 16 * h;  // quants 16h .. 16h+15
+    const int qo = boff + 2 + E * q;  // quants E q .. E q + E-1
     const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
     const uint32_t* a = reinterpret_cast<const uint32_t*>(lds) + (qo >> 2);
-    uint32_t dw[5];
+    uint32_t dw[E / 4 + 1];
 #pragma unroll
-    for (int i = 0; i < 5; ++i) dw[i] = a[i];
+    for (int i = 0; i < E / 4 + 1; ++i) dw[i] = a[i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t q = realign(dw[i + 1], dw[i], sh);
+    for (int i = 0; i < E / 4; ++i) {
+      const uint32_t v = realign(dw[i + 1], dw[i], sh);
 #pragma unroll
-      for (int b = 0; b < 4; ++b) wv[4 * i + b] = q8_at(q, b);
+      for (int b = 0; b < 4; ++b) wv[4 * i + b] = q8_at(v, b);
     }
     return d;
   } else {
     const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + boff));
-    const int qo = boff + 2 + 8 * h;  // quant bytes 8h .. 8h+7
+    const int qo = boff + 2 + (E / 2) * q;  // quant bytes (E/2) q .. (E/2) q + E/2-1
     const uint32_t sh = static_cast<uint32_t>(qo) & 3u;
     const uint32_t* a = reinterpret_cast<const uint32_t*>(lds) + (qo >> 2);
-    uint32_t dw[3];
+    uint32_t dw[E / 8 + 1];
 #pragma unroll
-    for (int i = 0; i < 3; ++i) dw[i] = a[i];
+    for (int i = 0; i < E / 8 + 1; ++i) dw[i] = a[i];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < E / 8; ++i) {
       const uint32_t lo = realign(dw[i + 1], dw[i], sh) ^ 0x88888888u;
       const uint32_t hi = __builtin_amdgcn_alignbit(lo, lo, 4);  // high nibbles into the low ones
       wv[4 * i] = __builtin_amdgcn_cvt_off_f32_i4(lo);
-      wv[8 + 4 * i] = __builtin_amdgcn_cvt_off_f32_i4(hi);
+      wv[E / 2 + 4 * i] = __builtin_amdgcn_cvt_off_f32_i4(hi);
 #pragma unroll
       for (int b = 1; b < 4; ++b) {
         wv[4 * i + b] = __builtin_amdgcn_cvt_off_f32_i4((lo >> (8 * b)) & 0xFFu);
-        wv[8 + 4 * i + b] = __builtin_amdgcn_cvt_off_f32_i4((hi >> (8 * b)) & 0xFFu);
+        wv[E / 2 + 4 * i + b] = __builtin_amdgcn_cvt_off_f32_i4((hi >> (8 * b)) & 0xFFu);
       }
     }
     return 16.f * d;
   }
 }
 
-// First element, within the lane's 1024-element k-slice, of each run of 8 activations the
-// lane multiplies (two runs per block; see the ownership above).
-template <int WT>
-__device__ __forceinline__ int x_run(int lane, int run) {
-  const int bl = lane >> 1, h = lane & 1;
-  if constexpr (WT == kQ4_0) return bl * 32 + 8 * h + 16 * run;
-  return bl * 32 + 16 * h + 8 * run;
+// First element, within the lane's k-slice, of the j-th run of 4 activations the lane
+// multiplies (E/4 runs, in the order of decode_lane's weights).
+template <int WT, int E>
+__device__ __forceinline__ int x_run(int lane, int j) {
+  const int bl = lane / (32 / E), q = lane % (32 / E);
+  if constexpr (WT == kQ4_0) return bl * 32 + (E / 2) * q + (j < E / 8 ? 4 * j : 16 + 4 * (j - E / 8));
+  return bl * 32 + E * q + 4 * j;
 }
 
-template <int WT, int NTC, int R, int NSTAGE, int MAXW>
+template <int WT, int NTC, int R, int NSTAGE, int MAXW, int SLICE>
 __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p, int tiles_per_wg) {
-  using S = Slice<WT>;
+  using S = Slice<WT, SLICE>;
+  constexpr int E = S::E;
+  constexpr int kFlushRows = flush_rows(NTC, MAXW);
   // A tile is R consecutive rows: R * rowbytes contiguous bytes, moved by 1024-byte loads.
   constexpr int kMaxLoads = (R * MAXW * S::kSegBytes + 1023) / 1024;
   // +16: the covering dwords of the tile's last block may reach 4 bytes past it.
   constexpr int kSlotBytes = kMaxLoads * 1024 + 16;
   // Every wave issues at least this many of a tile's loads (at most one more).
-  constexpr int kMinPerWave = R * S::BB / 32;
+  constexpr int kMinPerWave = R * S::kSegBytes / 1024;
   constexpr int kLanesPerRow = 64 / R;
   constexpr int kFlushTiles = kFlushRows / R;
   static_assert(NSTAGE >= 2 && (kMinPerWave + 1) * (NSTAGE - 2) < 64, "vmcnt range");
@@ -235,11 +251,11 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
     const int last = min(tile_bytes, (p.m - row0) * rowbytes) - 16;
     const uint32_t dst = ring_addr + static_cast<uint32_t>((tile % NSTAGE) * kSlotBytes);
     for (int i = ld0; i < ld1; ++i)
-      load_lds16(base, static_cast<uint32_t>(min(i * 1024 + lane * 16, last)), dst + i * 1024);
+      load_lds16<true>(base, static_cast<uint32_t>(min(i * 1024 + lane * 16, last)), dst + i * 1024);
   };
 
-  const int h = lane & 1;
-  const int blk_off = wave * S::kSegBytes + (lane >> 1) * S::BB;  // this lane's block in a row
+  const int q = lane % S::kLanesPerBlock;
+  const int blk_off = wave * S::kSegBytes + (lane / S::kLanesPerBlock) * S::BB;  // this lane's block in a row
 
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
@@ -264,27 +280,22 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
         }
       }
 
-      float xr[NTC][16];
+      float xr[NTC][E];
 #pragma unroll
       for (int t = 0; t < NTC; ++t) {
         if (slot[t] >= 0) {
-          const float* xs = p.x + static_cast<long long>(slot[t] / p.top_k) * p.k + wave * 1024;
+          const float* xs = p.x + static_cast<long long>(slot[t] / p.top_k) * p.k + wave * SLICE;
 #pragma unroll
-          for (int run = 0; run < 2; ++run) {
-            const float4* xp = reinterpret_cast<const float4*>(xs + x_run<WT>(lane, run));
-            const float4 v0 = xp[0], v1 = xp[1];
-            xr[t][8 * run + 0] = v0.x;
-            xr[t][8 * run + 1] = v0.y;
-            xr[t][8 * run + 2] = v0.z;
-            xr[t][8 * run + 3] = v0.w;
-            xr[t][8 * run + 4] = v1.x;
-            xr[t][8 * run + 5] = v1.y;
-            xr[t][8 * run + 6] = v1.z;
-            xr[t][8 * run + 7] = v1.w;
+          for (int j = 0; j < E / 4; ++j) {
+            const float4 v = *reinterpret_cast<const float4*>(xs + x_run<WT, E>(lane, j));
+            xr[t][4 * j + 0] = v.x;
+            xr[t][4 * j + 1] = v.y;
+            xr[t][4 * j + 2] = v.z;
+            xr[t][4 * j + 3] = v.w;
           }
         } else {
 #pragma unroll
-          for (int j = 0; j < 16; ++j) xr[t][j] = 0.f;
+          for (int j = 0; j < E; ++j) xr[t][j] = 0.f;
         }
       }
 
@@ -306,13 +317,13 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
           float acc[NTC][R];
 #pragma unroll
           for (int r = 0; r < R; ++r) {
-            float wv[16];
-            const float d = decode_lane<WT>(ring_lds, seg + r * rowbytes, h, wv);
+            float wv[E];
+            const float d = decode_lane<WT, E>(ring_lds, seg + r * rowbytes, q, wv);
 #pragma unroll
             for (int t = 0; t < NTC; ++t) {
               float s = 0.f;
 #pragma unroll
-              for (int j = 0; j < 16; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
+              for (int j = 0; j < E; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
               acc[t][r] = d * s;
             }
           }
@@ -379,15 +390,16 @@ int groups_per_cu(void (*kernel)(MatvecParams, int), int threads, int* cache) {
   return *cache;
 }
 
-template <int WT, int NTC, int R, int NSTAGE, int MAXW>
+template <int WT, int NTC, int R, int NSTAGE, int MAXW, int SLICE>
 hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
-  const int nw = p.k / 1024;
+  constexpr int kFlushRows = flush_rows(NTC, MAXW);
+  const int nw = p.k / SLICE;
   const int ntiles = (p.m + R - 1) / R;
-  auto kernel = matvec_sliced_kernel<WT, NTC, R, NSTAGE, MAXW>;
+  auto kernel = matvec_sliced_kernel<WT, NTC, R, NSTAGE, MAXW, SLICE>;
   // As many workgroups as are resident at once (no thin second round), split over the
   // experts; each walks a run of tiles with NSTAGE-1 of them in flight.
   const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
-  static int per_cu[9];  // per variant and wave count
+  static int per_cu[17];  // per variant and wave count
   int groups = groups_per_cu(kernel, 64 * nw, &per_cu[nw]) * device_cus() / experts;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
@@ -400,30 +412,41 @@ hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// Rows per tile and ring depth for each weight type, token count and wave count, from sweeps on
-// MI355X (Q8_0 4096x4096 at n = 1 and 4, Q4_0 14336x4096 at n = 1, bf16 4096x4096 at n = 1, and
-// the 16-token top-2-of-8 Q4_0 MoE): one tile in flight per workgroup with several workgroups per
-// CU beat deeper rings, and taller tiles pay off once several tokens share each decoded weight.
-// Eight-wave variants (k above 4096) halve the tile to stay inside the LDS.
-template <int WT, int NTC, int MAXW>
-struct SlicedShape {
-  static constexpr int R0 = WT == kBF16 ? (NTC >= 8 ? 2 : 4) : (NTC >= 4 ? 8 : 4);
-  static constexpr int R = MAXW > 4 && R0 > 2 ? R0 / 2 : R0;
-  static constexpr int NSTAGE = 2;
+// Launch shape: rows per tile, ring depth and k elements per wave.
+struct Shape {
+  int r, nstage, slice;
 };
 
-template <int WT, int NTC, int R4, int R8, int NSTAGE>
-hipError_t launch_shape(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
-  if (p.k <= 4096) return launch_r<WT, NTC, R4, NSTAGE, 4>(p, n_exp_rows, stream);
-  return launch_r<WT, NTC, R8, NSTAGE, 8>(p, n_exp_rows, stream);
+// Shapes per weight type, token count (1, 2, 4, 8) and k class (up to 4096, up to 8192), from
+// sweeps on MI355X of Q8_0 and bf16 4096 x k and Q4_0 14336 x 4096 / 4096 x 8192 at each token
+// count (the token pair at k = 8192 takes its neighbours' shape). Every workgroup loads the whole
+// activation rows, so the winners keep several workgroups per CU with one or two tiles in flight
+// each; 512-element slices win where a tile's arithmetic is heavy for its bytes (bf16, many
+// tokens), 1024-element slices where decoding dominates (Q4_0, one token).
+constexpr Shape sliced_shape(int wt, int ntc, bool k8) {
+  if (wt == kQ8_0) {
+    if (!k8) return ntc == 1 ? Shape{4, 2, 1024} : ntc == 2 ? Shape{8, 2, 512} : ntc == 4 ? Shape{8, 2, 1024}
+                                                                                             : Shape{4, 3, 512};
+    return ntc == 8 ? Shape{4, 2, 512} : Shape{4, 2, 1024};
+  }
+  if (wt == kQ4_0) {
+    if (!k8) return ntc == 4 ? Shape{4, 3, 1024} : Shape{4, 2, 1024};
+    return ntc == 1 ? Shape{8, 2, 1024} : Shape{4, 2, 1024};
+  }
+  return k8 ? Shape{2, 2, 1024} : Shape{4, 2, 512};
+}
+
+template <int WT, int NTC, bool K8>
+hipError_t launch_shaped(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
+  constexpr Shape c = sliced_shape(WT, NTC, K8);
+  constexpr int kMaxW = (K8 ? 8192 : 4096) / c.slice;
+  return launch_r<WT, NTC, c.r, c.nstage, kMaxW, c.slice>(p, n_exp_rows, stream);
 }
 
 template <int WT, int NTC>
 hipError_t launch_ntc(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
-  using C4 = SlicedShape<WT, NTC, 4>;
-  using C8 = SlicedShape<WT, NTC, 8>;
-  static_assert(C4::NSTAGE == C8::NSTAGE, "one ring depth per token count");
-  return launch_shape<WT, NTC, C4::R, C8::R, C4::NSTAGE>(p, n_exp_rows, stream);
+  if (p.k <= 4096) return launch_shaped<WT, NTC, false>(p, n_exp_rows, stream);
+  return launch_shaped<WT, NTC, true>(p, n_exp_rows, stream);
 }
 
 template <int WT>
