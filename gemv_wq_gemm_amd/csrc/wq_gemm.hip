@@ -317,24 +317,36 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 }
 
 // ---------------------------------------------------------------------------------------------
-// bf16 weights: a deeper pipeline (k step 32, NSTAGE LDS slots, NSTAGE-1 steps in flight).
+// bf16 weights: a deeper pipeline (k step BK, NSTAGE LDS slots, NSTAGE-1 steps in flight).
 //  * Both operands stream from global memory straight into LDS with global_load_lds_dwordx4, so
 //    the loads in flight hold no registers; X stays f32 in LDS and is rounded to bf16 (nearest
 //    even) as its fragments are read.
 //  * The loads are waited for with explicit vmcnt counts (wq_lds_dma.hpp).
+//  * The k step is 64: a step then takes whole 128-byte lines of every W row (and two of every X
+//    row). With a step of 32, each W row gives 64 bytes per step, and such half-line pieces
+//    stream into LDS at about 60% of the rate of whole lines (measured on MI355X).
 //  * LDS rows are XOR-swizzled by row so that the 16 lanes served per LDS cycle read 16 distinct
-//    groups of four banks: X rows (32 f32 = 8 chunks of 16 bytes) keep chunk c at
-//    c ^ ((r >> 1) & 7), W rows (32 bf16 = 4 chunks) at c ^ ((r >> 2) & 3).
+//    groups of four banks (64 banks): chunk c of 16 bytes in row r sits at c ^ s(r), where s(r)
+//    is r divided by the rows that fill the 64 banks, modulo the chunks per row: for k step 64,
+//    X rows (64 f32 = 16 chunks) use r & 15 and W rows (64 bf16 = 8 chunks) (r >> 1) & 7.
 //  * A direct-to-LDS load writes lane l's 16 bytes at (LDS base + 16 l); each lane fetches the
 //    global chunk that belongs at its LDS position. Rows past the end of X or W are clamped to the
 //    last row (their products land only in outputs that are never stored).
 
-__device__ __forceinline__ int x_swizzle(int r) { return (r >> 1) & 7; }
-__device__ __forceinline__ int w_swizzle(int r) { return (r >> 2) & 3; }
+// Swizzles for a k step of BK elements: rows of 4 BK bytes (X, f32) or 2 BK bytes (W, bf16).
+template <int BK>
+__device__ __forceinline__ int x_swizzle(int r) {
+  return (r >> (BK == 32 ? 1 : 0)) & (BK / 4 - 1);
+}
+template <int BK>
+__device__ __forceinline__ int w_swizzle(int r) {
+  return (r >> (BK == 32 ? 2 : 1)) & (BK / 8 - 1);
+}
 
-template <int BM, int BN, int WM, int WN, int NSTAGE>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int BK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n, int band) {
-  constexpr int BK = 32;
+  static_assert(BK == 32 || BK == 64, "k step");
+  constexpr int kXC = BK / 4, kWC = BK / 8;  // 16-byte chunks per X row and per W row
   constexpr int kWaves = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr int kABytes = BM * BK * 4;  // f32
@@ -377,15 +389,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 #pragma unroll
   for (int i = 0; i < kAInst; ++i) {
     const int L = (wave * kAInst + i) * 64 + lane;  // 16-byte chunk index in a step's X region
-    const int r = L >> 3, pos = L & 7;
-    const int c = pos ^ x_swizzle(r);
+    const int r = L / kXC, pos = L % kXC;
+    const int c = pos ^ x_swizzle<BK>(r);
     aoff[i] = static_cast<uint32_t>(min(n0 + r, p.n - 1)) * static_cast<uint32_t>(p.k) * 4u + c * 16u;
   }
 #pragma unroll
   for (int i = 0; i < kBInst; ++i) {
     const int L = (wave * kBInst + i) * 64 + lane;
-    const int r = L >> 2, pos = L & 3;
-    const int c = pos ^ w_swizzle(r);
+    const int r = L / kWC, pos = L % kWC;
+    const int c = pos ^ w_swizzle<BK>(r);
     boff[i] = static_cast<uint32_t>(min(m0 + r, p.m - 1)) * static_cast<uint32_t>(p.rowbytes) + c * 16u;
   }
   const uint32_t ring_lds = lds_address(ring);
@@ -439,7 +451,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
       for (int i = 0; i < FM; ++i) {
         const int r = wm * TM + i * 32 + frow;
         const int c0 = 4 * ks + 2 * khalf;  // two f32 chunks: k = 16 ks + 8 khalf .. +8
-        const int sw = x_swizzle(r);
+        const int sw = x_swizzle<BK>(r);
         ra[slot][i][0] = *reinterpret_cast<const float4*>(sa + r * BK + ((c0 ^ sw) << 2));
         ra[slot][i][1] = *reinterpret_cast<const float4*>(sa + r * BK + (((c0 + 1) ^ sw) << 2));
       }
@@ -447,24 +459,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
       for (int j = 0; j < FN; ++j) {
         const int r = wn * TN + j * 32 + frow;
         const int c = 2 * ks + khalf;
-        fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + r * BK + ((c ^ w_swizzle(r)) << 3));
+        fb[slot][j] = *reinterpret_cast<const bf16x8*>(sb + r * BK + ((c ^ w_swizzle<BK>(r)) << 3));
       }
     };
+    // Fragments of two 16-wide k slices are in registers at a time: slice ks + 2 is read into
+    // the slot of slice ks once its MFMAs are issued.
     read_frags(0, 0);
     read_frags(1, 1);
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
+      const int slot = ks & 1;
       bf16x8 a[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint2 l2 = round_bf16x4(ra[ks][i][0]), h2 = round_bf16x4(ra[ks][i][1]);
+        const uint2 l2 = round_bf16x4(ra[slot][i][0]), h2 = round_bf16x4(ra[slot][i][1]);
         a[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], fb[ks][j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], fb[slot][j], acc[i][j], 0, 0, 0);
+      if (ks + 2 < BK / 16) read_frags(ks + 2, slot);
     }
   }
 
@@ -529,12 +545,12 @@ int tile_band(int tiles_m, int per_xcd) {
   return best;
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int BK>
 hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
   const int tiles_m = (p.n + BM - 1) / BM;
   const int tiles_n = (p.m + BN - 1) / BN;
   const int per_xcd = (tiles_m * tiles_n + 7) / 8;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE>), dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream,
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK>), dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream,
                      p, tiles_m, tiles_n, tile_band(tiles_m, per_xcd));
   return hipGetLastError();
 }
@@ -548,12 +564,18 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
     if (!small_enough) return launch_tile<WT, 128, 128, 2, 2>(p, stream);
     const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
     // Measured on MI355X at n = 1500: 128 x 256 tiles win once they give at least half the CUs
-    // a tile; below that, 128 x 128 tiles (more of them) do. Both use 8 waves.
-    if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 4>(p, stream);
+    // a tile; below that, 128 x 128 tiles (more of them) do. Both use 8 waves. A k step of 64
+    // (k a multiple of 64) halves the ring depth that fits in the LDS.
     const long long mid_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 127) / 128);
-    if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 4>(p, stream);
-    // Few output tiles: 64 x 128 tiles keep more CUs streaming operands, with a deeper ring.
-    return launch_bf16<64, 128, 2, 4, 8>(p, stream);
+    if (p.k % 64 == 0) {
+      if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
+      if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 3, 64>(p, stream);
+      // Few output tiles: 64 x 128 tiles keep more CUs streaming operands, with a deeper ring.
+      return launch_bf16<64, 128, 2, 4, 4, 64>(p, stream);
+    }
+    if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 4, 32>(p, stream);
+    if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 4, 32>(p, stream);
+    return launch_bf16<64, 128, 2, 4, 8, 32>(p, stream);
   }
   // Wide tiles (128 X rows x 256 W rows) when they still give every CU work,
   // 128 x 128 otherwise.
