@@ -35,6 +35,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdlib>
+#include <type_traits>
 
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
@@ -484,24 +485,38 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
     }
   }
 
+  // The epilogue, with the flag tests taken once per workgroup and the bounds tests only on
+  // tiles that reach past the edge of Y.
+  const bool full = n0 + BM <= p.n && m0 + BN <= p.m;
+  auto store = [&](auto gelu, auto res) {
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = m0 + wn * TN + j * 32 + frow;
-    if (col >= p.m) continue;
+    for (int j = 0; j < FN; ++j) {
+      const int col = m0 + wn * TN + j * 32 + frow;
+      if (!full && col >= p.m) continue;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+      for (int i = 0; i < FM; ++i) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = n0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        if (row < p.n) {
-          float* yp = p.y + static_cast<long long>(row) * p.m + col;
-          float o = acc[i][j][v] + bias_v[j];
-          if (p.flags & 2u) o = gelu_erf(o);
-          if (p.flags & 4u) o += *yp;
-          *yp = o;
+        for (int v = 0; v < 16; ++v) {
+          const int row = n0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          if (full || row < p.n) {
+            float* yp = p.y + static_cast<long long>(row) * p.m + col;
+            float o = acc[i][j][v] + bias_v[j];
+            if constexpr (decltype(gelu)::value) o = gelu_erf(o);
+            if constexpr (decltype(res)::value) o += *yp;
+            *yp = o;
+          }
         }
       }
     }
+  };
+  using T = std::true_type;
+  using F = std::false_type;
+  if (p.flags & 2u) {
+    if (p.flags & 4u) store(T{}, T{});
+    else store(T{}, F{});
+  } else {
+    if (p.flags & 4u) store(F{}, T{});
+    else store(F{}, F{});
   }
 }
 

@@ -167,6 +167,22 @@ def test_identity_weight():
     assert np.array_equal(got, x[:16])
 
 
+@pytest.mark.parametrize("path", [wq.PATH_MATVEC, wq.PATH_MFMA])
+def test_gelu_epilogue_alone(path):
+    """With identity bf16 weights and bf16-exact activations (j/32, |j| < 256) the pre-activation
+    is exact on both paths, so all that is left is the epilogue's erf-GELU. It is held to the f32
+    rounding slack alone, against the exact erf."""
+    from tests.parity import ULP_SLACK
+    n, k = 4, 128
+    j = np.arange(-255, 257, dtype=np.float64)  # 512 values in [-7.97, 8.0]
+    x = (j / 32.0).astype(np.float32).reshape(n, k)
+    w = np.where(np.eye(k, dtype=bool), 0x3F80, 0).astype(np.uint16)
+    got = _run(x, w, wq.W_BF16, k, k, None, int(wq.GELU), None, path)
+    v = x.astype(np.float64)
+    y_ref = oracle.gelu_erf(v)
+    assert_within(got, y_ref, ULP_SLACK * (np.abs(v) + np.abs(y_ref)) + 1e-30, f"gelu alone path={path}")
+
+
 def test_zero_sized_calls_leave_output_alone():
     import torch
     x = torch.zeros(0, 32, device="cuda")
