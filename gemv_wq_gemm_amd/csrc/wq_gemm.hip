@@ -578,16 +578,24 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
   if constexpr (WT == kBF16) {
     if (!small_enough) return launch_tile<WT, 128, 128, 2, 2>(p, stream);
     const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
-    // Measured on MI355X at n = 1500: 128 x 256 tiles win once they give at least half the CUs
-    // a tile; below that, 128 x 128 tiles (more of them) do. Both use 8 waves. A k step of 64
-    // (k a multiple of 64) halves the ring depth that fits in the LDS.
     const long long mid_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 127) / 128);
     if (p.k % 64 == 0) {
-      if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
-      if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 3, 64>(p, stream);
-      // Few output tiles: 64 x 128 tiles keep more CUs streaming operands, with a deeper ring.
+      // A k step of 64 (k a multiple of 64). Measured on MI355X over n x m x k from
+      // 256 x 2048 x 2048 to 8192 x 8192 x 4096:
+      //  * a 128 x 256 tile for every CU: those tiles (fewest operand re-reads);
+      //  * more 64 x 128 tiles than CUs: those, two workgroups per CU (a 2-slot ring), so one
+      //    tile's epilogue and stores overlap the other's k loop;
+      //  * fewer: 64 x 64 tiles of 4 waves when the tiles are very few or k is short (more
+      //    tiles in flight), else 64 x 128 tiles with a 4-slot ring.
+      const int cus = device_cus();
+      const long long small_tiles = static_cast<long long>((p.n + 63) / 64) * ((p.m + 127) / 128);
+      if (wide_tiles >= cus) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
+      if (small_tiles > cus) return launch_bf16<64, 128, 2, 4, 2, 64>(p, stream);
+      if (small_tiles <= cus / 2 || p.k <= 1024) return launch_bf16<64, 64, 2, 2, 3, 64>(p, stream);
       return launch_bf16<64, 128, 2, 4, 4, 64>(p, stream);
     }
+    // k an odd multiple of 32 (k step 32): measured at n = 1500, 128 x 256 tiles win once they
+    // give at least half the CUs a tile; below that, 128 x 128 tiles (more of them) do.
     if (wide_tiles >= device_cus() / 2) return launch_bf16<128, 256, 2, 4, 4, 32>(p, stream);
     if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 4, 32>(p, stream);
     return launch_bf16<64, 128, 2, 4, 8, 32>(p, stream);

@@ -107,6 +107,20 @@ def test_gemm_parity(wtype, n, m, k):
     assert_within(got, y_ref, tol, f"gemm wtype={wtype} n={n} m={m} k={k} flags={flags}")
 
 
+# Shapes that take each bf16 tile variant of the GEMM (on a 256-CU MI355X), all with ragged
+# edges: 128x256 tiles (one per CU or more), 64x128 tiles two per CU, 64x64 tiles, and 64x128
+# tiles with a 4-slot ring (few tiles, long k).
+TILE_VARIANT_SHAPES = [(2050, 4100, 128, 5), (1100, 2000, 64, 3), (700, 1000, 192, 1), (1000, 2000, 1088, 7)]
+
+
+@pytest.mark.parametrize("n,m,k,flags", TILE_VARIANT_SHAPES)
+def test_gemm_bf16_tile_variants(n, m, k, flags):
+    x, w, bias, y_old = _inputs(15, wq.W_BF16, n, m, k, flags)
+    got = _run(x, w, wq.W_BF16, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wq.W_BF16, m, k, bias, flags, y_old, B_MFMA)
+    assert_within(got, y_ref, tol, f"gemm bf16 n={n} m={m} k={k} flags={flags}")
+
+
 @pytest.mark.parametrize("flags", range(8))
 def test_gemm_every_flag_combination(flags):
     wtype, n, m, k = wq.W_Q4_0, 70, 140, 192
