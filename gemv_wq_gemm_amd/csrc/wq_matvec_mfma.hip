@@ -1,7 +1,10 @@
-// The MoE matvec on matrix cores, with f32 accuracy (Q8_0 and Q4_0 weights).
+// The MoE matvec on matrix cores, with f32 accuracy (Q8_0 and Q4_0 weights); also the plain layer
+// at 9 to 16 tokens.
 //
 // Contract: per routed slot s and output row j, y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k]
-// (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), the same as the f32 matvec kernels.
+// (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), the same as the f32 matvec kernels. Without
+// ids (the plain layer) every slot takes the one weight and the store applies the epilogue
+// (bias, erf-GELU, + old Y).
 //
 // Why matrix cores: with f32 FMAs every weight costs one instruction per routed slot, so an
 // expert's several slots make the kernel bound by the vector ALU, not by HBM. Here each weight
@@ -152,8 +155,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
   const int t_begin = blockIdx.x * tiles_per_wg;
   const int t_end = min(ntiles, t_begin + tiles_per_wg);
   if (t_begin >= ntiles) return;  // workgroup-uniform
+  const bool moe = p.ids != nullptr;
 
-  if (e == p.n_exp) {
+  if (moe && e == p.n_exp) {
     // Slots routed outside the bank: their outputs in this run of rows become NaN.
     for (int win = 0; win < p.n_slots; win += 64) {
       const int s = win + lane;
@@ -212,18 +216,27 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
         // Not unrolled: this runs inside the tile loop, where registers are scarce.
 #pragma unroll 1
         for (int w = 0; w < nw; ++w) v += part[buf][w * kPartWave + i];
-        p.y[static_cast<long long>(slot) * p.m + row] = v;
+        float* yp = p.y + static_cast<long long>(slot) * p.m + row;
+        if (!moe) {
+          if (p.flags & 1u) v += p.bias[row];
+          if (p.flags & 2u) v = gelu_erf(v);
+          if (p.flags & 4u) v += *yp;
+        }
+        *yp = v;
       }
     }
   };
 
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
-    {
+    if (moe) {
       const int s = win + lane;
       int id = -1;
       if (s < p.n_slots) id = p.ids[s];
       mask = __ballot(id == e);
+    } else {
+      const int left = p.n_slots - win;
+      mask = left >= 64 ? ~0ull : ((1ull << left) - 1ull);
     }
     while (mask) {
       // This pass's slots, in order: A row (and D row) t is slot_of[t].
@@ -333,7 +346,7 @@ hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   const int tpw = (ntiles + groups - 1) / groups;
-  dim3 grid((ntiles + tpw - 1) / tpw, p.n_exp + 1);
+  dim3 grid((ntiles + tpw - 1) / tpw, p.ids ? p.n_exp + 1 : 1);
   hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, stream, p, tpw);
   return hipGetLastError();
 }
@@ -345,7 +358,7 @@ bool matvec_mfma_supports(int wtype, int k) {
 }
 
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream) {
-  if (!matvec_mfma_supports(wtype, p.k) || p.ids == nullptr) return hipErrorInvalidValue;
+  if (!matvec_mfma_supports(wtype, p.k) || (p.ids == nullptr && p.n_exp != 1)) return hipErrorInvalidValue;
   // LDS: a Q8_0 tile is twice a Q4_0 one, so Q8_0 runs a shallower ring.
   if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2>(p, stream);
   return launch_mfma<kQ4_0, 3>(p, stream);

@@ -92,6 +92,19 @@ def test_matvec_every_flag_combination(flags):
     assert_within(got, y_ref, tol, f"flags={flags}")
 
 
+@pytest.mark.parametrize("wtype", [wq.W_Q8_0, wq.W_Q4_0])
+@pytest.mark.parametrize("n", [9, 16])
+@pytest.mark.parametrize("flags", range(8))
+def test_matvec_matrix_core_route_every_flag(wtype, n, flags):
+    """Plain calls with 9-16 tokens on Q8_0 / Q4_0 (k 2048-4096) take the matrix-core kernel
+    (exact three-part activations), which then applies the epilogue itself."""
+    m, k = 75, 2048
+    x, w, bias, y_old = _inputs(16, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_F32)
+    assert_within(got, y_ref, tol, f"matrix-core matvec wtype={wtype} n={n} flags={flags}")
+
+
 # ---------------------------------------------------------------- MFMA path (bf16 x, exact w)
 
 GEMM_SHAPES = [(17, 1, 32), (64, 37, 96), (130, 128, 256), (200, 288, 160), (257, 130, 1024)]
