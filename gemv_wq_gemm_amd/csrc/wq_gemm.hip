@@ -600,11 +600,12 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
     if (mid_tiles >= device_cus() / 2) return launch_bf16<128, 128, 2, 4, 4, 32>(p, stream);
     return launch_bf16<64, 128, 2, 4, 8, 32>(p, stream);
   }
-  // Wide tiles (128 X rows x 256 W rows) when they still give every CU work,
-  // 128 x 128 otherwise.
+  // 8 waves per workgroup (two per SIMD, which hides the register-staged loads): 128 x 256 tiles
+  // once there are two per CU, 64 x 128 tiles below (measured on MI355X from 256 x 2048 x 2048 to
+  // 4096^3; at n = 1500 about 1.7x faster than 4-wave 128 x 256 / 128 x 128 tiles).
   const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
-  if (wide_tiles >= device_cus() / 2) return launch_tile<WT, 128, 256, 2, 2>(p, stream);
-  return launch_tile<WT, 128, 128, 2, 2>(p, stream);
+  if (wide_tiles >= 2LL * device_cus()) return launch_tile<WT, 128, 256, 2, 4>(p, stream);
+  return launch_tile<WT, 64, 128, 2, 4>(p, stream);
 }
 
 }  // namespace

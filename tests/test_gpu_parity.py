@@ -127,6 +127,17 @@ TILE_VARIANT_SHAPES = [(2050, 4100, 128, 5), (1100, 2000, 64, 3), (700, 1000, 19
                        (1000, 2000, 1088, 5), (900, 2040, 2048, 4)]
 
 
+@pytest.mark.parametrize("wtype", [wq.W_Q8_0, wq.W_Q4_0])
+@pytest.mark.parametrize("n,m,k,flags", [(2050, 8200, 64, 3), (1100, 2000, 128, 5), (300, 700, 512, 4)])
+def test_gemm_quantized_tile_variants(wtype, n, m, k, flags):
+    """Quantized weights on the matrix cores: 128x256 tiles (two per CU or more) and 64x128 tiles
+    (with and without the k split), ragged edges."""
+    x, w, bias, y_old = _inputs(17, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_MFMA)
+    assert_within(got, y_ref, tol, f"gemm wtype={wtype} n={n} m={m} k={k} flags={flags}")
+
+
 @pytest.mark.parametrize("n,m,k,flags", TILE_VARIANT_SHAPES)
 def test_gemm_bf16_tile_variants(n, m, k, flags):
     x, w, bias, y_old = _inputs(15, wq.W_BF16, n, m, k, flags)
