@@ -258,6 +258,19 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     fl = 24 * 2 * n * (3 * d * d + d * d + ff * d + d * ff)
     out["encoder_chain_bf16_24x4_n1500"] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
                                             "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del layers, calls
+
+    # Quantized weights on the matrix cores: the encoder's MLP-up shape (X[1500 x 1024], W[4096 x 1024]
+    # as Q8_0 / Q4_0 blocks, bias + GELU), 4 weight copies rotated.
+    for wt, name in ((wq.W_Q8_0, "q8_0"), (wq.W_Q4_0, "q4_0")):
+        ws = [to_dev(synth.weight(synth.rng(40 + i, wt), wt, ff, d).reshape(-1)) for i in range(4)]
+        bq = to_dev(synth.normal_f32(synth.rng(44, wt), (ff,), 0.1))
+        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f) for w_ in ws]
+        med = _time_calls(torch, stream, lambda i: gq[i % 4](), 40)
+        fl = 2 * n * ff * d
+        out[f"gemm_{name}_{n}x{ff}x{d}_gelu"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
+                                                 "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del ws, gq
     return out
 
 
