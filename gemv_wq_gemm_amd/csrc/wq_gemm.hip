@@ -583,13 +583,18 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
       // A k step of 64 (k a multiple of 64). Measured on MI355X over n x m x k from
       // 256 x 2048 x 2048 to 8192 x 8192 x 4096:
       //  * a 128 x 256 tile for every CU: those tiles (fewest operand re-reads);
-      //  * more 64 x 128 tiles than CUs: those, two workgroups per CU (a 2-slot ring), so one
-      //    tile's epilogue and stores overlap the other's k loop;
+      //  * more 64 x 128 tiles than CUs: tiles two workgroups per CU (2-slot rings), so one
+      //    tile's epilogue and stores overlap the other's k loop. A round is two tiles per CU:
+      //    64 x 128 tiles when they fit one round or 64 x 192 tiles do not either, else 64 x 192
+      //    tiles of 4 waves (one round instead of a thin second one: 1500 x 3072 x 1024
+      //    26.5 -> 19.1 us);
       //  * fewer: 64 x 64 tiles of 4 waves when the tiles are very few or k is short (more
       //    tiles in flight), else 64 x 128 tiles with a 4-slot ring.
       const int cus = device_cus();
       const long long small_tiles = static_cast<long long>((p.n + 63) / 64) * ((p.m + 127) / 128);
+      const long long tall_tiles = static_cast<long long>((p.n + 63) / 64) * ((p.m + 191) / 192);
       if (wide_tiles >= cus) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
+      if (small_tiles > 2LL * cus && tall_tiles <= 2LL * cus) return launch_bf16<64, 192, 2, 2, 2, 64>(p, stream);
       if (small_tiles > cus) return launch_bf16<64, 128, 2, 4, 2, 64>(p, stream);
       if (small_tiles <= cus / 2 || p.k <= 1024) return launch_bf16<64, 64, 2, 2, 3, 64>(p, stream);
       return launch_bf16<64, 128, 2, 4, 4, 64>(p, stream);

@@ -121,10 +121,10 @@ def test_gemm_parity(wtype, n, m, k):
 
 
 # Shapes that take each bf16 tile variant of the GEMM (on a 256-CU MI355X), all with ragged
-# edges: 128x256 tiles (one per CU or more), 64x128 tiles two per CU, 64x64 tiles, and 64x128
-# tiles with a 4-slot ring (few tiles, long k; every epilogue).
-TILE_VARIANT_SHAPES = [(2050, 4100, 128, 5), (1100, 2000, 64, 3), (700, 1000, 192, 1), (1000, 2000, 1088, 7),
-                       (1000, 2000, 1088, 5), (900, 2040, 2048, 4)]
+# edges: 128x256 tiles (one per CU or more), 64x128 tiles two per CU, 64x192 tiles two per CU,
+# 64x64 tiles, and 64x128 tiles with a 4-slot ring (few tiles, long k; every epilogue).
+TILE_VARIANT_SHAPES = [(2050, 4100, 128, 5), (1100, 2000, 64, 3), (1500, 3000, 64, 3), (1530, 2900, 192, 5),
+                       (700, 1000, 192, 1), (1000, 2000, 1088, 7), (1000, 2000, 1088, 5), (900, 2040, 2048, 4)]
 
 
 @pytest.mark.parametrize("wtype", [wq.W_Q8_0, wq.W_Q4_0])
