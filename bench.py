@@ -26,7 +26,8 @@ The same JSON line carries:
                 bounded sample of the same workload, on the host's cores;
   others        the remaining workloads (bf16 GEMM 64x256x256, Q4_0 matvec
                 14336x4096, MoE 16 tokens top-2 of 8, the 24-layer encoder
-                chain) with their own TFLOP/s or GB/s and roofline fractions.
+                chain, also on the f32-accurate matrix-core path) with their own
+                TFLOP/s or GB/s and roofline fractions.
 """
 from __future__ import annotations
 
@@ -243,22 +244,32 @@ def _others(torch, wq, synth, dev, stream, to_dev):
     qkv = torch.empty((n, 3 * d), device=dev)
     f = torch.empty((n, ff), device=dev)
 
-    calls = []
-    for W_ in layers:
-        calls.append(wq.bind_gemm(a1, W_["qkv"][0], wq.W_BF16, m=3 * d, k=d, bias=W_["qkv"][1], out=qkv))
-        calls.append(wq.bind_gemm(a2, W_["out"][0], wq.W_BF16, m=d, k=d, bias=W_["out"][1], residual=True, out=h))
-        calls.append(wq.bind_gemm(a3, W_["fc1"][0], wq.W_BF16, m=ff, k=d, bias=W_["fc1"][1], gelu=True, out=f))
-        calls.append(wq.bind_gemm(f, W_["fc2"][0], wq.W_BF16, m=d, k=ff, bias=W_["fc2"][1], residual=True, out=h))
+    def bind_chain(path):
+        calls = []
+        for W_ in layers:
+            calls.append(wq.bind_gemm(a1, W_["qkv"][0], wq.W_BF16, m=3 * d, k=d, bias=W_["qkv"][1], out=qkv,
+                                      path=path))
+            calls.append(wq.bind_gemm(a2, W_["out"][0], wq.W_BF16, m=d, k=d, bias=W_["out"][1], residual=True,
+                                      out=h, path=path))
+            calls.append(wq.bind_gemm(a3, W_["fc1"][0], wq.W_BF16, m=ff, k=d, bias=W_["fc1"][1], gelu=True,
+                                      out=f, path=path))
+            calls.append(wq.bind_gemm(f, W_["fc2"][0], wq.W_BF16, m=d, k=ff, bias=W_["fc2"][1], residual=True,
+                                      out=h, path=path))
 
-    def chain(_):
-        for c in calls:
-            c()
+        def chain(_):
+            for c in calls:
+                c()
+        return chain
 
-    med = _time_calls(torch, stream, chain, 10, warm=2)
     fl = 24 * 2 * n * (3 * d * d + d * d + ff * d + d * ff)
-    out["encoder_chain_bf16_24x4_n1500"] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
-                                            "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    del layers, calls
+    # bf16(X) on the matrix cores (the 2^-8 bound), then X as bf16 hi + lo parts (the f32 bound;
+    # twice the MFMA work, FLOP counted once).
+    for path, name in ((wq.PATH_AUTO, "encoder_chain_bf16_24x4_n1500"),
+                       (wq.PATH_MFMA_F32, "encoder_chain_bf16_f32acc_24x4_n1500")):
+        med = _time_calls(torch, stream, bind_chain(path), 10, warm=2)
+        out[name] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
+                     "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del layers
 
     # Quantized weights on the matrix cores: the encoder's MLP-up shape (X[1500 x 1024], W[4096 x 1024]
     # as Q8_0 / Q4_0 blocks, bias + GELU), 4 weight copies rotated.
@@ -270,6 +281,11 @@ def _others(torch, wq, synth, dev, stream, to_dev):
         fl = 2 * n * ff * d
         out[f"gemm_{name}_{n}x{ff}x{d}_gelu"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
                                                  "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f, path=wq.PATH_MFMA_F32) for w_ in ws]
+        med = _time_calls(torch, stream, lambda i: gq[i % 4](), 40)
+        out[f"gemm_{name}_f32acc_{n}x{ff}x{d}_gelu"] = {
+            "us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
+            "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
         del ws, gq
     return out
 

@@ -17,7 +17,7 @@ import os
 
 W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
 BIAS, GELU, RESIDUAL = 1, 2, 4
-PATH_AUTO, PATH_MATVEC, PATH_MFMA = 0, 1, 2
+PATH_AUTO, PATH_MATVEC, PATH_MFMA, PATH_MFMA_F32 = 0, 1, 2, 3
 MATVEC_MAX_N = 16
 
 STATUS = {

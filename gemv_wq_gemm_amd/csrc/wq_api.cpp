@@ -100,7 +100,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
   if (flags & ~(WQ_BIAS | WQ_GELU | WQ_RESIDUAL)) return fail(WQ_ERR_FLAGS, "unknown flag bits 0x%x", flags);
   if (((flags & WQ_BIAS) != 0) != (bias != nullptr))
     return fail(WQ_ERR_FLAGS, "WQ_BIAS must be set exactly when a bias pointer is given");
-  if (path != WQ_PATH_AUTO && path != WQ_PATH_MATVEC && path != WQ_PATH_MFMA)
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_MATVEC && path != WQ_PATH_MFMA && path != WQ_PATH_MFMA_F32)
     return fail(WQ_ERR_SHAPE, "unknown path %d", path);
   if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size n = %lld, m = %lld", (long long)n, (long long)m);
   if (int r = check_k(k)) return r;
@@ -108,7 +108,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
   if (path == WQ_PATH_AUTO) path = n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
   if (path == WQ_PATH_MATVEC && n > WQ_MATVEC_MAX_N)
     return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
-  if (path == WQ_PATH_MFMA && n > 65535LL * 128)
+  if ((path == WQ_PATH_MFMA || path == WQ_PATH_MFMA_F32) && n > 65535LL * 128)
     return fail(WQ_ERR_SHAPE, "n = %lld exceeds the GEMM grid (65535 x 128 rows)", (long long)n);
   if (n == 0 || m == 0) return WQ_OK;
   if (!x || !w || !y) return fail(WQ_ERR_NULL, "x, w and y must not be NULL");
@@ -150,6 +150,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.k = static_cast<int>(k);
     p.rowbytes = rowbytes;
     p.flags = flags;
+    p.x_parts = path == WQ_PATH_MFMA_F32 ? 3 : 1;
     e = wq::launch_gemm(wtype, p, s);
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");

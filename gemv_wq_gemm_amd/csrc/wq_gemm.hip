@@ -28,6 +28,9 @@
 //  * Tiles are numbered so that consecutive tiles share W rows, and the tile
 //    numbers are dealt to the 8 XCDs in contiguous ranges (workgroup i runs on
 //    XCD i % 8), so an XCD's L2 holds the panels its tiles reuse.
+//  * With X in three parts (the f32-accurate path) x = p1 + p2 + p3 exactly, each part bf16:
+//    the parts sit in three LDS buffers and each fragment takes three MFMAs into the same
+//    accumulator, so the products are exact and only the f32 sums round.
 //  * Split-K: when the output has too few tiles to fill the chip and the
 //    epilogue is linear in the product (no GELU, accumulate into Y), gridDim.z
 //    workgroups share a tile's k range and add their partial sums into Y with
@@ -63,6 +66,23 @@ __device__ __forceinline__ uint2 round_bf16x4(float4 v) {
   b[0] = static_cast<__bf16>(v.z);
   b[1] = static_cast<__bf16>(v.w);
   return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+// Splits four f32 values into three bf16 parts (pairs packed as round_bf16x4 packs them):
+// p1 = bf16(v), p2 = bf16(v - p1), p3 = bf16(v - p1 - p2), each rounded to nearest even. Both
+// differences are exact in f32, and what is left for p3 has at most 8 significant bits, so
+// p1 + p2 + p3 == v exactly (for |v| where bf16 holds the parts as normal numbers).
+__device__ __forceinline__ float bf16_lo_f32(uint32_t pair) { return __uint_as_float(pair << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t pair) { return __uint_as_float(pair & 0xFFFF0000u); }
+
+__device__ __forceinline__ void split3_bf16x4(float4 v, uint2& p1, uint2& p2, uint2& p3) {
+  p1 = round_bf16x4(v);
+  const float4 r1 = make_float4(v.x - bf16_lo_f32(p1.x), v.y - bf16_hi_f32(p1.x), v.z - bf16_lo_f32(p1.y),
+                                v.w - bf16_hi_f32(p1.y));
+  p2 = round_bf16x4(r1);
+  const float4 r2 = make_float4(r1.x - bf16_lo_f32(p2.x), r1.y - bf16_hi_f32(p2.x), r1.z - bf16_lo_f32(p2.y),
+                                r1.w - bf16_hi_f32(p2.y));
+  p3 = round_bf16x4(r2);
 }
 
 // Decoded block -> 16 dwords of bf16 pairs in element order.
@@ -111,11 +131,14 @@ struct QStage {
   bool ok[NQ];
 };
 
-template <int WT, int BM, int BN, int WM, int WN>
+template <int WT, int BM, int BN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
   using C = GemmCfg<WT, BM, BN, WM, WN>;
   constexpr bool kQuant = WT != kBF16;
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][BM * LDS_STRIDE];
+  // SPLIT: the second and third bf16 parts of X beside the first ones in sA.
+  __shared__ __attribute__((aligned(16))) __bf16 sAm[2][SPLIT ? BM * LDS_STRIDE : 8];
+  __shared__ __attribute__((aligned(16))) __bf16 sAl[2][SPLIT ? BM * LDS_STRIDE : 8];
   __shared__ __attribute__((aligned(16))) __bf16 sB[2][BN * LDS_STRIDE];
   __shared__ float sS[2][kQuant ? BN * 2 : 1];
 
@@ -193,7 +216,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 #pragma unroll
     for (int i = 0; i < C::kXLoads; ++i) {
       const int r = xr0 + i * (C::kThreads / 16);
-      *reinterpret_cast<uint2*>(&sA[buf][r * LDS_STRIDE + 4 * xc4]) = round_bf16x4(xs[i]);
+      if constexpr (SPLIT) {
+        uint2 p1, p2, p3;
+        split3_bf16x4(xs[i], p1, p2, p3);
+        *reinterpret_cast<uint2*>(&sA[buf][r * LDS_STRIDE + 4 * xc4]) = p1;
+        *reinterpret_cast<uint2*>(&sAm[buf][r * LDS_STRIDE + 4 * xc4]) = p2;
+        *reinterpret_cast<uint2*>(&sAl[buf][r * LDS_STRIDE + 4 * xc4]) = p3;
+      } else {
+        *reinterpret_cast<uint2*>(&sA[buf][r * LDS_STRIDE + 4 * xc4]) = round_bf16x4(xs[i]);
+      }
     }
     if constexpr (!kQuant) {
 #pragma unroll
@@ -249,6 +280,20 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
     for (int i = 0; i < C::FM; ++i)
 #pragma unroll
       for (int j = 0; j < C::FN; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
+    if constexpr (SPLIT) {
+#pragma unroll
+      for (int part = 0; part < 2; ++part) {
+        const __bf16* src = part == 0 ? sAm[buf] : sAl[buf];
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+          a[i] = *reinterpret_cast<const bf16x8*>(&src[(wm * C::TM + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j)
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
+      }
+    }
   };
 
   if (s_begin < s_end) {
@@ -321,7 +366,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 // bf16 weights: a deeper pipeline (k step BK, NSTAGE LDS slots, NSTAGE-1 steps in flight).
 //  * Both operands stream from global memory straight into LDS with global_load_lds_dwordx4, so
 //    the loads in flight hold no registers; X stays f32 in LDS and is rounded to bf16 (nearest
-//    even) as its fragments are read.
+//    even) as its fragments are read -- or, on the f32-accurate path, split there into three
+//    exact bf16 parts that take three MFMAs into the same accumulator.
 //  * The loads are waited for with explicit vmcnt counts (wq_lds_dma.hpp).
 //  * The k step is 64: a step then takes whole 128-byte lines of every W row (and two of every X
 //    row). With a step of 32, each W row gives 64 bytes per step, and such half-line pieces
@@ -344,7 +390,7 @@ __device__ __forceinline__ int w_swizzle(int r) {
   return (r >> (BK == 32 ? 2 : 1)) & (BK / 8 - 1);
 }
 
-template <int BM, int BN, int WM, int WN, int NSTAGE, int BK>
+template <int BM, int BN, int WM, int WN, int NSTAGE, int BK, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n, int band) {
   static_assert(BK == 32 || BK == 64, "k step");
   constexpr int kXC = BK / 4, kWC = BK / 8;  // 16-byte chunks per X row and per W row
@@ -470,17 +516,35 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int slot = ks & 1;
-      bf16x8 a[FM];
+      bf16x8 a[FM], am[FM], al[FM];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        const uint2 l2 = round_bf16x4(ra[slot][i][0]), h2 = round_bf16x4(ra[slot][i][1]);
-        a[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        if constexpr (SPLIT) {
+          uint2 l1, l2, l3, h1, h2, h3;
+          split3_bf16x4(ra[slot][i][0], l1, l2, l3);
+          split3_bf16x4(ra[slot][i][1], h1, h2, h3);
+          a[i] = __builtin_bit_cast(bf16x8, make_uint4(l1.x, l1.y, h1.x, h1.y));
+          am[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+          al[i] = __builtin_bit_cast(bf16x8, make_uint4(l3.x, l3.y, h3.x, h3.y));
+        } else {
+          const uint2 l2 = round_bf16x4(ra[slot][i][0]), h2 = round_bf16x4(ra[slot][i][1]);
+          a[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
+        }
       }
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], fb[slot][j], acc[i][j], 0, 0, 0);
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) {
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(am[i], fb[slot][j], acc[i][j], 0, 0, 0);
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(al[i], fb[slot][j], acc[i][j], 0, 0, 0);
+          }
+      }
       if (ks + 2 < BK / 16) read_frags(ks + 2, slot);
     }
   }
@@ -534,6 +598,13 @@ int device_cus() {
 
 template <int WT, int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
+  // X in three parts needs three A buffers in LDS: more than fits beside W for 128 x 256 tiles.
+  constexpr bool kPartsFit = BM * BN <= 128 * 128;
+  auto kernel = gemm_kernel<WT, BM, BN, WM, WN, false>;
+  if (p.x_parts == 3) {
+    if constexpr (kPartsFit) kernel = gemm_kernel<WT, BM, BN, WM, WN, true>;
+    else return hipErrorInvalidValue;
+  }
   const int tiles_m = (p.n + BM - 1) / BM;
   const int tiles_n = (p.m + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
@@ -547,7 +618,7 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
   }
   const int per_xcd = (tiles + 7) / 8;
   dim3 grid(per_xcd * 8, 1, splits);
-  hipLaunchKernelGGL((gemm_kernel<WT, BM, BN, WM, WN>), grid, dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n);
+  hipLaunchKernelGGL(kernel, grid, dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n);
   return hipGetLastError();
 }
 
@@ -565,8 +636,10 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
   const int tiles_m = (p.n + BM - 1) / BM;
   const int tiles_n = (p.m + BN - 1) / BN;
   const int per_xcd = (tiles_m * tiles_n + 7) / 8;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK>), dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream,
-                     p, tiles_m, tiles_n, tile_band(tiles_m, per_xcd));
+  auto kernel = p.x_parts == 3 ? gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK, true>
+                               : gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK, false>;
+  hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n,
+                     tile_band(tiles_m, per_xcd));
   return hipGetLastError();
 }
 
@@ -608,8 +681,9 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
   // 8 waves per workgroup (two per SIMD, which hides the register-staged loads): 128 x 256 tiles
   // once there are two per CU, 64 x 128 tiles below (measured on MI355X from 256 x 2048 x 2048 to
   // 4096^3; at n = 1500 about 1.7x faster than 4-wave 128 x 256 / 128 x 128 tiles).
+  // (X in three parts takes 64 x 128 tiles: the parts of a 128-row tile do not fit in LDS beside W.)
   const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
-  if (wide_tiles >= 2LL * device_cus()) return launch_tile<WT, 128, 256, 2, 4>(p, stream);
+  if (wide_tiles >= 2LL * device_cus() && p.x_parts == 1) return launch_tile<WT, 128, 256, 2, 4>(p, stream);
   return launch_tile<WT, 64, 128, 2, 4>(p, stream);
 }
 

@@ -62,6 +62,7 @@ struct GemmParams {
   int n, m, k;
   long long rowbytes;
   unsigned flags;
+  int x_parts;        // 3: X enters as three exact bf16 parts (three MFMAs per product); 1: as bf16(X)
 };
 
 hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream);

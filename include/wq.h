@@ -69,10 +69,21 @@ extern "C" {
  *   nearest even), W fed exactly (bf16 as stored; Q8_0/Q4_0 as their integer
  *   quants, with the f16 scale applied in f32 per 32-element block), f32
  *   accumulation. Error: |y - y_ref| <= 2^-8 * sum_k |x_k * w_k|.
+ * WQ_PATH_MFMA_F32: the matrix-core path with f32 accuracy for any n: the
+ *   arithmetic of the encoder on the cortiq-engine page (nemotron_audio.rs,
+ *   module doc: bf16 weights, f32 activations and f32 accumulation, as its
+ *   fp32 reference tower computes). Each x is split into three bf16 parts,
+ *   p1 = bf16(x), p2 = bf16(x - p1), p3 = bf16(x - p1 - p2) (nearest even),
+ *   which add up to x exactly; each part is multiplied by the exact weights
+ *   on the matrix cores (three times the MFMA work of WQ_PATH_MFMA). The
+ *   products are thus exact and only the f32 running sums round, as in an f32
+ *   GEMM; the result is held to the WQ_PATH_MATVEC bound,
+ *   |y - y_ref| <= 1e-5 * sum_k |x_k * w_k|. Never chosen by WQ_PATH_AUTO.
  * WQ_PATH_AUTO: MATVEC when n <= 16, else MFMA (`wq_gemm_path` tells which). */
 #define WQ_PATH_AUTO 0
 #define WQ_PATH_MATVEC 1
 #define WQ_PATH_MFMA 2
+#define WQ_PATH_MFMA_F32 3
 #define WQ_MATVEC_MAX_N 16
 
 /* ---- status codes ---------------------------------------------------------- */
@@ -97,7 +108,8 @@ extern "C" {
 int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
             float* y, int64_t n, int64_t m, int64_t k, void* stream);
 
-/* wq_gemm with the path forced (WQ_PATH_*). WQ_PATH_MATVEC requires n <= 16. */
+/* wq_gemm with the path forced (WQ_PATH_*). WQ_PATH_MATVEC requires n <= 16;
+ * WQ_PATH_MFMA_F32 (f32 accuracy on the matrix cores) is reached only here. */
 int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
                float* y, int64_t n, int64_t m, int64_t k, int path, void* stream);
 

@@ -42,6 +42,8 @@ def test_header_constants_match_binding():
     assert int(consts["WQ_BIAS"]) == wq.BIAS and int(consts["WQ_GELU"]) == wq.GELU
     assert int(consts["WQ_RESIDUAL"]) == wq.RESIDUAL
     assert int(consts["WQ_MATVEC_MAX_N"]) == wq.MATVEC_MAX_N
+    assert [int(consts[f"WQ_PATH_{p}"]) for p in ("AUTO", "MATVEC", "MFMA", "MFMA_F32")] == [
+        wq.PATH_AUTO, wq.PATH_MATVEC, wq.PATH_MFMA, wq.PATH_MFMA_F32]
     for name, code in consts.items():
         if name.startswith("WQ_ERR_") or name == "WQ_OK":
             assert wq.STATUS[int(code)] == name
@@ -92,6 +94,10 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
     (dict(m=-5), -2, "negative"),
     (dict(n=17, path=1), -2, "n <= 16"),
     (dict(path=7), -2, "path"),
+    (dict(path=-1), -2, "path"),
+    (dict(path=3, flags=8), -4, "flag"),
+    (dict(path=3, k=48), -2, "multiple of 32"),
+    (dict(path=3, y=X), -6, "overlaps"),
     (dict(x=None), -1, "NULL"),
     (dict(w=None), -1, "NULL"),
     (dict(y=None), -1, "NULL"),
