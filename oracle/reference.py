@@ -12,7 +12,9 @@ What it computes, written out from the pages it follows:
   ``GmP`` parameter block), with the epilogue of its ``ae_put``: add the bias
   (flag 1), then erf-GELU (flag 2), then add the value already in Y (flag 4).
   wavo ``gpu/mod.rs`` ``Epilogue`` (``Residual``/``GeluResidual``) describes
-  the same accumulate-into-output step.
+  the same accumulate-into-output step, and adds the other activations
+  (SiLU, ReLU, tanh: flags 8, 16, 32 here) and a factor alpha on the
+  accumulated value (``Residual(alpha)``).
 * Weights are decoded exactly before the product: bf16 is the upper half of
   an f32 (``ae_gemm``'s weight-pair unpacking); Q8_0 is ``d * q`` with an f16
   ``d`` and int8 ``q`` (wavo ``Gpu::upload_linear`` and the test helper
@@ -36,6 +38,7 @@ from scipy.special import erf
 
 W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
 FLAG_BIAS, FLAG_GELU, FLAG_RESIDUAL = 1, 2, 4
+FLAG_SILU, FLAG_RELU, FLAG_TANH = 8, 16, 32
 QBLOCK = 32
 QBYTES = {W_Q8_0: 34, W_Q4_0: 18}
 
@@ -155,13 +158,44 @@ def gelu_erf(v) -> np.ndarray:
     return 0.5 * v * (1.0 + erf(v / np.sqrt(2.0)))
 
 
-def epilogue(v: np.ndarray, flags: int, bias=None, y_old=None) -> np.ndarray:
-    """bias -> GELU -> +old output, in that order (``ae_put``)."""
+def silu(v) -> np.ndarray:
+    """SiLU: ``v / (1 + exp(-v))`` (wavo ``gpu/mod.rs`` test reference ``silu``, ``Epilogue::Silu``)."""
+    v = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return v / (1.0 + np.exp(-v))
+
+
+def relu(v) -> np.ndarray:
+    """ReLU: ``max(v, 0)`` (wavo ``Epilogue::Relu``)."""
+    return np.maximum(np.asarray(v, dtype=np.float64), 0.0)
+
+
+def tanh(v) -> np.ndarray:
+    """Hyperbolic tangent (wavo ``Epilogue::Tanh``), numpy's f64 ``tanh``."""
+    return np.tanh(np.asarray(v, dtype=np.float64))
+
+
+ACTIVATIONS = {FLAG_GELU: gelu_erf, FLAG_SILU: silu, FLAG_RELU: relu, FLAG_TANH: tanh}
+
+
+def epilogue(v: np.ndarray, flags: int, bias=None, y_old=None, alpha: float = 1.0) -> np.ndarray:
+    """bias -> activation -> times alpha -> + old output, in that order.
+
+    The order and flag bits 1/2/4 are ``ae_put``'s (cortiq-engine); the other
+    activations (flag 8 SiLU, 16 ReLU, 32 tanh; at most one activation) and the
+    factor ``alpha`` on the accumulated value are wavo's ``Epilogue`` modes
+    (``Residual(alpha)``: ``c + alpha * (a.W^T + b)``, ``GeluResidual``:
+    ``c + GELU(a.W^T + b)``). ``alpha = 1`` is the cortiq-engine epilogue.
+    """
     out = np.array(v, dtype=np.float64, copy=True)
     if flags & FLAG_BIAS:
         out = out + np.asarray(bias, dtype=np.float64)[None, :]
-    if flags & FLAG_GELU:
-        out = gelu_erf(out)
+    acts = [f for f in ACTIVATIONS if flags & f]
+    if len(acts) > 1:
+        raise ValueError("at most one activation flag")
+    if acts:
+        out = ACTIVATIONS[acts[0]](out)
+    out = float(alpha) * out
     if flags & FLAG_RESIDUAL:
         out = out + np.asarray(y_old, dtype=np.float64)
     return out
@@ -172,7 +206,7 @@ def epilogue(v: np.ndarray, flags: int, bias=None, y_old=None) -> np.ndarray:
 # ---------------------------------------------------------------------------
 
 def linear(x, w_raw, wtype: int, m: int, k: int, bias=None, flags: int = 0, y_old=None,
-           rows=None):
+           rows=None, alpha: float = 1.0):
     """``(Y_ref, S)`` for ``Y = epilogue(X . W^T + b)``; both ``f64[n][len(rows) or m]``.
 
     ``rows`` restricts the output columns (rows of W) to a subset, so that a
@@ -189,7 +223,7 @@ def linear(x, w_raw, wtype: int, m: int, k: int, bias=None, flags: int = 0, y_ol
         r = np.asarray(rows)
         b = None if b is None else b[r]
         yo = None if yo is None else yo[:, r]
-    return epilogue(v, flags, b, yo), s
+    return epilogue(v, flags, b, yo, alpha), s
 
 
 def moe(x, bank_raw, wtype: int, ids, n_exp: int, m: int, k: int, gates=None, rows=None):
