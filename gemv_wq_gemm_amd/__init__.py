@@ -16,7 +16,8 @@ import ctypes
 import os
 
 W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
-BIAS, GELU, RESIDUAL = 1, 2, 4
+BIAS, GELU, RESIDUAL, SILU, RELU, TANH = 1, 2, 4, 8, 16, 32
+ACTIVATIONS = {None: 0, "gelu": GELU, "silu": SILU, "relu": RELU, "tanh": TANH}
 PATH_AUTO, PATH_MATVEC, PATH_MFMA, PATH_MFMA_F32 = 0, 1, 2, 3
 MATVEC_MAX_N = 16
 
@@ -32,6 +33,7 @@ _P, _I64, _I, _U = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_uint
 SIGNATURES = [
     ("wq_gemm", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _P]),
     ("wq_gemm_ex", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _I, _P]),
+    ("wq_linear", _I, [_P, _P, _I, _P, _U, ctypes.c_float, _P, _I64, _I64, _I64, _I, _P]),
     ("wq_moe_matvec", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     ("wq_dequantize", _I, [_P, _I, _P, _I64, _I64, _P]),
     ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
@@ -123,12 +125,23 @@ def _weight(w, wtype, nbytes, name="w"):
     return _dev(w, name)
 
 
+def _flags(bias, gelu: bool, act, residual: bool) -> int:
+    if act not in ACTIVATIONS:
+        raise ValueError(f"act must be one of {sorted(a for a in ACTIVATIONS if a)} or None, got {act!r}")
+    if gelu and act not in (None, "gelu"):
+        raise ValueError("gelu=True and another act")
+    a = GELU if gelu else ACTIVATIONS[act]
+    return (BIAS if bias is not None else 0) | a | (RESIDUAL if residual else 0)
+
+
 def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, residual: bool = False,
-         out=None, path: int = PATH_AUTO):
-    """``out[n][m] = epilogue(x[n][k] . W^T + bias)`` via ``wq_gemm_ex``.
+         out=None, path: int = PATH_AUTO, act=None, alpha: float = 1.0):
+    """``out[n][m] = alpha * act(x[n][k] . W^T + bias) (+ out)`` via ``wq_linear``.
 
     ``w`` holds the weight in its storage format (any dtype; its bytes are
-    used). With ``residual=True``, ``out`` is required and accumulated into.
+    used). ``act`` is None, "gelu", "silu", "relu" or "tanh" (``gelu=True`` is
+    ``act="gelu"``). With ``residual=True``, ``out`` is required and
+    accumulated into.
     """
     import torch
     n = x.numel() // k if k else 0
@@ -138,20 +151,20 @@ def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, res
         if residual:
             raise ValueError("residual=True needs out= (the values to accumulate into)")
         out = torch.empty((n, m), dtype=torch.float32, device=x.device)
-    flags = (BIAS if bias is not None else 0) | (GELU if gelu else 0) | (RESIDUAL if residual else 0)
+    flags = _flags(bias, gelu, act, residual)
     nbytes = weight_bytes(wtype, m, k)
     if nbytes < 0:
         _check(lib().wq_gemm_path(n, m, k, wtype))
-    st = lib().wq_gemm_ex(
+    st = lib().wq_linear(
         _f32(x, "x"), _weight(w, wtype, nbytes), wtype,
-        None if bias is None else _f32(bias, "bias", m), flags,
+        None if bias is None else _f32(bias, "bias", m), flags, float(alpha),
         _f32(out, "out", n * m), n, m, k, path, _stream())
     _check(st)
     return out
 
 
 class BoundGemm:
-    """One ``wq_gemm_ex`` call with every argument resolved up front.
+    """One ``wq_linear`` call with every argument resolved up front.
 
     For loops that call the same layer on the same buffers again and again (a
     timing loop, a decode step): calling the object costs one ctypes call, with
@@ -168,18 +181,18 @@ class BoundGemm:
 
 
 def bind_gemm(x, w, wtype: int, *, m: int, k: int, out, bias=None, gelu: bool = False,
-              residual: bool = False, path: int = PATH_AUTO) -> BoundGemm:
+              residual: bool = False, path: int = PATH_AUTO, act=None, alpha: float = 1.0) -> BoundGemm:
     """Checks the arguments as :func:`gemm` does and returns a :class:`BoundGemm`."""
     n = x.numel() // k if k else 0
     if x.numel() != n * k:
         raise ValueError("x must hold n*k elements")
-    flags = (BIAS if bias is not None else 0) | (GELU if gelu else 0) | (RESIDUAL if residual else 0)
+    flags = _flags(bias, gelu, act, residual)
     nbytes = weight_bytes(wtype, m, k)
     if nbytes < 0:
         _check(lib().wq_gemm_path(n, m, k, wtype))
     args = (_f32(x, "x"), _weight(w, wtype, nbytes), wtype, None if bias is None else _f32(bias, "bias", m),
-            flags, _f32(out, "out", n * m), n, m, k, path, _stream())
-    return BoundGemm(lib().wq_gemm_ex, args)
+            flags, ctypes.c_float(alpha), _f32(out, "out", n * m), n, m, k, path, _stream())
+    return BoundGemm(lib().wq_linear, args)
 
 
 def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: int, k: int, out=None):

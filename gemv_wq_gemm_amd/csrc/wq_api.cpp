@@ -9,6 +9,7 @@
 // flag 1 exactly when a bias is given). Every check runs before any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -93,11 +94,15 @@ int workspace(hipStream_t stream, size_t bytes, void** out) {
   return WQ_OK;
 }
 
-int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y,
-                 int64_t n, int64_t m, int64_t k, int path, void* stream) {
+int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
+                 float* y, int64_t n, int64_t m, int64_t k, int path, void* stream) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
-  if (flags & ~(WQ_BIAS | WQ_GELU | WQ_RESIDUAL)) return fail(WQ_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+  constexpr unsigned kActs = WQ_GELU | WQ_SILU | WQ_RELU | WQ_TANH;
+  if (flags & ~(WQ_BIAS | WQ_RESIDUAL | kActs)) return fail(WQ_ERR_FLAGS, "unknown flag bits 0x%x", flags);
+  if (__builtin_popcount(flags & kActs) > 1)
+    return fail(WQ_ERR_FLAGS, "at most one activation flag (GELU, SILU, RELU, TANH), got 0x%x", flags);
+  if (!std::isfinite(alpha)) return fail(WQ_ERR_FLAGS, "alpha must be finite");
   if (((flags & WQ_BIAS) != 0) != (bias != nullptr))
     return fail(WQ_ERR_FLAGS, "WQ_BIAS must be set exactly when a bias pointer is given");
   if (path != WQ_PATH_AUTO && path != WQ_PATH_MATVEC && path != WQ_PATH_MFMA && path != WQ_PATH_MFMA_F32)
@@ -138,6 +143,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.k = static_cast<int>(k);
     p.rowbytes = rowbytes;
     p.flags = flags;
+    p.alpha = alpha;
     e = wq::launch_matvec(wtype, p, static_cast<int>(n), s);
   } else {
     wq::GemmParams p{};
@@ -150,6 +156,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.k = static_cast<int>(k);
     p.rowbytes = rowbytes;
     p.flags = flags;
+    p.alpha = alpha;
     p.x_parts = path == WQ_PATH_MFMA_F32 ? 3 : 1;
     e = wq::launch_gemm(wtype, p, s);
   }
@@ -181,12 +188,17 @@ int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype) {
 
 int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
             int64_t m, int64_t k, void* stream) {
-  return gemm_checked(x, w, wtype, bias, flags, y, n, m, k, WQ_PATH_AUTO, stream);
+  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, WQ_PATH_AUTO, stream);
 }
 
 int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
                int64_t m, int64_t k, int path, void* stream) {
-  return gemm_checked(x, w, wtype, bias, flags, y, n, m, k, path, stream);
+  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, path, stream);
+}
+
+int wq_linear(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha, float* y,
+              int64_t n, int64_t m, int64_t k, int path, void* stream) {
+  return gemm_checked(x, w, wtype, bias, flags, alpha, y, n, m, k, path, stream);
 }
 
 int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
@@ -234,6 +246,7 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
   p.k = static_cast<int>(k);
   p.rowbytes = ebytes / m;
   p.flags = 0;
+  p.alpha = 1.0f;
   // Twice the mean count of slots per expert picks the tokens-per-pass variant: an expert
   // holding more than that is rare, and is still served exactly by a further pass over its rows.
   const int64_t per_expert = 2 * ((n_slots + n_experts - 1) / n_experts);

@@ -129,4 +129,31 @@ __device__ __forceinline__ float gelu_erf(float v) {
   return 0.5f * v * (1.0f + erf_as(v * 0.70710678118654752f));
 }
 
+// Epilogue flag bits (include/wq.h): bias 1, erf-GELU 2 and accumulate into the old output 4 are
+// those of cortiq-engine `ae_put`; SiLU 8, ReLU 16 and tanh 32 are the other activations of wavo
+// src/gpu/mod.rs `Epilogue`. The host lets at most one activation through.
+constexpr unsigned kEpiBias = 1u, kEpiGelu = 2u, kEpiResidual = 4u, kEpiSilu = 8u, kEpiRelu = 16u, kEpiTanh = 32u;
+constexpr unsigned kEpiAct = kEpiGelu | kEpiSilu | kEpiRelu | kEpiTanh;
+
+// The activation `flags` selects (v itself when none): erf-GELU as above, SiLU v / (1 + e^-v)
+// (ROCm's expf; for v far below 0 the quotient is -0), ReLU max(v, 0), ROCm's tanhf.
+__device__ __forceinline__ float activation(float v, unsigned flags) {
+  if (flags & kEpiGelu) return gelu_erf(v);
+  if (flags & kEpiSilu) return v / (1.0f + expf(-v));
+  if (flags & kEpiRelu) return fmaxf(v, 0.0f);
+  if (flags & kEpiTanh) return tanhf(v);
+  return v;
+}
+
+// The whole epilogue of one output: (+ bias) -> activation -> times alpha -> (+ old output).
+// `bias` and `old` are read only when their flags are set.
+__device__ __forceinline__ float epilogue(float acc, unsigned flags, float alpha, const float* bias,
+                                          const float* old) {
+  float v = acc;
+  if (flags & kEpiBias) v += *bias;
+  v = alpha * activation(v, flags);
+  if (flags & kEpiResidual) v += *old;
+  return v;
+}
+
 }  // namespace wq

@@ -32,7 +32,7 @@
 //    the parts sit in three LDS buffers and each fragment takes three MFMAs into the same
 //    accumulator, so the products are exact and only the f32 sums round.
 //  * Split-K: when the output has too few tiles to fill the chip and the
-//    epilogue is linear in the product (no GELU, accumulate into Y), gridDim.z
+//    epilogue is linear in the product (no activation, accumulate into Y), gridDim.z
 //    workgroups share a tile's k range and add their partial sums into Y with
 //    f32 atomics; the first one adds the bias.
 #include <hip/hip_runtime.h>
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
   for (int j = 0; j < C::FN; ++j) {
     const int col = m0 + wn * C::TN + j * 32 + frow;
     if (col >= p.m) continue;
-    const float b = (p.flags & 1u) && first ? p.bias[col] : 0.f;
+    const float b = (p.flags & kEpiBias) && first ? p.bias[col] : 0.f;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
@@ -350,10 +350,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
           float* yp = p.y + static_cast<long long>(row) * p.m + col;
           float o = acc[i][j][v] + b;
           if (split) {
-            unsafeAtomicAdd(yp, o);  // Y already holds the old values (residual, no GELU)
+            unsafeAtomicAdd(yp, p.alpha * o);  // Y already holds the old values (residual, no activation)
           } else {
-            if (p.flags & 2u) o = gelu_erf(o);
-            if (p.flags & 4u) o += *yp;
+            o = p.alpha * activation(o, p.flags);
+            if (p.flags & kEpiResidual) o += *yp;
             *yp = o;
           }
         }
@@ -474,7 +474,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = min(m0 + wn * TN + j * 32 + frow, p.m - 1);
-    bias_v[j] = (p.flags & 1u) ? p.bias[col] : 0.f;
+    bias_v[j] = (p.flags & kEpiBias) ? p.bias[col] : 0.f;
   }
 
   // Prologue: steps 0..P-1 in flight.
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
   // The epilogue, with the flag tests taken once per workgroup and the bounds tests only on
   // tiles that reach past the edge of Y.
   const bool full = n0 + BM <= p.n && m0 + BN <= p.m;
-  auto store = [&](auto gelu, auto res) {
+  auto store = [&](auto act, auto res) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = m0 + wn * TN + j * 32 + frow;
@@ -565,7 +565,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
           if (full || row < p.n) {
             float* yp = p.y + static_cast<long long>(row) * p.m + col;
             float o = acc[i][j][v] + bias_v[j];
-            if constexpr (decltype(gelu)::value) o = gelu_erf(o);
+            if constexpr (decltype(act)::value != 0) o = activation(o, decltype(act)::value);
+            o *= p.alpha;
             if constexpr (decltype(res)::value) o += *yp;
             *yp = o;
           }
@@ -573,14 +574,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
       }
     }
   };
-  using T = std::true_type;
-  using F = std::false_type;
-  if (p.flags & 2u) {
-    if (p.flags & 4u) store(T{}, T{});
-    else store(T{}, F{});
-  } else {
-    if (p.flags & 4u) store(F{}, T{});
-    else store(F{}, F{});
+  auto with_residual = [&](auto act) {
+    if (p.flags & kEpiResidual) store(act, std::true_type{});
+    else store(act, std::false_type{});
+  };
+  switch (p.flags & kEpiAct) {
+    case kEpiGelu: with_residual(std::integral_constant<unsigned, kEpiGelu>{}); break;
+    case kEpiSilu: with_residual(std::integral_constant<unsigned, kEpiSilu>{}); break;
+    case kEpiRelu: with_residual(std::integral_constant<unsigned, kEpiRelu>{}); break;
+    case kEpiTanh: with_residual(std::integral_constant<unsigned, kEpiTanh>{}); break;
+    default: with_residual(std::integral_constant<unsigned, 0u>{}); break;
   }
 }
 
@@ -610,9 +613,9 @@ hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
   const int tiles = tiles_m * tiles_n;
   int splits = 1;
   // Split the k range when the tiles alone leave most CUs idle and the
-  // epilogue allows adding partial sums into Y (accumulate, no GELU).
+  // epilogue allows adding partial sums into Y (accumulate, no activation).
   const int nk = (p.k + BK - 1) / BK;
-  if ((p.flags & 4u) && !(p.flags & 2u)) {
+  if ((p.flags & kEpiResidual) && !(p.flags & kEpiAct)) {
     const int cus = device_cus();
     while (tiles * splits * 2 <= cus * 3 / 2 && nk / (splits * 2) >= 4) splits *= 2;
   }

@@ -26,6 +26,7 @@ struct MatvecParams {
   int m, k;
   long long rowbytes;       // bytes of one weight row
   unsigned flags;           // epilogue flags (plain layer only)
+  float alpha;              // factor on the activated value (plain layer only)
 };
 
 // Picks the kernel variant (tokens per pass, rows per wave) and launches it.
@@ -62,6 +63,7 @@ struct GemmParams {
   int n, m, k;
   long long rowbytes;
   unsigned flags;
+  float alpha;        // factor on the activated value, before the old output is added
   int x_parts;        // 3: X enters as three exact bf16 parts (three MFMAs per product); 1: as bf16(X)
 };
 

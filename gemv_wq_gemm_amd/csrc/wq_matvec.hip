@@ -249,9 +249,7 @@ __global__ __launch_bounds__(kThreads) void matvec_general_kernel(MatvecParams p
             float* yp = p.y + static_cast<long long>(slot[t]) * p.m + row;
             float o = v;
             if (!moe) {
-              if (p.flags & 1u) o += p.bias[row];
-              if (p.flags & 2u) o = gelu_erf(o);
-              if (p.flags & 4u) o += *yp;
+              o = epilogue(o, p.flags, p.alpha, p.bias + row, yp);
             }
             *yp = o;
           }

@@ -4,7 +4,7 @@
 // Contract: per routed slot s and output row j, y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k]
 // (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), the same as the f32 matvec kernels. Without
 // ids (the plain layer) every slot takes the one weight and the store applies the epilogue
-// (bias, erf-GELU, + old Y).
+// (bias, activation, alpha, + old Y).
 //
 // Why matrix cores: with f32 FMAs every weight costs one instruction per routed slot, so an
 // expert's several slots make the kernel bound by the vector ALU, not by HBM. Here each weight
@@ -217,11 +217,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void matvec_mfma_kernel(MatvecParam
 #pragma unroll 1
         for (int w = 0; w < nw; ++w) v += part[buf][w * kPartWave + i];
         float* yp = p.y + static_cast<long long>(slot) * p.m + row;
-        if (!moe) {
-          if (p.flags & 1u) v += p.bias[row];
-          if (p.flags & 2u) v = gelu_erf(v);
-          if (p.flags & 4u) v += *yp;
-        }
+        if (!moe) v = epilogue(v, p.flags, p.alpha, p.bias + row, yp);
         *yp = v;
       }
     }

@@ -353,11 +353,7 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
             for (int w = 0; w < MAXW; ++w)
               if (w < nw) v += part[i * MAXW + w];
             float* yp = p.y + static_cast<long long>(st_slot) * p.m + row;
-            if (!moe) {
-              if (p.flags & 1u) v += p.bias[row];
-              if (p.flags & 2u) v = gelu_erf(v);
-              if (p.flags & 4u) v += *yp;
-            }
+            if (!moe) v = epilogue(v, p.flags, p.alpha, p.bias + row, yp);
             *yp = v;
           }
         }
@@ -406,7 +402,7 @@ hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   int tpw = (ntiles + groups - 1) / groups;
   // An epilogue that reads memory (bias, residual) makes the compiler wait for every load in
   // flight, so such launches give each workgroup no more rows than one flush holds.
-  if (p.ids == nullptr && (p.flags & 5u) != 0 && tpw * R > kFlushRows) tpw = kFlushRows / R;
+  if (p.ids == nullptr && (p.flags & (kEpiBias | kEpiResidual)) != 0 && tpw * R > kFlushRows) tpw = kFlushRows / R;
   dim3 grid((ntiles + tpw - 1) / tpw, n_exp_rows);
   hipLaunchKernelGGL(kernel, grid, dim3(64 * nw), 0, stream, p, tpw);
   return hipGetLastError();

@@ -54,13 +54,25 @@ extern "C" {
 #define WQ_W_Q8_0 1
 #define WQ_W_Q4_0 2
 
-/* ---- epilogue flags (the bit values of `GmP.flags` / `ae_put`) ------------
- * Applied to each output in this order: + bias[j] (WQ_BIAS), then erf-GELU
- * 0.5*v*(1+erf(v/sqrt 2)) (WQ_GELU), then + the value Y held before the call
- * (WQ_RESIDUAL; Y is read and written in place). */
+/* ---- epilogue flags ---------------------------------------------------------
+ * Applied to each output in this order: + bias[j] (WQ_BIAS); then at most one
+ * activation; then times alpha (wq_linear; 1 for every other entry point);
+ * then + the value Y held before the call (WQ_RESIDUAL; Y is read and written
+ * in place). Bits 1, 2, 4 and that order are those of `GmP.flags` / `ae_put`
+ * (cortiq-engine). The activations and alpha are the modes of wavo's
+ * `Epilogue` (src/gpu/mod.rs: Silu, Relu, Tanh, Gelu, GeluResidual,
+ * Residual(alpha) = c + alpha * (a.W^T + b)):
+ *   WQ_GELU  erf-GELU 0.5*v*(1+erf(v/sqrt 2));
+ *   WQ_SILU  v / (1 + exp(-v));
+ *   WQ_RELU  max(v, 0);
+ *   WQ_TANH  tanh(v).
+ * Two activation bits together are refused (WQ_ERR_FLAGS). */
 #define WQ_BIAS 1u
 #define WQ_GELU 2u
 #define WQ_RESIDUAL 4u
+#define WQ_SILU 8u
+#define WQ_RELU 16u
+#define WQ_TANH 32u
 
 /* ---- contraction paths ----------------------------------------------------
  * WQ_PATH_MATVEC: all-f32 FMA path for n <= 16 (weights streamed once for all
@@ -91,7 +103,8 @@ extern "C" {
 #define WQ_ERR_NULL (-1)   /* a required pointer is NULL */
 #define WQ_ERR_SHAPE (-2)  /* negative size, k % 32 != 0, n too large for the path, ... */
 #define WQ_ERR_WTYPE (-3)  /* unknown weight type */
-#define WQ_ERR_FLAGS (-4)  /* unknown flag bits, or WQ_BIAS set without a bias (or a bias without WQ_BIAS) */
+#define WQ_ERR_FLAGS (-4)  /* unknown flag bits, two activations, WQ_BIAS without a bias (or a bias
+                              without WQ_BIAS), or a non-finite alpha */
 #define WQ_ERR_ALIGN (-5)  /* x, w or y not 16-byte aligned; bias, ids or gates not 4-byte aligned */
 #define WQ_ERR_ALIAS (-6)  /* y overlaps x, w, bias, ids or gates */
 #define WQ_ERR_HIP (-7)    /* a HIP call failed (launch, allocation, device query) */
@@ -112,6 +125,16 @@ int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigne
  * WQ_PATH_MFMA_F32 (f32 accuracy on the matrix cores) is reached only here. */
 int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
                float* y, int64_t n, int64_t m, int64_t k, int path, void* stream);
+
+/*
+ * wq_linear: wq_gemm_ex with a factor on the activated value:
+ *   Y = alpha * act(X . W^T + bias) (+ Y_old when flags & WQ_RESIDUAL),
+ * wavo's `Epilogue::Residual(alpha)` (with WQ_BIAS | WQ_RESIDUAL) and its
+ * activations at any scale. alpha must be finite (WQ_ERR_FLAGS otherwise);
+ * alpha = 1 is exactly wq_gemm_ex. Every other argument as for wq_gemm_ex.
+ */
+int wq_linear(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
+              float* y, int64_t n, int64_t m, int64_t k, int path, void* stream);
 
 /*
  * wq_moe_matvec: the MoE matvec of hanzo-ml `moe_matvec_gpu`, expert-major.

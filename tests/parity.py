@@ -4,10 +4,12 @@ buffers, and the acceptance bound.
 Acceptance (elementwise), with S = sum_k |x_k * w_k| from the oracle:
     |y - y_ref| <= g * B * S + 8 * 2^-24 * (|y_ref| + |v| + |bias| + |y_old|)
 B = 2^-8 on the MFMA path (X rounded to bf16), 1e-5 on the all-f32 paths;
-g = 1.13 >= max |GELU'| when GELU is applied (an error before the activation
-is stretched by at most that factor), else 1; v is the pre-activation value.
-The last term covers the f32 roundings of the epilogue itself (bias add, the
-GELU evaluation, the residual add), which the sum S does not scale.
+g is the largest slope of the activation (an error before it is stretched by
+at most that factor): 1.13 for GELU, 1.1 for SiLU, 1 for ReLU, tanh or none;
+v is the pre-activation value. With a factor alpha on the activated value
+(wq_linear), the first term and v, bias scale by |alpha|. The last term
+covers the f32 roundings of the epilogue itself (bias add, the activation's
+evaluation, the alpha product, the residual add), which S does not scale.
 """
 from __future__ import annotations
 
@@ -19,6 +21,7 @@ CANARY = 12345.0
 B_MFMA = 2.0 ** -8
 B_F32 = 1e-5
 GELU_SLOPE = 1.13
+SLOPES = {2: GELU_SLOPE, 8: 1.1, 16: 1.0, 32: 1.0}  # max |act'| of GELU, SiLU, ReLU, tanh
 ULP_SLACK = 8 * 2.0 ** -24
 
 
@@ -45,16 +48,17 @@ def read_guarded(buf, rows: int, cols: int) -> np.ndarray:
     return host[: rows * cols].reshape(rows, cols)
 
 
-def tolerance(S, y_ref, bound, flags=0, v=None, bias=None, y_old=None):
-    g = GELU_SLOPE if flags & oracle.FLAG_GELU else 1.0
+def tolerance(S, y_ref, bound, flags=0, v=None, bias=None, y_old=None, alpha=1.0):
+    g = max([SLOPES[a] for a in SLOPES if flags & a], default=1.0)
+    a = abs(float(alpha))
     mag = np.abs(y_ref)
     if v is not None:
-        mag = mag + np.abs(v)
+        mag = mag + a * np.abs(v)
     if bias is not None and flags & oracle.FLAG_BIAS:
-        mag = mag + np.abs(np.asarray(bias, np.float64))[None, :]
+        mag = mag + a * np.abs(np.asarray(bias, np.float64))[None, :]
     if y_old is not None and flags & oracle.FLAG_RESIDUAL:
         mag = mag + np.abs(np.asarray(y_old, np.float64))
-    return g * bound * S + ULP_SLACK * mag
+    return a * g * bound * S + ULP_SLACK * mag
 
 
 def assert_within(got, y_ref, tol, what=""):
@@ -71,15 +75,18 @@ def assert_within(got, y_ref, tol, what=""):
     return float((err / np.maximum(tol, 1e-300)).max())
 
 
-def oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, bound, rows=None):
+ACT_FLAGS = 2 | 8 | 16 | 32
+
+
+def oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, bound, rows=None, alpha=1.0):
     """(y_ref, tol) from the oracle for one layer call."""
-    y_ref, S = oracle.linear(x, w, wtype, m, k, bias, flags, y_old, rows=rows)
+    y_ref, S = oracle.linear(x, w, wtype, m, k, bias, flags, y_old, rows=rows, alpha=alpha)
     v = None
-    if flags & oracle.FLAG_GELU:
+    if flags & ACT_FLAGS:
         v, _ = oracle.linear(x, w, wtype, m, k, bias, flags & oracle.FLAG_BIAS, rows=rows)
     b = None if bias is None else (np.asarray(bias)[rows] if rows is not None else bias)
     yo = None
     if y_old is not None:
         yo = np.asarray(y_old, np.float64).reshape(-1, m)
         yo = yo[:, rows] if rows is not None else yo
-    return y_ref, tolerance(S, y_ref, bound, flags, v, b, yo)
+    return y_ref, tolerance(S, y_ref, bound, flags, v, b, yo, alpha)

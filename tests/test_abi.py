@@ -41,6 +41,7 @@ def test_header_constants_match_binding():
     assert int(consts["WQ_W_Q4_0"]) == wq.W_Q4_0
     assert int(consts["WQ_BIAS"]) == wq.BIAS and int(consts["WQ_GELU"]) == wq.GELU
     assert int(consts["WQ_RESIDUAL"]) == wq.RESIDUAL
+    assert [int(consts[f"WQ_{a}"]) for a in ("SILU", "RELU", "TANH")] == [wq.SILU, wq.RELU, wq.TANH]
     assert int(consts["WQ_MATVEC_MAX_N"]) == wq.MATVEC_MAX_N
     assert [int(consts[f"WQ_PATH_{p}"]) for p in ("AUTO", "MATVEC", "MFMA", "MFMA_F32")] == [
         wq.PATH_AUTO, wq.PATH_MATVEC, wq.PATH_MFMA, wq.PATH_MFMA_F32]
@@ -85,7 +86,9 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
 
 @pytest.mark.parametrize("kwargs,code,msg", [
     (dict(wtype=3), -3, "weight type"),
-    (dict(flags=8), -4, "flag"),
+    (dict(flags=64), -4, "flag"),
+    (dict(flags=2 | 8), -4, "at most one activation"),
+    (dict(flags=16 | 32 | 4), -4, "at most one activation"),
     (dict(flags=1), -4, "WQ_BIAS"),
     (dict(bias=B), -4, "WQ_BIAS"),
     (dict(k=40), -2, "multiple of 32"),
@@ -95,7 +98,7 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
     (dict(n=17, path=1), -2, "n <= 16"),
     (dict(path=7), -2, "path"),
     (dict(path=-1), -2, "path"),
-    (dict(path=3, flags=8), -4, "flag"),
+    (dict(path=3, flags=128), -4, "flag"),
     (dict(path=3, k=48), -2, "multiple of 32"),
     (dict(path=3, y=X), -6, "overlaps"),
     (dict(x=None), -1, "NULL"),
@@ -113,6 +116,30 @@ def test_gemm_argument_errors(kwargs, code, msg):
     st, err = _gemm(**kwargs)
     assert st == code, err
     assert msg in err
+
+
+@pytest.mark.parametrize("alpha", [float("nan"), float("inf"), float("-inf")])
+def test_linear_refuses_non_finite_alpha(alpha):
+    lib = wq.lib()
+    st = lib.wq_linear(X, W, 0, None, 4, ctypes.c_float(alpha), Y, 4, 8, 32, 0, None)
+    assert st == -4 and "alpha" in lib.wq_last_error().decode()
+
+
+def test_linear_checks_like_gemm_ex():
+    lib = wq.lib()
+    assert lib.wq_linear(X, W, 3, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -3
+    assert lib.wq_linear(X, W, 0, None, 2 | 16, ctypes.c_float(0.5), Y, 4, 8, 32, 2, None) == -4
+    assert lib.wq_linear(X, W, 0, None, 0, ctypes.c_float(0.5), Y, 4, 8, 40, 0, None) == -2
+    assert lib.wq_linear(None, None, 0, None, 0, ctypes.c_float(2.0), None, 0, 8, 32, 0, None) == 0
+
+
+def test_binding_refuses_unknown_or_double_activation():
+    import torch
+    x = torch.zeros(2, 32)
+    with pytest.raises(ValueError):
+        wq.gemm(x, x, wq.W_BF16, m=2, k=32, act="swish")
+    with pytest.raises(ValueError):
+        wq.gemm(x, x, wq.W_BF16, m=2, k=32, gelu=True, act="tanh")
 
 
 def test_empty_shapes_are_noops_even_with_null_pointers():
