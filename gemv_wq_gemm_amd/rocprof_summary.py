@@ -1,6 +1,6 @@
 """Short text summaries of rocprofv3 output, and the reader of the HBM byte counts they record.
 
-    python -m gemv_wq_gemm_amd.rocprof_summary trace STATS_CSV OUT_MD --command CMD
+    python -m gemv_wq_gemm_amd.rocprof_summary trace STATS_CSV OUT_MD --command CMD [--top N]
     python -m gemv_wq_gemm_amd.rocprof_summary counters FETCH_CSV WRITE_CSV OUT_MD --command CMD \\
         --kernel LABEL=SUBSTRING [...] --copy SUBSTRING --copy-bytes N
 
@@ -141,6 +141,7 @@ def main() -> None:
     t.add_argument("stats_csv")
     t.add_argument("out")
     t.add_argument("--command", required=True)
+    t.add_argument("--top", type=int, default=16, help="kernels listed, by total time")
     c = sub.add_parser("counters")
     c.add_argument("fetch_csv")
     c.add_argument("write_csv")
@@ -151,7 +152,7 @@ def main() -> None:
     c.add_argument("--copy-bytes", type=int, required=True)
     a = ap.parse_args()
     if a.what == "trace":
-        print(trace_summary(a.stats_csv, a.command, a.out))
+        print(trace_summary(a.stats_csv, a.command, a.out, a.top))
     else:
         kernels = dict(kv.split("=", 1) for kv in a.kernel)
         print(counter_summary(a.fetch_csv, a.write_csv, a.command, a.out, kernels, a.copy, a.copy_bytes))
