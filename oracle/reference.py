@@ -16,7 +16,8 @@ What it computes, written out from the pages it follows:
   (SiLU, ReLU, tanh: flags 8, 16, 32 here) and a factor alpha on the
   accumulated value (``Residual(alpha)``).
 * Weights are decoded exactly before the product: bf16 is the upper half of
-  an f32 (``ae_gemm``'s weight-pair unpacking); Q8_0 is ``d * q`` with an f16
+  an f32 (``ae_gemm``'s weight-pair unpacking); f32 and f16 are IEEE values
+  (wavo's ``Linear`` types 0 and 1); Q8_0 is ``d * q`` with an f16
   ``d`` and int8 ``q`` (wavo ``Gpu::upload_linear`` and the test helper
   ``weights``); Q4_0 is ``d * (q - 8)`` with 4-bit ``q`` (format named by
   hanzo-ml ``wgpu_backend.rs`` ``matvec_q4_0_gpu``; nibble order: low nibbles
@@ -36,7 +37,7 @@ from __future__ import annotations
 import numpy as np
 from scipy.special import erf
 
-W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
+W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16 = 0, 1, 2, 3, 4
 FLAG_BIAS, FLAG_GELU, FLAG_RESIDUAL = 1, 2, 4
 FLAG_SILU, FLAG_RELU, FLAG_TANH = 8, 16, 32
 QBLOCK = 32
@@ -81,13 +82,34 @@ def bf16_bits_to_f64(bits) -> np.ndarray:
     return np.where(e == 0, sub, np.where(e == 255, special, normal))
 
 
+def f32_bits_to_f64(bits) -> np.ndarray:
+    """Value of IEEE-754 binary32 bit patterns: 1 sign, 8 exponent (bias 127), 23 fraction bits.
+
+    Normals are ``(-1)^s * 2^(e-127) * (1 + f/2^23)``, subnormals (e = 0)
+    ``(-1)^s * 2^-126 * f/2^23``, e = 255 is infinity (f = 0) or NaN. (wavo's
+    ``Linear`` F32 weights, type 0 of ``Gpu::upload_linear``, are these values.)
+    """
+    b = np.asarray(bits).astype(np.int64) & 0xFFFFFFFF
+    s = np.where(b >> 31, -1.0, 1.0)
+    e = (b >> 23) & 0xFF
+    f = (b & 0x7FFFFF).astype(np.float64)
+    normal = s * np.ldexp(1.0 + f / 2.0 ** 23, (e - 127).astype(np.int64))
+    sub = s * np.ldexp(f / 2.0 ** 23, -126)
+    special = np.where(f == 0, s * np.inf, np.nan)
+    return np.where(e == 0, sub, np.where(e == 255, special, normal))
+
+
 # ---------------------------------------------------------------------------
 # Weight decode
 # ---------------------------------------------------------------------------
 
+# Bytes per weight of the plain (unblocked) types: bf16, wavo's F32 (type 0) and F16 (type 1).
+PLAIN_BYTES = {W_BF16: 2, W_F32: 4, W_F16: 2}
+
+
 def weight_nbytes(wtype: int, m: int, k: int) -> int:
-    if wtype == W_BF16:
-        return 2 * m * k
+    if wtype in PLAIN_BYTES:
+        return PLAIN_BYTES[wtype] * m * k
     return QBYTES[wtype] * m * (k // QBLOCK)
 
 
@@ -130,12 +152,20 @@ def decode_bf16(raw: np.ndarray, m: int, k: int) -> np.ndarray:
 
 
 def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray:
-    """Exact f64 values of an ``m x k`` weight (optionally only the listed rows)."""
-    if wtype == W_BF16:
-        a = np.ascontiguousarray(raw).view(np.uint16).reshape(m, k)
+    """Exact f64 values of an ``m x k`` weight (optionally only the listed rows).
+
+    bf16 and f16 rows are 16-bit patterns, f32 rows 32-bit patterns, all
+    little-endian (wavo ``Gpu::upload_linear`` copies F32 / F16 tensor bytes as
+    stored); Q8_0 / Q4_0 rows are 34- / 18-byte blocks.
+    """
+    if wtype in PLAIN_BYTES:
+        dt = np.uint32 if wtype == W_F32 else np.uint16
+        a = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)[: PLAIN_BYTES[wtype] * m * k].view(dt)
+        a = a.reshape(m, k)
         if rows is not None:
             a = a[np.asarray(rows)]
-        return bf16_bits_to_f64(a)
+        fn = {W_BF16: bf16_bits_to_f64, W_F32: f32_bits_to_f64, W_F16: f16_bits_to_f64}[wtype]
+        return fn(a)
     per_row = QBYTES.get(wtype)
     if per_row is None:
         raise ValueError(f"unknown weight type {wtype}")

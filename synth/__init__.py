@@ -14,6 +14,9 @@ follows, and restated here only to lay the bytes out):
   f16 scale followed by 32 signed bytes (wavo ``gpu/mod.rs``,
   ``Gpu::upload_linear`` and the test helper ``weights``; hanzo-ml
   ``wgpu_backend.rs``, ``matvec_q8_0_gpu``).
+* f32 / f16 weights: ``float32[m][k]`` / IEEE ``float16[m][k]`` bit patterns
+  (wavo ``gpu/mod.rs`` ``Linear``: GEMM types 0 and 1, copied as stored by
+  ``Gpu::upload_linear``).
 * Q4_0 weights: ``m`` rows of ``k/32`` blocks of 18 bytes -- a little-endian
   f16 scale followed by 16 bytes whose low nibbles are elements 0-15 and high
   nibbles elements 16-31 (hanzo-ml ``wgpu_backend.rs`` names the format in
@@ -26,7 +29,7 @@ from __future__ import annotations
 
 import numpy as np
 
-W_BF16, W_Q8_0, W_Q4_0 = 0, 1, 2
+W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16 = 0, 1, 2, 3, 4
 BLOCK = 32
 BLOCK_BYTES = {W_Q8_0: 34, W_Q4_0: 18}
 
@@ -100,13 +103,24 @@ def weight(g: np.random.Generator, wtype: int, m: int, k: int, sigma: float = 0.
         return q8_0_weight(g, m, k, dsigma)
     if wtype == W_Q4_0:
         return q4_0_weight(g, m, k, dsigma)
+    if wtype == W_F32:
+        return normal_f32(g, (m, k), sigma)
+    if wtype == W_F16:
+        return f16_weight(g, m, k, sigma)
     raise ValueError(f"unknown weight type {wtype}")
+
+
+def f16_weight(g: np.random.Generator, m: int, k: int, sigma: float) -> np.ndarray:
+    """``uint16[m][k]`` f16 bits of N(0, sigma^2) samples (numpy's round-to-nearest f16)."""
+    return normal_f32(g, (m, k), sigma).astype(np.float16).view(np.uint16)
 
 
 def weight_nbytes(wtype: int, m: int, k: int) -> int:
     """Bytes of one ``m x k`` weight in its storage format."""
-    if wtype == W_BF16:
+    if wtype in (W_BF16, W_F16):
         return 2 * m * k
+    if wtype == W_F32:
+        return 4 * m * k
     return BLOCK_BYTES[wtype] * m * (k // BLOCK)
 
 

@@ -44,6 +44,30 @@ def test_bf16_decode_all_bit_patterns_match_f32_upper_half():
     assert same.all()
 
 
+def test_f32_decode_matches_numpy_on_edge_and_random_patterns():
+    g = np.random.default_rng(15)
+    edge = np.array([0, 0x80000000, 1, 0x007FFFFF, 0x00800000, 0x3F800000, 0xBF800000, 0x7F7FFFFF,
+                     0x7F800000, 0xFF800000, 0x7FC00000, 0x34000000], np.uint32)
+    bits = np.concatenate([edge, g.integers(0, 1 << 32, 200000, dtype=np.uint64).astype(np.uint32)])
+    got = oracle.f32_bits_to_f64(bits)
+    want = bits.view(np.float32).astype(np.float64)
+    same = (got == want) | (np.isnan(got) & np.isnan(want))
+    assert same.all()
+    assert np.signbit(got[1]) and not np.signbit(got[0])
+    assert got[2] == 2.0 ** -149 and got[5] == 1.0
+
+
+def test_plain_f32_and_f16_weights_decode_to_their_values():
+    g = np.random.default_rng(16)
+    w32 = g.standard_normal((5, 64)).astype(np.float32)
+    assert np.array_equal(oracle.decode(w32, oracle.W_F32, 5, 64), w32.astype(np.float64))
+    w16 = g.standard_normal((5, 64)).astype(np.float16)
+    assert np.array_equal(oracle.decode(w16.view(np.uint16), oracle.W_F16, 5, 64), w16.astype(np.float64))
+    assert np.array_equal(oracle.decode(w32, oracle.W_F32, 5, 64, rows=[4, 1]), w32[[4, 1]].astype(np.float64))
+    assert oracle.weight_nbytes(oracle.W_F32, 5, 64) == 4 * 5 * 64
+    assert oracle.weight_nbytes(oracle.W_F16, 5, 64) == 2 * 5 * 64
+
+
 def test_f16_subnormals_are_exact():
     # every subnormal f16 is f * 2^-24 for f in 1..1023
     f = np.arange(1, 1024)

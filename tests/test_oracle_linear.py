@@ -36,6 +36,13 @@ def _brute_weight(raw, wtype, m, k):
                 v = int(bits[j, x])
                 w[j][x] = struct.unpack("<f", bytes([0, 0, v & 0xFF, v >> 8]))[0]
         return w
+    if wtype in (oracle.W_F32, oracle.W_F16):
+        by = np.asarray(raw).view(np.uint8).reshape(m, -1)
+        size, fmt = (4, "<f") if wtype == oracle.W_F32 else (2, "<e")
+        for j in range(m):
+            for x in range(k):
+                w[j][x] = struct.unpack(fmt, bytes(int(b) for b in by[j, size * x:size * x + size]))[0]
+        return w
     bpb = 34 if wtype == oracle.W_Q8_0 else 18
     raw = np.asarray(raw).view(np.uint8).reshape(m, -1)
     for j in range(m):
@@ -71,7 +78,7 @@ def _brute(x, raw, wtype, m, k, bias, flags, y_old):
     return y, s
 
 
-@pytest.mark.parametrize("wtype", [oracle.W_BF16, oracle.W_Q8_0, oracle.W_Q4_0])
+@pytest.mark.parametrize("wtype", [oracle.W_BF16, oracle.W_Q8_0, oracle.W_Q4_0, oracle.W_F32, oracle.W_F16])
 @pytest.mark.parametrize("shape", [(1, 1, 32), (2, 3, 64), (3, 2, 32)])
 @pytest.mark.parametrize("flags", FLAGS)
 def test_linear_matches_brute_force(wtype, shape, flags):
