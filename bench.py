@@ -25,9 +25,10 @@ The same JSON line carries:
   cpu_baseline  the f64 oracle (decode + product, numpy/OpenBLAS) on a
                 bounded sample of the same workload, on the host's cores;
   others        the remaining workloads (bf16 GEMM 64x256x256, Q4_0 matvec
-                14336x4096, MoE 16 tokens top-2 of 8, the 24-layer encoder
-                chain, also on the f32-accurate matrix-core path) with their own
-                TFLOP/s or GB/s and roofline fractions.
+                14336x4096, f16 matvec 4096x4096, MoE 16 tokens top-2 of 8, the
+                24-layer encoder chain, also on the f32-accurate matrix-core
+                path, and the MLP-up GEMM with f16 / f32 / Q8_0 / Q4_0 weights)
+                with their own TFLOP/s or GB/s and roofline fractions.
 """
 from __future__ import annotations
 
@@ -215,6 +216,21 @@ def _others(torch, wq, synth, dev, stream, to_dev):
                                         "copies": nc}
     del Wc
 
+    # f16 weights 4096 x 4096 at n = 1 (wavo Linear type 1), rotated copies
+    m16 = 4096
+    wb16 = wq.weight_bytes(wq.W_F16, m16, k)
+    nc16 = max(2, -(-ROTATE_BYTES // wb16))
+    base = to_dev(synth.weight(synth.rng(53), wq.W_F16, m16, k).reshape(-1).view(np.uint8))
+    Wc = torch.stack([torch.roll(base.view(m16, -1), shifts=7 * i, dims=0).reshape(-1) for i in range(nc16)])
+    x = to_dev(synth.normal_f32(synth.rng(54), (1, k), 1.0))
+    y = torch.empty((1, m16), device=dev)
+    gs = [wq.bind_gemm(x, Wc[i], wq.W_F16, m=m16, k=k, out=y) for i in range(nc16)]
+    med = _time_calls(torch, stream, lambda i: gs[i % nc16](), 100)
+    out["matvec_f16_4096x4096_n1"] = {"us": round(med * 1e3, 3), "GB/s": round(wb16 / (med * 1e-3) / 1e9, 1),
+                                      "frac_hbm": round(wb16 / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                                      "copies": nc16}
+    del Wc
+
     # MoE: 16 tokens, top-2 of 8 Q4_0 experts, gated; 3 banks rotated
     banks = []
     for bank in range(3):
@@ -270,6 +286,17 @@ def _others(torch, wq, synth, dev, stream, to_dev):
         out[name] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
                      "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
     del layers
+
+    # f16 / f32 weights (two / three exact bf16 parts on the matrix cores) at the same shape.
+    for wt, name in ((wq.W_F16, "f16"), (wq.W_F32, "f32")):
+        ws = [to_dev(synth.weight(synth.rng(50 + i, wt), wt, ff, d).reshape(-1)) for i in range(2)]
+        bq = to_dev(synth.normal_f32(synth.rng(52, wt), (ff,), 0.1))
+        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f) for w_ in ws]
+        med = _time_calls(torch, stream, lambda i: gq[i % 2](), 20)
+        fl = 2 * n * ff * d
+        out[f"gemm_{name}_{n}x{ff}x{d}_gelu"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
+                                                 "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        del ws, gq
 
     # Quantized weights on the matrix cores: the encoder's MLP-up shape (X[1500 x 1024], W[4096 x 1024]
     # as Q8_0 / Q4_0 blocks, bias + GELU), 4 weight copies rotated.

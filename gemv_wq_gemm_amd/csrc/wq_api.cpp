@@ -50,8 +50,8 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 }
 
 int check_wtype(int wtype) {
-  if (wtype != WQ_W_BF16 && wtype != WQ_W_Q8_0 && wtype != WQ_W_Q4_0)
-    return fail(WQ_ERR_WTYPE, "unknown weight type %d (0 = bf16, 1 = Q8_0, 2 = Q4_0)", wtype);
+  if (wtype != WQ_W_BF16 && wtype != WQ_W_Q8_0 && wtype != WQ_W_Q4_0 && wtype != WQ_W_F32 && wtype != WQ_W_F16)
+    return fail(WQ_ERR_WTYPE, "unknown weight type %d (0 = bf16, 1 = Q8_0, 2 = Q4_0, 3 = f32, 4 = f16)", wtype);
   return WQ_OK;
 }
 
@@ -174,6 +174,8 @@ int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k) {
     case WQ_W_BF16: return 2 * m * k;
     case WQ_W_Q8_0: return 34 * m * (k / 32);
     case WQ_W_Q4_0: return 18 * m * (k / 32);
+    case WQ_W_F32: return 4 * m * k;
+    case WQ_W_F16: return 2 * m * k;
     default: return -1;
   }
 }

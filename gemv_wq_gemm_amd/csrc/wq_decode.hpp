@@ -2,6 +2,8 @@
 //
 // bf16  : a 16-bit pattern that is the upper half of an f32 (the weight-pair
 //         unpack of `ae_gemm`, cortiq-engine src/gpu_wgpu/nemotron_audio.rs).
+// f32, f16: IEEE values as stored (wavo src/gpu/mod.rs `Linear` GEMM types 0
+//         and 1, copied as they are by `Gpu::upload_linear`).
 // Q8_0  : 34-byte block = little-endian f16 scale d, then 32 int8 q; w = d*q
 //         (wavo src/gpu/mod.rs `Gpu::upload_linear`; hanzo-ml src/wgpu_backend.rs
 //         `matvec_q8_0_gpu`).
@@ -63,6 +65,14 @@ template <>
 struct BlockWords<2> {
   static constexpr int NW = 4;
 };
+template <>
+struct BlockWords<3> {
+  static constexpr int NW = 32;
+};
+template <>
+struct BlockWords<4> {
+  static constexpr int NW = 16;
+};
 
 // Reads the block that starts `off` bytes after the 4-byte aligned `base`
 // (off even), through the aligned dwords that cover exactly
@@ -72,14 +82,16 @@ template <int WT, typename Off>
 __device__ __forceinline__ void read_block(const uint32_t* base, Off off, uint32_t* q, uint32_t* scale) {
   const uint32_t sh = static_cast<uint32_t>(off) & 3u;  // 0 or 2
   const uint32_t* a = base + (off >> 2);
-  if constexpr (WT == 0) {
-    // 64 bytes: 17 covering dwords when sh == 2, 16 when sh == 0.
-    uint32_t d[17];
+  if constexpr (WT == 0 || WT == 3 || WT == 4) {
+    // bf16 / f16 (64 bytes) or f32 (128 bytes), no scale: NW + 1 covering dwords when sh == 2,
+    // NW when sh == 0.
+    constexpr int NW = BlockWords<WT>::NW;
+    uint32_t d[NW + 1];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) d[i] = a[i];
-    d[16] = sh ? a[16] : 0u;
+    for (int i = 0; i < NW; ++i) d[i] = a[i];
+    d[NW] = sh ? a[NW] : 0u;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) q[i] = realign(d[i + 1], d[i], sh);
+    for (int i = 0; i < NW; ++i) q[i] = realign(d[i + 1], d[i], sh);
     *scale = 0;
   } else {
     constexpr int NW = BlockWords<WT>::NW;
@@ -91,6 +103,15 @@ __device__ __forceinline__ void read_block(const uint32_t* base, Off off, uint32
 #pragma unroll
     for (int i = 0; i < NW; ++i) q[i] = sh ? d[i + 1] : realign(d[i + 1], d[i], 2u);
   }
+}
+
+// Element e (0..31) of a block of a plain type (bf16 0, f32 3, f16 4) read by read_block, exact.
+template <int WT>
+__device__ __forceinline__ float plain_at(const uint32_t* q, int e) {
+  if constexpr (WT == 3) return __uint_as_float(q[e]);
+  const uint32_t h = (e & 1) ? q[e >> 1] >> 16 : q[e >> 1] & 0xFFFFu;
+  if constexpr (WT == 4) return f16_to_f32(h);
+  return __uint_as_float(h << 16);
 }
 
 // erf, branch-free, to within about 3.2e-7 in f32 (checked against the exact erf over the whole

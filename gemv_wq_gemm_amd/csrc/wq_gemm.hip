@@ -134,12 +134,14 @@ struct QStage {
 template <int WT, int BM, int BN, int WM, int WN, bool SPLIT>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int tiles_m, int tiles_n) {
   using C = GemmCfg<WT, BM, BN, WM, WN>;
-  constexpr bool kQuant = WT != kBF16;
+  constexpr bool kQuant = !plain_type(WT);  // Q8_0 / Q4_0: integer quants and a per-block scale
   __shared__ __attribute__((aligned(16))) __bf16 sA[2][BM * LDS_STRIDE];
   // SPLIT: the second and third bf16 parts of X beside the first ones in sA.
   __shared__ __attribute__((aligned(16))) __bf16 sAm[2][SPLIT ? BM * LDS_STRIDE : 8];
   __shared__ __attribute__((aligned(16))) __bf16 sAl[2][SPLIT ? BM * LDS_STRIDE : 8];
-  __shared__ __attribute__((aligned(16))) __bf16 sB[2][BN * LDS_STRIDE];
+  // W as WP exact bf16 parts (f16 weights 2, f32 weights 3, else 1), each double-buffered.
+  constexpr int WP = weight_parts(WT);
+  __shared__ __attribute__((aligned(16))) __bf16 sB[WP][2][BN * LDS_STRIDE];
   __shared__ float sS[2][kQuant ? BN * 2 : 1];
 
   const int tid = threadIdx.x;
@@ -173,8 +175,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
   const int wr0 = tid >> 3;   // first W row; rows wr0 + i * (threads / 8)
 
   float4 xs[C::kXLoads];
-  uint4 wsb[kQuant ? 1 : C::kWLoads];
-  QStage<WT == kBF16 ? kQ8_0 : WT, C::kQLoads> wsq;
+  // Plain weights: 8 elements per chunk, 16 bytes (bf16, f16) or 32 bytes (f32).
+  constexpr int kChunkU4 = WT == kF32 ? 2 : 1;
+  uint4 wsb[kQuant ? 1 : C::kWLoads][kChunkU4];
+  QStage<plain_type(WT) ? kQ8_0 : WT, C::kQLoads> wsq;
 
   auto load_stage = [&](int s) {
     const int k0 = s * BK;
@@ -191,10 +195,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
       for (int i = 0; i < C::kWLoads; ++i) {
         const int r = m0 + wr0 + i * (C::kThreads / 8);
         const int kk = k0 + 8 * wc16;
-        uint4 v = make_uint4(0u, 0u, 0u, 0u);
-        if (r < p.m && kk < p.k)
-          v = *reinterpret_cast<const uint4*>(p.w + static_cast<long long>(r) * p.rowbytes + 2LL * kk);
-        wsb[i] = v;
+        const uint4* src = reinterpret_cast<const uint4*>(p.w + static_cast<long long>(r) * p.rowbytes +
+                                                          (WT == kF32 ? 4LL : 2LL) * kk);
+#pragma unroll
+        for (int u = 0; u < kChunkU4; ++u) {
+          uint4 v = make_uint4(0u, 0u, 0u, 0u);
+          if (r < p.m && kk < p.k) v = src[u];
+          wsb[i][u] = v;
+        }
       }
     } else {
 #pragma unroll
@@ -230,7 +238,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 #pragma unroll
       for (int i = 0; i < C::kWLoads; ++i) {
         const int r = wr0 + i * (C::kThreads / 8);
-        *reinterpret_cast<uint4*>(&sB[buf][r * LDS_STRIDE + 8 * wc16]) = wsb[i];
+        const int at = r * LDS_STRIDE + 8 * wc16;
+        if constexpr (WT == kBF16) {
+          *reinterpret_cast<uint4*>(&sB[0][buf][at]) = wsb[i][0];
+        } else {
+          // f16 / f32 -> WP bf16 parts that add up to the weight exactly.
+          float4 f[2];
+          if constexpr (WT == kF16) {
+            const uint4 h = wsb[i][0];
+            f[0] = make_float4(f16_to_f32(h.x & 0xFFFFu), f16_to_f32(h.x >> 16), f16_to_f32(h.y & 0xFFFFu),
+                               f16_to_f32(h.y >> 16));
+            f[1] = make_float4(f16_to_f32(h.z & 0xFFFFu), f16_to_f32(h.z >> 16), f16_to_f32(h.w & 0xFFFFu),
+                               f16_to_f32(h.w >> 16));
+          } else {
+            f[0] = __builtin_bit_cast(float4, wsb[i][0]);
+            f[1] = __builtin_bit_cast(float4, wsb[i][1]);
+          }
+          uint2 pa[2][3];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) split3_bf16x4(f[h], pa[h][0], pa[h][1], pa[h][2]);
+#pragma unroll
+          for (int wp = 0; wp < WP; ++wp)
+            *reinterpret_cast<uint4*>(&sB[wp][buf][at]) = make_uint4(pa[0][wp].x, pa[0][wp].y, pa[1][wp].x, pa[1][wp].y);
+        }
       }
     } else {
 #pragma unroll
@@ -248,7 +278,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
             for (int j = 0; j < 16; ++j) o[j] = 0u;
             sS[buf][rr * 2 + half] = 0.f;
           }
-          uint4* dst = reinterpret_cast<uint4*>(&sB[buf][rr * LDS_STRIDE + 32 * half]);
+          uint4* dst = reinterpret_cast<uint4*>(&sB[0][buf][rr * LDS_STRIDE + 32 * half]);
 #pragma unroll
           for (int j = 0; j < 4; ++j) dst[j] = make_uint4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
         }
@@ -268,31 +298,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
   const int frow = lane & 31;
   const int fk = 8 * (lane >> 5);
 
+  // One 16-wide k slice: every part of X (1, or 3 with SPLIT) times every part of W (WP).
   auto mfma_step = [&](int buf, int ks, f32x16 (&c)[C::FM][C::FN]) {
-    bf16x8 a[C::FM], b[C::FN];
+    bf16x8 a[C::FM], b[WP][C::FN];
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][(wm * C::TM + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+    for (int wp = 0; wp < WP; ++wp)
 #pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-      b[j] = *reinterpret_cast<const bf16x8*>(&sB[buf][(wn * C::TN + j * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+      for (int j = 0; j < C::FN; ++j)
+        b[wp][j] =
+            *reinterpret_cast<const bf16x8*>(&sB[wp][buf][(wn * C::TN + j * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
 #pragma unroll
-    for (int i = 0; i < C::FM; ++i)
+    for (int part = 0; part < (SPLIT ? 3 : 1); ++part) {
+      const __bf16* src = part == 0 ? sA[buf] : part == 1 ? sAm[buf] : sAl[buf];
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
-    if constexpr (SPLIT) {
+      for (int i = 0; i < C::FM; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&src[(wm * C::TM + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
 #pragma unroll
-      for (int part = 0; part < 2; ++part) {
-        const __bf16* src = part == 0 ? sAm[buf] : sAl[buf];
-#pragma unroll
-        for (int i = 0; i < C::FM; ++i)
-          a[i] = *reinterpret_cast<const bf16x8*>(&src[(wm * C::TM + i * 32 + frow) * LDS_STRIDE + ks * 16 + fk]);
+      for (int wp = 0; wp < WP; ++wp)
 #pragma unroll
         for (int i = 0; i < C::FM; ++i)
 #pragma unroll
           for (int j = 0; j < C::FN; ++j)
-            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], c[i][j], 0, 0, 0);
-      }
+            c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[wp][j], c[i][j], 0, 0, 0);
     }
   };
 
@@ -599,15 +626,28 @@ int device_cus() {
   return cus[dev];
 }
 
+constexpr int kLdsBytes = 160 * 1024;
+
+// LDS of gemm_kernel: X (x_parts buffers) and W (weight_parts buffers), each double-buffered, plus
+// the block scales of quantized weights.
+constexpr int gemm_lds_bytes(int wt, int bm, int bn, int x_parts) {
+  return 2 * bm * LDS_STRIDE * 2 * x_parts + 2 * bn * LDS_STRIDE * 2 * weight_parts(wt) +
+         (plain_type(wt) ? 8 : 2 * bn * 2 * 4);
+}
+
 template <int WT, int BM, int BN, int WM, int WN>
 hipError_t launch_tile(const GemmParams& p, hipStream_t stream) {
-  // X in three parts needs three A buffers in LDS: more than fits beside W for 128 x 256 tiles.
-  constexpr bool kPartsFit = BM * BN <= 128 * 128;
-  auto kernel = gemm_kernel<WT, BM, BN, WM, WN, false>;
+  // X in three parts needs three A buffers in LDS (and f16 / f32 weights two or three B buffers):
+  // only the tiles whose buffers fit in LDS are built. The launcher never picks another.
+  constexpr bool kFits1 = gemm_lds_bytes(WT, BM, BN, 1) <= kLdsBytes;
+  constexpr bool kFits3 = gemm_lds_bytes(WT, BM, BN, 3) <= kLdsBytes;
+  void (*kernel)(GemmParams, int, int) = nullptr;
   if (p.x_parts == 3) {
-    if constexpr (kPartsFit) kernel = gemm_kernel<WT, BM, BN, WM, WN, true>;
-    else return hipErrorInvalidValue;
+    if constexpr (kFits3) kernel = gemm_kernel<WT, BM, BN, WM, WN, true>;
+  } else {
+    if constexpr (kFits1) kernel = gemm_kernel<WT, BM, BN, WM, WN, false>;
   }
+  if (kernel == nullptr) return hipErrorInvalidValue;
   const int tiles_m = (p.n + BM - 1) / BM;
   const int tiles_n = (p.m + BN - 1) / BN;
   const int tiles = tiles_m * tiles_n;
@@ -685,9 +725,16 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
   // once there are two per CU, 64 x 128 tiles below (measured on MI355X from 256 x 2048 x 2048 to
   // 4096^3; at n = 1500 about 1.7x faster than 4-wave 128 x 256 / 128 x 128 tiles).
   // (X in three parts takes 64 x 128 tiles: the parts of a 128-row tile do not fit in LDS beside W.)
-  const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
-  if (wide_tiles >= 2LL * device_cus() && p.x_parts == 1) return launch_tile<WT, 128, 256, 2, 4>(p, stream);
-  return launch_tile<WT, 64, 128, 2, 4>(p, stream);
+  if constexpr (WT == kF32 || WT == kF16) {
+    // f16 / f32 weights enter as two / three bf16 parts: 64 x 128 tiles, or 64 x 64 tiles of 4
+    // waves where f32 weights meet X in three parts (their six buffers fit no larger tile).
+    if (WT == kF32 && p.x_parts == 3) return launch_tile<WT, 64, 64, 2, 2>(p, stream);
+    return launch_tile<WT, 64, 128, 2, 4>(p, stream);
+  } else {
+    const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);
+    if (wide_tiles >= 2LL * device_cus() && p.x_parts == 1) return launch_tile<WT, 128, 256, 2, 4>(p, stream);
+    return launch_tile<WT, 64, 128, 2, 4>(p, stream);
+  }
 }
 
 }  // namespace
@@ -697,6 +744,8 @@ hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream) {
     case kBF16: return launch_wt<kBF16>(p, stream);
     case kQ8_0: return launch_wt<kQ8_0>(p, stream);
     case kQ4_0: return launch_wt<kQ4_0>(p, stream);
+    case kF32: return launch_wt<kF32>(p, stream);
+    case kF16: return launch_wt<kF16>(p, stream);
     default: return hipErrorInvalidValue;
   }
 }

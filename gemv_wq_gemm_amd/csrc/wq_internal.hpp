@@ -7,10 +7,19 @@
 
 namespace wq {
 
-enum WType : int { kBF16 = 0, kQ8_0 = 1, kQ4_0 = 2 };
+enum WType : int { kBF16 = 0, kQ8_0 = 1, kQ4_0 = 2, kF32 = 3, kF16 = 4 };
 
-// Bytes of one 32-element block in each storage type (bf16: 32 x 2 bytes).
-__host__ __device__ constexpr int block_bytes(int wt) { return wt == kBF16 ? 64 : wt == kQ8_0 ? 34 : 18; }
+// Bytes of one 32-element block in each storage type (bf16, f16: 32 x 2 bytes; f32: 32 x 4).
+__host__ __device__ constexpr int block_bytes(int wt) {
+  return wt == kBF16 || wt == kF16 ? 64 : wt == kF32 ? 128 : wt == kQ8_0 ? 34 : 18;
+}
+
+// Types stored value by value (no per-block scale): bf16, f16, f32.
+__host__ __device__ constexpr bool plain_type(int wt) { return wt == kBF16 || wt == kF16 || wt == kF32; }
+
+// Exact bf16 parts one weight splits into on the matrix cores: bf16 and the integer quants 1,
+// f16 2 (11 significant bits), f32 3 (24 bits).
+__host__ __device__ constexpr int weight_parts(int wt) { return wt == kF32 ? 3 : wt == kF16 ? 2 : 1; }
 
 // ---- matvec / MoE (f32 FMA path) ---------------------------------------------------------------
 struct MatvecParams {

@@ -188,15 +188,12 @@ __global__ __launch_bounds__(kThreads) void matvec_general_kernel(MatvecParams p
               float part[NTC];
 #pragma unroll
               for (int t = 0; t < NTC; ++t) part[t] = 0.f;
-              if constexpr (WT == kBF16) {
+              if constexpr (plain_type(WT)) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                  const float w0 = bf16_lo(q[i]), w1 = bf16_hi(q[i]);
+                for (int i = 0; i < 32; ++i) {
+                  const float wv = plain_at<WT>(q, i);
 #pragma unroll
-                  for (int t = 0; t < NTC; ++t) {
-                    part[t] = __builtin_fmaf(xr[t][j * 32 + 2 * i], w0, part[t]);
-                    part[t] = __builtin_fmaf(xr[t][j * 32 + 2 * i + 1], w1, part[t]);
-                  }
+                  for (int t = 0; t < NTC; ++t) part[t] = __builtin_fmaf(xr[t][j * 32 + i], wv, part[t]);
                 }
 #pragma unroll
                 for (int t = 0; t < NTC; ++t) acc[r][t] += part[t];
@@ -273,10 +270,15 @@ hipError_t launch_rw(const MatvecParams& p, int n_exp_rows, hipStream_t stream) 
   // rows per wave (more reuse of the activations held in VGPRs).
   const long long waves_rw4 = (static_cast<long long>(p.m) + 3) / 4 * n_exp_rows;
   const long long waves_rw2 = (static_cast<long long>(p.m) + 1) / 2 * n_exp_rows;
-  if constexpr (!(WT == kBF16 && KB == 2)) {  // 8 KiB bf16 rows: keep LDS per workgroup modest
+  // Row chunks of 8 KiB (bf16, f16 at KB = 2; f32 at KB = 1) or 16 KiB (f32 at KB = 2): fewer
+  // rows per wave keep the LDS of a workgroup modest.
+  constexpr int kChunkBytes = Geometry<WT, KB>::kChunkBytes;
+  if constexpr (kChunkBytes < 8192) {
     if (waves_rw4 >= 2048) return launch_variant<WT, NTC, KB, 4>(p, n_exp_rows, stream);
   }
-  if (waves_rw2 >= 2048) return launch_variant<WT, NTC, KB, 2>(p, n_exp_rows, stream);
+  if constexpr (kChunkBytes < 16384) {
+    if (waves_rw2 >= 2048) return launch_variant<WT, NTC, KB, 2>(p, n_exp_rows, stream);
+  }
   return launch_variant<WT, NTC, KB, 1>(p, n_exp_rows, stream);
 }
 
@@ -316,12 +318,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* w, float
   read_block<WT>(reinterpret_cast<const uint32_t*>(w), row * rowbytes + static_cast<long long>(blk) * block_bytes(WT),
                  q, &sbits);
   float v[32];
-  if constexpr (WT == kBF16) {
+  if constexpr (plain_type(WT)) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      v[2 * i] = bf16_lo(q[i]);
-      v[2 * i + 1] = bf16_hi(q[i]);
-    }
+    for (int i = 0; i < 32; ++i) v[i] = plain_at<WT>(q, i);
   } else if constexpr (WT == kQ8_0) {
     const float d = f16_to_f32(sbits);
 #pragma unroll
@@ -359,6 +358,8 @@ hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStrea
     case kBF16: return launch_wt<kBF16>(p, max_tok, n_exp_rows, stream);
     case kQ8_0: return launch_wt<kQ8_0>(p, max_tok, n_exp_rows, stream);
     case kQ4_0: return launch_wt<kQ4_0>(p, max_tok, n_exp_rows, stream);
+    case kF32: return launch_wt<kF32>(p, max_tok, n_exp_rows, stream);
+    case kF16: return launch_wt<kF16>(p, max_tok, n_exp_rows, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -385,6 +386,12 @@ hipError_t launch_dequantize(int wtype, const uint8_t* w, float* out, int m, int
       break;
     case kQ4_0:
       hipLaunchKernelGGL(dequantize_kernel<kQ4_0>, dim3(grid), dim3(256), 0, stream, w, out, m, k, rowbytes);
+      break;
+    case kF32:
+      hipLaunchKernelGGL(dequantize_kernel<kF32>, dim3(grid), dim3(256), 0, stream, w, out, m, k, rowbytes);
+      break;
+    case kF16:
+      hipLaunchKernelGGL(dequantize_kernel<kF16>, dim3(grid), dim3(256), 0, stream, w, out, m, k, rowbytes);
       break;
     default: return hipErrorInvalidValue;
   }

@@ -123,7 +123,7 @@ constexpr int flush_rows(int ntc, int maxw) { return 4096 / (ntc * maxw) < 128 ?
 // (element order as described above) and returns the factor that scales their sum.
 template <int WT, int E>
 __device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int q, float (&wv)[E]) {
-  if constexpr (WT == kBF16) {
+  if constexpr (WT == kBF16 || WT == kF16) {
     const uint32_t* a = reinterpret_cast<const uint32_t*>(lds + boff + 2 * E * q);
     uint32_t w[E / 2];
 #pragma unroll
@@ -136,8 +136,24 @@ __device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int q
     }
 #pragma unroll
     for (int i = 0; i < E / 2; ++i) {
-      wv[2 * i] = bf16_lo(w[i]);
-      wv[2 * i + 1] = bf16_hi(w[i]);
+      if constexpr (WT == kBF16) {
+        wv[2 * i] = bf16_lo(w[i]);
+        wv[2 * i + 1] = bf16_hi(w[i]);
+      } else {
+        wv[2 * i] = f16_to_f32(w[i] & 0xFFFFu);
+        wv[2 * i + 1] = f16_to_f32(w[i] >> 16);
+      }
+    }
+    return 1.f;
+  } else if constexpr (WT == kF32) {
+    const float4* a = reinterpret_cast<const float4*>(lds + boff + 4 * E * q);
+#pragma unroll
+    for (int i = 0; i < E / 4; ++i) {
+      const float4 v = a[i];
+      wv[4 * i] = v.x;
+      wv[4 * i + 1] = v.y;
+      wv[4 * i + 2] = v.z;
+      wv[4 * i + 3] = v.w;
     }
     return 1.f;
   } else if constexpr (WT == kQ8_0) {
@@ -429,7 +445,8 @@ constexpr Shape sliced_shape(int wt, int ntc, bool k8) {
     if (!k8) return ntc == 4 ? Shape{4, 3, 1024} : Shape{4, 2, 1024};
     return ntc == 1 ? Shape{8, 2, 1024} : Shape{4, 2, 1024};
   }
-  return k8 ? Shape{2, 2, 1024} : Shape{4, 2, 512};
+  if (wt == kF32) return k8 ? Shape{2, 2, 1024} : Shape{2, 2, 512};  // rows twice bf16's
+  return k8 ? Shape{2, 2, 1024} : Shape{4, 2, 512};                  // bf16, f16
 }
 
 template <int WT, int NTC, bool K8>
@@ -463,6 +480,8 @@ hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tok, h
     case kBF16: return launch_wt<kBF16>(p, max_tok, n_exp_rows, stream);
     case kQ8_0: return launch_wt<kQ8_0>(p, max_tok, n_exp_rows, stream);
     case kQ4_0: return launch_wt<kQ4_0>(p, max_tok, n_exp_rows, stream);
+    case kF32: return launch_wt<kF32>(p, max_tok, n_exp_rows, stream);
+    case kF16: return launch_wt<kF16>(p, max_tok, n_exp_rows, stream);
     default: return hipErrorInvalidValue;
   }
 }

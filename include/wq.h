@@ -49,10 +49,20 @@ extern "C" {
  * WQ_W_Q4_0: m rows of k/32 blocks of 18 bytes: a little-endian f16 scale d,
  *            then 16 bytes; byte j holds element j in its low nibble and
  *            element j+16 in its high nibble; value = d*(q-8) (hanzo-ml
- *            `matvec_q4_0_gpu`). Rows follow each other with no padding. */
+ *            `matvec_q4_0_gpu`). Rows follow each other with no padding.
+ * WQ_W_F32:  float[m][k], IEEE binary32, little-endian (wavo `Linear` GEMM
+ *            type 0, copied as stored by `Gpu::upload_linear`).
+ * WQ_W_F16:  uint16[m][k], IEEE binary16, little-endian (wavo `Linear` GEMM
+ *            type 1).
+ * Every type enters every path exactly: the f32 paths decode each weight to
+ * its f32 value; the matrix cores take bf16 as stored, the integer quants with
+ * the block scale applied in f32, and f16 / f32 weights as two / three bf16
+ * parts that add up to the weight (two / three times the MFMA work). */
 #define WQ_W_BF16 0
 #define WQ_W_Q8_0 1
 #define WQ_W_Q4_0 2
+#define WQ_W_F32 3
+#define WQ_W_F16 4
 
 /* ---- epilogue flags ---------------------------------------------------------
  * Applied to each output in this order: + bias[j] (WQ_BIAS); then at most one
@@ -159,12 +169,13 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
 
 /*
  * wq_dequantize: out[m][k] = the exact f32 value of every weight (bf16: the
- * upper-half bit pattern; Q8_0: d*q; Q4_0: d*(q-8), all exact in f32).
+ * upper-half bit pattern; Q8_0: d*q; Q4_0: d*(q-8); f32 as stored; f16
+ * widened; all exact in f32).
  *   w    weight in `wtype` storage, 16-byte aligned; out f32 [m][k], 16-byte aligned.
  */
 int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream);
 
-/* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32);
+/* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32); f32 4*m*k; f16 2*m*k;
  * -1 for an unknown type, negative sizes or k % 32 != 0. */
 int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k);
 

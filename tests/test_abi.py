@@ -39,6 +39,7 @@ def test_header_constants_match_binding():
     assert int(consts["WQ_W_BF16"]) == wq.W_BF16
     assert int(consts["WQ_W_Q8_0"]) == wq.W_Q8_0
     assert int(consts["WQ_W_Q4_0"]) == wq.W_Q4_0
+    assert int(consts["WQ_W_F32"]) == wq.W_F32 and int(consts["WQ_W_F16"]) == wq.W_F16
     assert int(consts["WQ_BIAS"]) == wq.BIAS and int(consts["WQ_GELU"]) == wq.GELU
     assert int(consts["WQ_RESIDUAL"]) == wq.RESIDUAL
     assert [int(consts[f"WQ_{a}"]) for a in ("SILU", "RELU", "TANH")] == [wq.SILU, wq.RELU, wq.TANH]
@@ -62,7 +63,10 @@ def test_version():
     (2, 1, 32, 18),
     (0, 0, 64, 0),
     (1, 5, 33, -1),
-    (3, 5, 32, -1),
+    (3, 5, 32, 640),
+    (4, 5, 32, 320),
+    (3, 5, 48, -1),
+    (5, 5, 32, -1),
     (0, -1, 32, -1),
 ])
 def test_weight_bytes(wtype, m, k, want):
@@ -85,7 +89,8 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
 
 
 @pytest.mark.parametrize("kwargs,code,msg", [
-    (dict(wtype=3), -3, "weight type"),
+    (dict(wtype=5), -3, "weight type"),
+    (dict(wtype=-1), -3, "weight type"),
     (dict(flags=64), -4, "flag"),
     (dict(flags=2 | 8), -4, "at most one activation"),
     (dict(flags=16 | 32 | 4), -4, "at most one activation"),
@@ -127,7 +132,7 @@ def test_linear_refuses_non_finite_alpha(alpha):
 
 def test_linear_checks_like_gemm_ex():
     lib = wq.lib()
-    assert lib.wq_linear(X, W, 3, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -3
+    assert lib.wq_linear(X, W, 5, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -3
     assert lib.wq_linear(X, W, 0, None, 2 | 16, ctypes.c_float(0.5), Y, 4, 8, 32, 2, None) == -4
     assert lib.wq_linear(X, W, 0, None, 0, ctypes.c_float(0.5), Y, 4, 8, 40, 0, None) == -2
     assert lib.wq_linear(None, None, 0, None, 0, ctypes.c_float(2.0), None, 0, 8, 32, 0, None) == 0
