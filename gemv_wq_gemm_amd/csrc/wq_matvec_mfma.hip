@@ -24,10 +24,11 @@
 //
 // Layout of the work (gfx950, wave64):
 //  * A workgroup has k/(32 SB) waves; wave w owns SB blocks of every row, the k-slice
-//    [32 SB w, 32 SB (w + 1)). Q4_0 takes SB = 8 (up to 16 waves): the activation parts of a
-//    narrower slice need half the registers, so four waves fit on each SIMD instead of two and
-//    hide each other's LDS and barrier waits (the MoE workload 9% faster). Q8_0 keeps SB = 16:
-//    its tiles are twice as large, and the partial sums of 16 waves would not fit beside them. MFMA roles: A = activations (16 slots x 32 k), B = weights (32 k x 16 weight
+//    [32 SB w, 32 SB (w + 1)). Both types take SB = 8 (up to 16 waves): the activation parts of a
+//    256-element slice need half the registers of a 512-element one, so four waves fit on each
+//    SIMD instead of two and hide each other's LDS and barrier waits (9-10% faster for both
+//    types, on the MoE workload and on the plain layer at 12 and 16 tokens). Q8_0 tiles are
+//    twice as large, so its 16 waves keep a single buffer of partial sums (PB = 1). MFMA roles: A = activations (16 slots x 32 k), B = weights (32 k x 16 weight
 //    rows), D[t][j] in lane 16 (t / 4) + j, value t % 4.
 //  * Lane l = 16 o + j: weight row j of the tile and k-octet o of each block (elements 8o..8o+7);
 //    as A it holds slot j at the same octet. Its three activation parts for the SB blocks of its
@@ -135,7 +136,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
-template <int WT, int NSTAGE, int SB>
+// PB: buffers of wave partial sums (2: a tile's partials are written while the previous tile's
+// are still being added up; 1: one buffer and one more barrier per tile, for LDS).
+template <int WT, int NSTAGE, int SB, int PB>
 __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(MatvecParams p, int tiles_per_wg) {
   constexpr int kSliceBlocks = SB;  // blocks per wave
   constexpr int kMaxWaves = kMaxK / (32 * SB);
@@ -149,7 +152,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
   static_assert(NSTAGE >= 2 && kMaxPending < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE * kSlotBytes];
-  __shared__ float part[2][kMaxWaves * kPartWave];
+  __shared__ float part[PB][kMaxWaves * kPartWave];
   __shared__ int slot_lds[kSlots];
 
   const int lane = threadIdx.x & 63;
@@ -287,10 +290,10 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         // This wave's loads of `tile` have landed once only those of the later tiles in flight
         // are pending (the exact count: a smaller one would also wait for part of the next tile).
         wait_at_most<kMaxPending>(per_tile * min(NSTAGE - 2, t_end - 1 - tile));
-        __syncthreads();  // the tile is in; the slot of tile-1 and part[(tile-1)&1] are complete
+        __syncthreads();  // the tile is in; the slot of tile-1 and the partials of tile-1 are complete
         // Stores count in vmcnt too: issued before the next tile's loads, they are never among the
         // most recent operations a wait leaves in flight, so they cannot stretch it.
-        if (tile > t_begin) finish(tile - 1, (tile - 1) & 1);
+        if (tile > t_begin) finish(tile - 1, (tile - 1) % PB);
         if (tile + NSTAGE - 1 < t_end) issue(tile + NSTAGE - 1);
 
         const int slot_base = (tile % NSTAGE) * kSlotBytes;
@@ -308,12 +311,14 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
           // Keep the scheduler within a few blocks: hoisting many decodes runs out of registers.
           if constexpr (B % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
         });
-        float* pw = part[tile & 1] + wave * kPartWave;
+        // One buffer: every thread has finished adding up the previous tile's partials.
+        if constexpr (PB == 1) __syncthreads();
+        float* pw = part[tile % PB] + wave * kPartWave;
 #pragma unroll
         for (int v = 0; v < 4; ++v) pw[(4 * o + v) * kTileRows + j] = acc[v];
       }
       __syncthreads();
-      finish(t_end - 1, (t_end - 1) & 1);
+      finish(t_end - 1, (t_end - 1) % PB);
       __syncthreads();  // part, slot_lds and the ring are reused by the next group of slots
     }
   }
@@ -331,12 +336,12 @@ int mfma_device_cus() {
   return cus[dev];
 }
 
-template <int WT, int NSTAGE, int SB>
+template <int WT, int NSTAGE, int SB, int PB>
 hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
   constexpr int kMaxWaves = kMaxK / (32 * SB);
   const int nw = p.k / (32 * SB);
   const int ntiles = (p.m + kTileRows - 1) / kTileRows;
-  auto kernel = matvec_mfma_kernel<WT, NSTAGE, SB>;
+  auto kernel = matvec_mfma_kernel<WT, NSTAGE, SB, PB>;
   static int per_cu = 0;
   if (per_cu <= 0) {
     int v = 0;
@@ -362,8 +367,8 @@ bool matvec_mfma_supports(int wtype, int k) {
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream) {
   if (!matvec_mfma_supports(wtype, p.k) || (p.ids == nullptr && p.n_exp != 1)) return hipErrorInvalidValue;
   // LDS: a Q8_0 tile is twice a Q4_0 one, so Q8_0 runs a shallower ring.
-  if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2, 16>(p, stream);
-  return launch_mfma<kQ4_0, 3, 8>(p, stream);
+  if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2, 8, 1>(p, stream);
+  return launch_mfma<kQ4_0, 3, 8, 2>(p, stream);
 }
 
 }  // namespace wq
