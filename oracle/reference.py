@@ -235,6 +235,30 @@ def epilogue(v: np.ndarray, flags: int, bias=None, y_old=None, alpha: float = 1.
 # The layer
 # ---------------------------------------------------------------------------
 
+def linear_dual(x, w_raw, wtype: int, m: int, k: int, dual: int, bias=None, flags: int = 0, y_old=None,
+                alpha: float = 1.0):
+    """``(Y_ref, S)`` with wavo's dual outputs: ``Y`` is ``[n][m + dual]``; columns ``0..m-1``
+    are the layer with ``bias[0..m-1]``, and columns ``m + j`` (``j < dual``) repeat output ``j``
+    with its own bias ``bias[m + j]`` (wavo ``Linear.dual`` and ``Gpu::upload_linear``: the first
+    ``dual`` outputs written again after the others, with the extra bias values). ``y_old`` is
+    ``[n][m + dual]`` too; ``S`` is that of each column's product.
+    """
+    if not 0 <= dual <= m:
+        raise ValueError("dual must be in [0, m]")
+    n = np.asarray(x).reshape(-1, k).shape[0]
+    b = None if bias is None else np.asarray(bias, dtype=np.float64).reshape(-1)
+    yo = None if y_old is None else np.asarray(y_old, dtype=np.float64).reshape(n, m + dual)
+    main, s = linear(x, w_raw, wtype, m, k, None if b is None else b[:m], flags,
+                     None if yo is None else yo[:, :m], alpha=alpha)
+    if dual == 0:
+        return main, s
+    rows = np.arange(dual)
+    bias2 = None if b is None else np.concatenate([b[m:m + dual], np.zeros(m - dual)])
+    yo2 = None if yo is None else np.concatenate([yo[:, m:], np.zeros((n, m - dual))], axis=1)
+    second, s2 = linear(x, w_raw, wtype, m, k, bias2, flags, yo2, rows=rows, alpha=alpha)
+    return np.concatenate([main, second], axis=1), np.concatenate([s, s2], axis=1)
+
+
 def linear(x, w_raw, wtype: int, m: int, k: int, bias=None, flags: int = 0, y_old=None,
            rows=None, alpha: float = 1.0):
     """``(Y_ref, S)`` for ``Y = epilogue(X . W^T + b)``; both ``f64[n][len(rows) or m]``.

@@ -119,3 +119,31 @@ def test_linear_with_each_activation_matches_brute_force(wtype, act, alpha):
     got, _ = oracle.linear(x, raw, wtype, m, k, bias, flags, y_old, alpha=alpha)
     want = _brute(x, raw, wtype, m, k, bias, act, alpha, y_old)
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+def test_dual_outputs_repeat_the_first_outputs_with_their_own_bias():
+    # wavo Linear.dual: the first `dual` outputs again after the m others, with bias[m + j].
+    g = synth.rng(63)
+    n, m, k, dual = 3, 5, 64, 2
+    x = synth.normal_f32(g, (n, k), 1.0)
+    w = synth.bf16_weight(g, m, k, 0.1)
+    bias = synth.normal_f32(g, (m + dual,), 0.5)
+    y_old = synth.normal_f32(g, (n, m + dual), 1.0)
+    flags = oracle.FLAG_BIAS | oracle.FLAG_SILU | oracle.FLAG_RESIDUAL
+    got, s = oracle.linear_dual(x, w, oracle.W_BF16, m, k, dual, bias, flags, y_old, alpha=0.5)
+    assert got.shape == (n, m + dual) and s.shape == (n, m + dual)
+    # brute force, column by column
+    wd = oracle.decode(w, oracle.W_BF16, m, k)
+    for t in range(n):
+        for c in range(m + dual):
+            j = c if c < m else c - m
+            v = math.fsum(float(x[t, i]) * wd[j, i] for i in range(k)) + float(bias[c])
+            want = float(y_old[t, c]) + 0.5 * v * 0.5 * (1.0 + math.tanh(0.5 * v))
+            assert got[t, c] == pytest.approx(want, rel=1e-12, abs=1e-12)
+    assert np.array_equal(s[:, m:], s[:, :dual])
+    # dual = 0 is the plain layer
+    plain, _ = oracle.linear(x, w, oracle.W_BF16, m, k, bias[:m], flags, y_old[:, :m], alpha=0.5)
+    zero, _ = oracle.linear_dual(x, w, oracle.W_BF16, m, k, 0, bias[:m], flags, y_old[:, :m], alpha=0.5)
+    assert np.array_equal(plain, zero)
+    with pytest.raises(ValueError):
+        oracle.linear_dual(x, w, oracle.W_BF16, m, k, m + 1)
