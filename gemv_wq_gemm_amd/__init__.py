@@ -34,6 +34,7 @@ SIGNATURES = [
     ("wq_gemm", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _P]),
     ("wq_gemm_ex", _I, [_P, _P, _I, _P, _U, _P, _I64, _I64, _I64, _I, _P]),
     ("wq_linear", _I, [_P, _P, _I, _P, _U, ctypes.c_float, _P, _I64, _I64, _I64, _I, _P]),
+    ("wq_linear_dual", _I, [_P, _P, _I, _P, _U, ctypes.c_float, _P, _I64, _I64, _I64, _I64, _I, _P]),
     ("wq_moe_matvec", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     ("wq_dequantize", _I, [_P, _I, _P, _I64, _I64, _P]),
     ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
@@ -135,13 +136,15 @@ def _flags(bias, gelu: bool, act, residual: bool) -> int:
 
 
 def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, residual: bool = False,
-         out=None, path: int = PATH_AUTO, act=None, alpha: float = 1.0):
-    """``out[n][m] = alpha * act(x[n][k] . W^T + bias) (+ out)`` via ``wq_linear``.
+         out=None, path: int = PATH_AUTO, act=None, alpha: float = 1.0, dual: int = 0):
+    """``out[n][m] = alpha * act(x[n][k] . W^T + bias) (+ out)`` via ``wq_linear_dual``.
 
     ``w`` holds the weight in its storage format (any dtype; its bytes are
     used). ``act`` is None, "gelu", "silu", "relu" or "tanh" (``gelu=True`` is
     ``act="gelu"``). With ``residual=True``, ``out`` is required and
-    accumulated into.
+    accumulated into. With ``dual > 0``, ``out`` is ``[n][m + dual]`` and
+    ``bias`` has ``m + dual`` values: outputs ``0..dual-1`` are written again
+    at ``m + j`` with ``bias[m + j]``.
     """
     import torch
     n = x.numel() // k if k else 0
@@ -150,15 +153,15 @@ def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, res
     if out is None:
         if residual:
             raise ValueError("residual=True needs out= (the values to accumulate into)")
-        out = torch.empty((n, m), dtype=torch.float32, device=x.device)
+        out = torch.empty((n, m + dual), dtype=torch.float32, device=x.device)
     flags = _flags(bias, gelu, act, residual)
     nbytes = weight_bytes(wtype, m, k)
     if nbytes < 0:
         _check(lib().wq_gemm_path(n, m, k, wtype))
-    st = lib().wq_linear(
+    st = lib().wq_linear_dual(
         _f32(x, "x"), _weight(w, wtype, nbytes), wtype,
-        None if bias is None else _f32(bias, "bias", m), flags, float(alpha),
-        _f32(out, "out", n * m), n, m, k, path, _stream())
+        None if bias is None else _f32(bias, "bias", m + dual), flags, float(alpha),
+        _f32(out, "out", n * (m + dual)), n, m, k, dual, path, _stream())
     _check(st)
     return out
 

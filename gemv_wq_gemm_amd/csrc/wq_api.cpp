@@ -95,7 +95,7 @@ int workspace(hipStream_t stream, size_t bytes, void** out) {
 }
 
 int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
-                 float* y, int64_t n, int64_t m, int64_t k, int path, void* stream) {
+                 float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   constexpr unsigned kActs = WQ_GELU | WQ_SILU | WQ_RELU | WQ_TANH;
@@ -110,6 +110,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
   if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size n = %lld, m = %lld", (long long)n, (long long)m);
   if (int r = check_k(k)) return r;
   if (n > kIntMax || m > kIntMax) return fail(WQ_ERR_SHAPE, "n or m exceeds 2^31 - 1");
+  if (dual < 0 || dual > m) return fail(WQ_ERR_SHAPE, "dual must be in [0, m], got %lld", (long long)dual);
+  if (m + dual > kIntMax) return fail(WQ_ERR_SHAPE, "m + dual exceeds 2^31 - 1");
   if (path == WQ_PATH_AUTO) path = n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
   if (path == WQ_PATH_MATVEC && n > WQ_MATVEC_MAX_N)
     return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
@@ -121,8 +123,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     return fail(WQ_ERR_ALIGN, "x, w and y must be 16-byte aligned");
   if (bias && !aligned(bias, 4)) return fail(WQ_ERR_ALIGN, "bias must be 4-byte aligned");
   const int64_t wbytes = wq_weight_bytes(wtype, m, k);
-  const int64_t ybytes = n * m * 4;
-  if (overlap(y, ybytes, x, n * k * 4) || overlap(y, ybytes, w, wbytes) || overlap(y, ybytes, bias, m * 4))
+  const int64_t ybytes = n * (m + dual) * 4;
+  if (overlap(y, ybytes, x, n * k * 4) || overlap(y, ybytes, w, wbytes) || overlap(y, ybytes, bias, (m + dual) * 4))
     return fail(WQ_ERR_ALIAS, "y overlaps x, w or bias");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -144,6 +146,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.rowbytes = rowbytes;
     p.flags = flags;
     p.alpha = alpha;
+    p.ystride = static_cast<int>(m + dual);
+    p.dual = static_cast<int>(dual);
     e = wq::launch_matvec(wtype, p, static_cast<int>(n), s);
   } else {
     wq::GemmParams p{};
@@ -157,6 +161,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.rowbytes = rowbytes;
     p.flags = flags;
     p.alpha = alpha;
+    p.ystride = static_cast<int>(m + dual);
+    p.dual = static_cast<int>(dual);
     p.x_parts = path == WQ_PATH_MFMA_F32 ? 3 : 1;
     e = wq::launch_gemm(wtype, p, s);
   }
@@ -190,17 +196,22 @@ int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype) {
 
 int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
             int64_t m, int64_t k, void* stream) {
-  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, WQ_PATH_AUTO, stream);
+  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, 0, WQ_PATH_AUTO, stream);
 }
 
 int wq_gemm_ex(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float* y, int64_t n,
                int64_t m, int64_t k, int path, void* stream) {
-  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, path, stream);
+  return gemm_checked(x, w, wtype, bias, flags, 1.0f, y, n, m, k, 0, path, stream);
 }
 
 int wq_linear(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha, float* y,
               int64_t n, int64_t m, int64_t k, int path, void* stream) {
-  return gemm_checked(x, w, wtype, bias, flags, alpha, y, n, m, k, path, stream);
+  return gemm_checked(x, w, wtype, bias, flags, alpha, y, n, m, k, 0, path, stream);
+}
+
+int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
+                   float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream) {
+  return gemm_checked(x, w, wtype, bias, flags, alpha, y, n, m, k, dual, path, stream);
 }
 
 int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
@@ -249,6 +260,8 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
   p.rowbytes = ebytes / m;
   p.flags = 0;
   p.alpha = 1.0f;
+  p.ystride = static_cast<int>(m);
+  p.dual = 0;
   // Twice the mean count of slots per expert picks the tokens-per-pass variant: an expert
   // holding more than that is rare, and is still served exactly by a further pass over its rows.
   const int64_t per_expert = 2 * ((n_slots + n_experts - 1) / n_experts);

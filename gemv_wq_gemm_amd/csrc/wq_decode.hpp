@@ -167,6 +167,8 @@ __device__ __forceinline__ float activation(float v, unsigned flags) {
 }
 
 // The whole epilogue of one output: (+ bias) -> activation -> times alpha -> (+ old output).
+// Dual outputs (wavo `Linear.dual`) call it a second time for output j < dual, with bias[m + j]
+// and the old value at column m + j.
 // `bias` and `old` are read only when their flags are set.
 __device__ __forceinline__ float epilogue(float acc, unsigned flags, float alpha, const float* bias,
                                           const float* old) {

@@ -368,17 +368,24 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
     const int col = m0 + wn * C::TN + j * 32 + frow;
     if (col >= p.m) continue;
     const float b = (p.flags & kEpiBias) && first ? p.bias[col] : 0.f;
+    const float b2 = (p.flags & kEpiBias) && first && col < p.dual ? p.bias[p.m + col] : 0.f;
 #pragma unroll
     for (int i = 0; i < C::FM; ++i) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = n0 + wm * C::TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
         if (row < p.n) {
-          float* yp = p.y + static_cast<long long>(row) * p.m + col;
+          float* yp = p.y + static_cast<long long>(row) * p.ystride + col;
           float o = acc[i][j][v] + b;
           if (split) {
             unsafeAtomicAdd(yp, p.alpha * o);  // Y already holds the old values (residual, no activation)
+            if (col < p.dual) unsafeAtomicAdd(yp + p.m, p.alpha * (acc[i][j][v] + b2));
           } else {
+            if (col < p.dual) {
+              float o2 = p.alpha * activation(acc[i][j][v] + b2, p.flags);
+              if (p.flags & kEpiResidual) o2 += yp[p.m];
+              yp[p.m] = o2;
+            }
             o = p.alpha * activation(o, p.flags);
             if (p.flags & kEpiResidual) o += *yp;
             *yp = o;
@@ -590,12 +597,37 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
         for (int v = 0; v < 16; ++v) {
           const int row = n0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
           if (full || row < p.n) {
-            float* yp = p.y + static_cast<long long>(row) * p.m + col;
+            float* yp = p.y + static_cast<long long>(row) * p.ystride + col;
             float o = acc[i][j][v] + bias_v[j];
             if constexpr (decltype(act)::value != 0) o = activation(o, decltype(act)::value);
             o *= p.alpha;
             if constexpr (decltype(res)::value) o += *yp;
             *yp = o;
+          }
+        }
+      }
+    }
+    // wavo's dual outputs: columns below `dual` are stored again at m + col, with bias[m + col].
+    // A second pass, taken only by waves that own such columns, keeps the store above unchanged.
+    if (p.dual > m0 + wn * TN) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = m0 + wn * TN + j * 32 + frow;
+        if (col >= p.dual) continue;
+        const float b2 = (p.flags & kEpiBias) ? p.bias[p.m + col] : 0.f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int row = n0 + wm * TM + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (row < p.n) {
+              float* yq = p.y + static_cast<long long>(row) * p.ystride + p.m + col;
+              float o = acc[i][j][v] + b2;
+              if constexpr (decltype(act)::value != 0) o = activation(o, decltype(act)::value);
+              o *= p.alpha;
+              if constexpr (decltype(res)::value) o += *yq;
+              *yq = o;
+            }
           }
         }
       }

@@ -36,6 +36,8 @@ struct MatvecParams {
   long long rowbytes;       // bytes of one weight row
   unsigned flags;           // epilogue flags (plain layer only)
   float alpha;              // factor on the activated value (plain layer only)
+  int ystride;              // floats from one row of y to the next: m + dual (MoE: m)
+  int dual;                 // plain layer: outputs 0..dual-1 stored again at m + j (bias[m + j])
 };
 
 // Picks the kernel variant (tokens per pass, rows per wave) and launches it.
@@ -73,6 +75,8 @@ struct GemmParams {
   long long rowbytes;
   unsigned flags;
   float alpha;        // factor on the activated value, before the old output is added
+  int ystride;        // floats from one row of y to the next: m + dual
+  int dual;           // outputs 0..dual-1 stored again at columns m + j, with bias[m + j]
   int x_parts;        // 3: X enters as three exact bf16 parts (three MFMAs per product); 1: as bf16(X)
 };
 

@@ -243,10 +243,11 @@ __global__ __launch_bounds__(kThreads) void matvec_general_kernel(MatvecParams p
           const float v = wave_sum(acc[r][t]);
           const int row = row0 + r;
           if (lane == r * NTC + t && slot[t] >= 0 && row < p.m) {
-            float* yp = p.y + static_cast<long long>(slot[t]) * p.m + row;
+            float* yp = p.y + static_cast<long long>(slot[t]) * p.ystride + row;
             float o = v;
             if (!moe) {
               o = epilogue(o, p.flags, p.alpha, p.bias + row, yp);
+              if (row < p.dual) yp[p.m] = epilogue(v, p.flags, p.alpha, p.bias + p.m + row, yp + p.m);
             }
             *yp = o;
           }

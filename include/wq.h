@@ -147,6 +147,22 @@ int wq_linear(const float* x, const void* w, int wtype, const float* bias, unsig
               float* y, int64_t n, int64_t m, int64_t k, int path, void* stream);
 
 /*
+ * wq_linear_dual: wq_linear with wavo's dual outputs (`Linear.dual`, set up by
+ * `Gpu::upload_linear` from a bias with `dual` extra values): the first `dual`
+ * outputs are written a second time, after the m others, each with its own
+ * bias -- for one projection that needs two position biases.
+ *   bias  f32 [m + dual] when flags & WQ_BIAS (bias[m + j] is the second bias
+ *         of output j), else NULL.
+ *   y     f32 [n][m + dual]: y[t][j] for j < m as wq_linear; y[t][m + j] for
+ *         j < dual is the same product with bias[m + j], the same activation
+ *         and alpha, and (WQ_RESIDUAL) its own old value.
+ *   dual  0 <= dual <= m (WQ_ERR_SHAPE otherwise); 0 is exactly wq_linear.
+ * Every other argument as for wq_linear.
+ */
+int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
+                   float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream);
+
+/*
  * wq_moe_matvec: the MoE matvec of hanzo-ml `moe_matvec_gpu`, expert-major.
  *   x          f32 [n_tok][k], 16-byte aligned.
  *   w_experts  one bank of n_experts weights, expert e at byte offset

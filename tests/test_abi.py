@@ -13,6 +13,15 @@ import pytest
 import gemv_wq_gemm_amd as wq
 from tests.conftest import ROOT
 
+# The calls below pass fake device addresses and rely on the host checks to refuse them. With a GPU
+# present a slip in one of them would launch a kernel on those addresses, so the module runs only
+# where no GPU is visible (device_count does not initialise the runtime).
+import torch  # noqa: E402
+
+if torch.cuda.device_count() > 0:
+    pytest.skip("host-side checks with fake device pointers: run where no GPU is visible",
+                allow_module_level=True)
+
 HEADER = os.path.join(ROOT, "include", "wq.h")
 
 # Aligned fake addresses, never dereferenced (every call here fails validation).
@@ -136,6 +145,18 @@ def test_linear_checks_like_gemm_ex():
     assert lib.wq_linear(X, W, 0, None, 2 | 16, ctypes.c_float(0.5), Y, 4, 8, 32, 2, None) == -4
     assert lib.wq_linear(X, W, 0, None, 0, ctypes.c_float(0.5), Y, 4, 8, 40, 0, None) == -2
     assert lib.wq_linear(None, None, 0, None, 0, ctypes.c_float(2.0), None, 0, 8, 32, 0, None) == 0
+
+
+def test_linear_dual_checks():
+    lib = wq.lib()
+    one = ctypes.c_float(1.0)
+    assert lib.wq_linear_dual(X, W, 0, None, 0, one, Y, 4, 8, 32, -1, 0, None) == -2
+    assert lib.wq_linear_dual(X, W, 0, None, 0, one, Y, 4, 8, 32, 9, 0, None) == -2
+    assert "dual" in lib.wq_last_error().decode()
+    # y [4][8 + 8] f32 is 256 bytes, [4][8] would be 128: a bias 200 bytes on overlaps y only
+    # through the dual columns. (Every call here must fail a host check: none may reach a launch.)
+    assert lib.wq_linear_dual(X, W, 0, Y + 200, 1, one, Y, 4, 8, 32, 8, 0, None) == -6
+    assert lib.wq_linear_dual(None, None, 0, None, 0, one, None, 0, 8, 32, 3, 0, None) == 0
 
 
 def test_binding_refuses_unknown_or_double_activation():
