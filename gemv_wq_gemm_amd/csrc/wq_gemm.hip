@@ -379,9 +379,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
           float o = acc[i][j][v] + b;
           if (split) {
             unsafeAtomicAdd(yp, p.alpha * o);  // Y already holds the old values (residual, no activation)
-            if (col < p.dual) unsafeAtomicAdd(yp + p.m, p.alpha * (acc[i][j][v] + b2));
+            if (p.dual > 0 && col < p.dual) unsafeAtomicAdd(yp + p.m, p.alpha * (acc[i][j][v] + b2));
           } else {
-            if (col < p.dual) {
+            if (p.dual > 0 && col < p.dual) {
               float o2 = p.alpha * activation(acc[i][j][v] + b2, p.flags);
               if (p.flags & kEpiResidual) o2 += yp[p.m];
               yp[p.m] = o2;

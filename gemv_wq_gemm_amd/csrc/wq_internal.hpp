@@ -36,7 +36,8 @@ struct MatvecParams {
   long long rowbytes;       // bytes of one weight row
   unsigned flags;           // epilogue flags (plain layer only)
   float alpha;              // factor on the activated value (plain layer only)
-  int ystride;              // floats from one row of y to the next: m + dual (MoE: m)
+  int ystride;              // floats from one row of y to the next: m + dual (MoE: m); the sliced
+                            // and matrix-core kernels take only dual == 0 (stride m)
   int dual;                 // plain layer: outputs 0..dual-1 stored again at m + j (bias[m + j])
 };
 

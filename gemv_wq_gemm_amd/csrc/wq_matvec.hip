@@ -247,7 +247,8 @@ __global__ __launch_bounds__(kThreads) void matvec_general_kernel(MatvecParams p
             float o = v;
             if (!moe) {
               o = epilogue(o, p.flags, p.alpha, p.bias + row, yp);
-              if (row < p.dual) yp[p.m] = epilogue(v, p.flags, p.alpha, p.bias + p.m + row, yp + p.m);
+              if (p.dual > 0 && row < p.dual)
+                yp[p.m] = epilogue(v, p.flags, p.alpha, p.bias + p.m + row, yp + p.m);
             }
             *yp = o;
           }
@@ -352,8 +353,13 @@ hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStrea
   // operands once). The plain layer takes the f32 FMA kernels up to 8 tokens (one pass); from 9
   // tokens, where those would stream the weights twice, the matrix cores (one pass for up to 16,
   // measured 20.9 -> 16.3 us for Q8_0 4096 x 4096 at n = 16).
-  if (matvec_mfma_supports(wtype, p.k) && (p.ids != nullptr || max_tok > 8)) return launch_matvec_mfma(wtype, p, stream);
-  if (matvec_sliced_supports(p.k)) return launch_matvec_sliced(wtype, p, max_tok, stream);
+  // Dual outputs (wavo `Linear.dual`) are stored by this file's general kernel only: the sliced
+  // and matrix-core kernels keep one output per row, since even a skipped second store in their
+  // flush measured 12% slower on Q4_0 14336 x 4096 at n = 1.
+  const bool dual = p.dual > 0;
+  if (!dual && matvec_mfma_supports(wtype, p.k) && (p.ids != nullptr || max_tok > 8))
+    return launch_matvec_mfma(wtype, p, stream);
+  if (!dual && matvec_sliced_supports(p.k)) return launch_matvec_sliced(wtype, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;
   switch (wtype) {
     case kBF16: return launch_wt<kBF16>(p, max_tok, n_exp_rows, stream);

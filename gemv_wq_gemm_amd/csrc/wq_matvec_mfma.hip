@@ -224,8 +224,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         // Not unrolled: this runs inside the tile loop, where registers are scarce.
 #pragma unroll 1
         for (int w = 0; w < nw; ++w) v += part[buf][w * kPartWave + i];
-        float* yp = p.y + static_cast<long long>(slot) * p.ystride + row;
-        if (!moe && row < p.dual) yp[p.m] = epilogue(v, p.flags, p.alpha, p.bias + p.m + row, yp + p.m);
+        float* yp = p.y + static_cast<long long>(slot) * p.m + row;
         if (!moe) v = epilogue(v, p.flags, p.alpha, p.bias + row, yp);
         *yp = v;
       }

@@ -368,8 +368,7 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
 #pragma unroll
             for (int w = 0; w < MAXW; ++w)
               if (w < nw) v += part[i * MAXW + w];
-            float* yp = p.y + static_cast<long long>(st_slot) * p.ystride + row;
-            if (!moe && row < p.dual) yp[p.m] = epilogue(v, p.flags, p.alpha, p.bias + p.m + row, yp + p.m);
+            float* yp = p.y + static_cast<long long>(st_slot) * p.m + row;
             if (!moe) v = epilogue(v, p.flags, p.alpha, p.bias + row, yp);
             *yp = v;
           }
