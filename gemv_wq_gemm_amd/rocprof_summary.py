@@ -3,9 +3,14 @@
     python -m gemv_wq_gemm_amd.rocprof_summary trace STATS_CSV OUT_MD --command CMD [--top N]
     python -m gemv_wq_gemm_amd.rocprof_summary counters FETCH_CSV WRITE_CSV OUT_MD --command CMD \\
         --kernel LABEL=SUBSTRING [...] --copy SUBSTRING --copy-bytes N
+    python -m gemv_wq_gemm_amd.rocprof_summary pmc OUT_MD CSV [CSV ...] --command CMD --title T \\
+        --kernel LABEL=SUBSTRING [...]
 
 ``trace`` condenses a ``--kernel-trace --stats`` kernel statistics file into a table of
 per-kernel call counts and durations.
+
+``pmc`` tabulates the mean per dispatch of every counter in one or more ``--pmc`` runs
+for the labelled kernels.
 
 ``counters`` condenses two ``--pmc FETCH_SIZE`` / ``--pmc WRITE_SIZE`` runs of the same
 command into HBM bytes per launch for the kernels named by ``--kernel``. The raw
@@ -118,6 +123,34 @@ def counter_summary(fetch_csv: str, write_csv: str, command: str, out: str, kern
     return text
 
 
+def pmc_summary(csvs: list[str], command: str, out: str, kernels: dict[str, str], title: str) -> str:
+    """Mean per dispatch of every counter in the ``--pmc`` CSVs, for the labelled kernels."""
+    names: list[str] = []
+    values: dict[str, dict[str, float]] = {}
+    for path in csvs:
+        rows = list(csv.DictReader(open(path)))
+        for counter in dict.fromkeys(r["Counter_Name"] for r in rows):
+            if counter not in names:
+                names.append(counter)
+            acc: dict[str, list[float]] = defaultdict(list)
+            for r in rows:
+                if r["Counter_Name"] == counter:
+                    acc[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+            for label, sub in kernels.items():
+                _, vals = _pick(acc, sub)
+                values.setdefault(label, {})[counter] = sum(vals) / len(vals)
+    lines = [f"# {title}", "", f"Command (one run per pass): `{command}`", "",
+             "Mean per dispatch. " + ", ".join(names) + ".", "",
+             "| label | kernel | " + " | ".join(names) + " |", "|---|---|" + "---:|" * len(names)]
+    for label, sub in kernels.items():
+        lines.append(f"| {label} | `{_short(sub, 60)}` | " +
+                     " | ".join(f"{values[label][c]:.4g}" for c in names) + " |")
+    text = "\n".join(lines) + "\n"
+    with open(out, "w") as fh:
+        fh.write(text)
+    return text
+
+
 def read_traffic(path: str, label: str) -> float | None:
     """Bytes per launch recorded for ``label``, or None if absent or the kernel sources changed."""
     if not os.path.exists(path):
@@ -150,9 +183,17 @@ def main() -> None:
     c.add_argument("--kernel", action="append", required=True, help="LABEL=SUBSTRING of the kernel name")
     c.add_argument("--copy", required=True, help="substring of the calibration copy kernel's name")
     c.add_argument("--copy-bytes", type=int, required=True)
+    q = sub.add_parser("pmc")
+    q.add_argument("out")
+    q.add_argument("csvs", nargs="+")
+    q.add_argument("--command", required=True)
+    q.add_argument("--title", required=True)
+    q.add_argument("--kernel", action="append", required=True, help="LABEL=SUBSTRING of the kernel name")
     a = ap.parse_args()
     if a.what == "trace":
         print(trace_summary(a.stats_csv, a.command, a.out, a.top))
+    elif a.what == "pmc":
+        print(pmc_summary(a.csvs, a.command, a.out, dict(kv.split("=", 1) for kv in a.kernel), a.title))
     else:
         kernels = dict(kv.split("=", 1) for kv in a.kernel)
         print(counter_summary(a.fetch_csv, a.write_csv, a.command, a.out, kernels, a.copy, a.copy_bytes))
