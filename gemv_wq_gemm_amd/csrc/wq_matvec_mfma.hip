@@ -15,8 +15,8 @@
 //    x2 = bf16(x - x1), x3 = bf16(x - x1 - x2), all rounded to nearest even. Both differences are
 //    exact in f32, and the last part holds the at most 8 bits left, so the three parts add up to x
 //    exactly (outside the bottom of the exponent range).
-//  * The integer quants q (Q8_0) and q - 8 (Q4_0, taken as (q - 8) / 16 and scaled by 16 d) are
-//    exact in bf16, and products of two bf16 values are exact in f32.
+//  * The integer quants q (Q8_0) and q - 8 (Q4_0, taken as (q - 8) / 16 against activations
+//    times 16) are exact in bf16, and products of two bf16 values are exact in f32.
 //  * One 32-element block is one MFMA's k: three chained MFMAs (one per activation part, sharing
 //    the decoded weights) sum the block's products into a fresh 16x16 f32 tile, which the block's
 //    scale then multiplies and adds to the running sum in f32. So only f32 additions round: the
@@ -30,8 +30,9 @@
 //    types, on the MoE workload and on the plain layer at 12 and 16 tokens). Q8_0 tiles are
 //    twice as large, so its 16 waves keep a single buffer of partial sums (PB = 1). MFMA roles: A = activations (16 slots x 32 k), B = weights (32 k x 16 weight
 //    rows), D[t][j] in lane 16 (t / 4) + j, value t % 4.
-//  * Lane l = 16 o + j: weight row j of the tile and k-octet o of each block (elements 8o..8o+7);
-//    as A it holds slot j at the same octet. Its three activation parts for the SB blocks of its
+//  * Lane l = 16 o + j: weight row j of the tile and k-octet o of each block (Q8_0: elements
+//    8o..8o+7; Q4_0: 4o..4o+3 and 16+4o..16+4o+3, see decode_octet); as A it holds slot j at the
+//    same octet. Its three activation parts for the SB blocks of its
 //    slice (12 SB VGPRs) are built once per group of slots and reused for every tile.
 //  * A tile is 16 consecutive weight rows, streamed by the workgroup into a ring of NSTAGE LDS
 //    slots with direct-to-LDS loads (each wave a share of the rows, 1024 bytes per load, the last
@@ -76,15 +77,33 @@ __device__ __forceinline__ float q4_byte(uint32_t word, int b) {
 
 // The 8 weights of k-octet o of block BLK of this lane's row slice, as MFMA B operand, and the
 // factor that scales their products. `q_base` (4-byte aligned) is the LDS byte offset of the
-// slice's first block plus the lane's quant offset (8 o for Q8_0, 8 (o & 1) for Q4_0); `s_base`
-// is the slice's first block. Every other offset is a compile-time constant.
+// slice's first block plus the lane's quant offset (8 o for Q8_0, 4 o for Q4_0); `s_base` is the
+// slice's first block. Every other offset is a compile-time constant.
+//  * Q8_0: octet o is elements 8o .. 8o+7 (quant bytes 8o .. 8o+7).
+//  * Q4_0: octet o is elements 4o .. 4o+3 and 16+4o .. 16+4o+3: the low and high nibbles of quant
+//    bytes 4o .. 4o+3, one dword. The MFMA sums over k in any order, so the activations (A) take
+//    the same order; this layout needs one quant dword, XOR and shift per block instead of two.
 template <int WT, int BLK>
-__device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int q_base, int s_base, int o, float& scale) {
+__device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int q_base, int s_base, float& scale) {
   constexpr int BB = block_bytes(WT);
   constexpr int kQ = BLK * BB + 2;  // first quant byte of the block, from an aligned base
   constexpr int kSh = kQ & 3;       // 0 or 2
   const float d = f16_to_f32(*reinterpret_cast<const uint16_t*>(lds + s_base + BLK * BB));
   const uint32_t* a = reinterpret_cast<const uint32_t*>(lds + q_base) + (kQ >> 2);
+  uint4 u;
+  if constexpr (WT == kQ4_0) {
+    const uint32_t q = kSh == 0 ? a[0] : realign(a[1], a[0], kSh);
+    const uint32_t lo = q ^ 0x88888888u;  // nibbles of elements 4o .. 4o+3 in the low halves
+    // And of 16+4o .. 16+4o+3, by a rotate the compiler keeps (a plain shift would be folded into
+    // each byte extract, which then loses its byte select).
+    const uint32_t hi = __builtin_amdgcn_alignbit(lo, lo, 4);
+    u.x = bf16_pair(q4_byte(lo, 0), q4_byte(lo, 1));
+    u.y = bf16_pair(q4_byte(lo, 2), q4_byte(lo, 3));
+    u.z = bf16_pair(q4_byte(hi, 0), q4_byte(hi, 1));
+    u.w = bf16_pair(q4_byte(hi, 2), q4_byte(hi, 3));
+    scale = d;  // (q - 8) / 16 here; the activations enter times 16 (exact)
+    return __builtin_bit_cast(bf16x8, u);
+  }
   uint32_t q0, q1;
   if constexpr (kSh == 0) {
     q0 = a[0];
@@ -94,23 +113,11 @@ __device__ __forceinline__ bf16x8 decode_octet(const uint8_t* lds, int q_base, i
     q0 = realign(d1, d0, kSh);
     q1 = realign(d2, d1, kSh);
   }
-  uint4 u;
-  if constexpr (WT == kQ8_0) {
-    u.x = bf16_pair(q8_at(q0, 0), q8_at(q0, 1));
-    u.y = bf16_pair(q8_at(q0, 2), q8_at(q0, 3));
-    u.z = bf16_pair(q8_at(q1, 0), q8_at(q1, 1));
-    u.w = bf16_pair(q8_at(q1, 2), q8_at(q1, 3));
-    scale = d;
-  } else {
-    // Octets 0, 1 are the low nibbles of bytes 0-7, 8-15; octets 2, 3 their high nibbles.
-    const uint32_t s4 = 4u * static_cast<uint32_t>(o >> 1);
-    const uint32_t x0 = (q0 ^ 0x88888888u) >> s4, x1 = (q1 ^ 0x88888888u) >> s4;
-    u.x = bf16_pair(q4_byte(x0, 0), q4_byte(x0, 1));
-    u.y = bf16_pair(q4_byte(x0, 2), q4_byte(x0, 3));
-    u.z = bf16_pair(q4_byte(x1, 0), q4_byte(x1, 1));
-    u.w = bf16_pair(q4_byte(x1, 2), q4_byte(x1, 3));
-    scale = 16.f * d;
-  }
+  u.x = bf16_pair(q8_at(q0, 0), q8_at(q0, 1));
+  u.y = bf16_pair(q8_at(q0, 2), q8_at(q0, 3));
+  u.z = bf16_pair(q8_at(q1, 0), q8_at(q1, 1));
+  u.w = bf16_pair(q8_at(q1, 2), q8_at(q1, 3));
+  scale = d;
   return __builtin_bit_cast(bf16x8, u);
 }
 
@@ -209,7 +216,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
   const int j = lane & 15;  // weight row in the tile (B, D column); slot as A
   const int o = lane >> 4;  // k-octet of each block; D rows 4o .. 4o+3
   const int s_off = j * stride + wave * kSliceBlocks * BB;         // the lane's row slice
-  const int q_off = s_off + (WT == kQ8_0 ? 8 * o : 8 * (o & 1));  // and its quant octet
+  const int q_off = s_off + (WT == kQ8_0 ? 8 * o : 4 * o);  // and its quant bytes
 
   // Finishes tile `tile` from the wave partials in part[buf]: the k-slices of all waves, added in
   // wave order.
@@ -272,13 +279,21 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         for (int bb = 0; bb < kSliceBlocks; ++bb) {
           float xv[8];
           if (xs) {
-            const float4* xp = reinterpret_cast<const float4*>(xs + wave * (32 * kSliceBlocks) + bb * 32 + 8 * o);
-            const float4 v0 = xp[0], v1 = xp[1];
+            // The k order of decode_octet: Q8_0 elements 8o .. 8o+7, Q4_0 4o .. 4o+3 and 16+4o .. 16+4o+3.
+            const float* xb = xs + wave * (32 * kSliceBlocks) + bb * 32;
+            const float4 v0 = *reinterpret_cast<const float4*>(xb + (WT == kQ8_0 ? 8 * o : 4 * o));
+            const float4 v1 = *reinterpret_cast<const float4*>(xb + (WT == kQ8_0 ? 8 * o + 4 : 16 + 4 * o));
             xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
             xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
           } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) xv[i] = 0.f;
+          }
+          if constexpr (WT == kQ4_0) {
+            // Q4_0 weights enter as (q - 8) / 16: the activations take the 16, a power of two, so
+            // the parts stay exact and each block's scale is d itself.
+#pragma unroll
+            for (int i = 0; i < 8; ++i) xv[i] *= 16.f;
           }
           split3(xv, xa[0][bb], xa[1][bb], xa[2][bb]);
           // Load and split a few blocks at a time: hoisting every load first runs out of registers.
@@ -301,7 +316,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         static_for<0, kSliceBlocks>([&](auto bb) {
           constexpr int B = decltype(bb)::value;
           float scale;
-          const bf16x8 wb = decode_octet<WT, B>(ring, slot_base + q_off, slot_base + s_off, o, scale);
+          const bf16x8 wb = decode_octet<WT, B>(ring, slot_base + q_off, slot_base + s_off, scale);
           f32x4 blk = {0.f, 0.f, 0.f, 0.f};
           blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][B], wb, blk, 0, 0, 0);
           blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][B], wb, blk, 0, 0, 0);
