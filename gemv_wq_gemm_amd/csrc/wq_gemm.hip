@@ -124,10 +124,14 @@ struct GemmCfg {
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 fragments");
 };
 
+// One step's quantized blocks as loaded: the NW + 1 aligned dwords that cover each block and
+// where in the first one it starts (byte 0 or 2). Scale and quants are pulled out only when the
+// step is written to LDS, so nothing waits on these loads until then: the step's MFMAs and
+// scaling run while they are in flight.
 template <int WT, int NQ>
 struct QStage {
-  uint32_t q[NQ][BlockWords<WT>::NW];
-  uint32_t s[NQ];
+  uint32_t d[NQ][BlockWords<WT>::NW + 1];
+  uint32_t sh[NQ];
   bool ok[NQ];
 };
 
@@ -212,10 +216,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
         const int blk = s * 2 + (e & 1);
         const bool ok = e < BN * 2 && m0 + rr < p.m && blk * 32 < p.k;
         wsq.ok[i] = ok;
-        if (ok)
-          read_block<WT>(reinterpret_cast<const uint32_t*>(p.w),
-                         static_cast<long long>(m0 + rr) * p.rowbytes + static_cast<long long>(blk) * block_bytes(WT),
-                         wsq.q[i], &wsq.s[i]);
+        if (ok) {
+          const long long off =
+              static_cast<long long>(m0 + rr) * p.rowbytes + static_cast<long long>(blk) * block_bytes(WT);
+          const uint32_t* a = reinterpret_cast<const uint32_t*>(p.w) + (off >> 2);
+#pragma unroll
+          for (int j = 0; j <= BlockWords<WT>::NW; ++j) wsq.d[i][j] = a[j];
+          wsq.sh[i] = static_cast<uint32_t>(off) & 3u;
+        }
       }
     }
   };
@@ -271,8 +279,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
           const int half = e & 1;
           uint32_t o[16];
           if (wsq.ok[i]) {
-            quants_to_bf16<WT>(wsq.q[i], o);
-            sS[buf][rr * 2 + half] = f16_to_f32(wsq.s[i]);
+            // The f16 scale, then the quants from 2 bytes further on (as read_block does).
+            constexpr int NW = BlockWords<WT>::NW;
+            const uint32_t sh = wsq.sh[i];
+            uint32_t q[NW];
+#pragma unroll
+            for (int j = 0; j < NW; ++j) q[j] = sh ? wsq.d[i][j + 1] : realign(wsq.d[i][j + 1], wsq.d[i][j], 2u);
+            quants_to_bf16<WT>(q, o);
+            sS[buf][rr * 2 + half] = f16_to_f32((sh ? (wsq.d[i][0] >> 16) : wsq.d[i][0]) & 0xFFFFu);
           } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) o[j] = 0u;
