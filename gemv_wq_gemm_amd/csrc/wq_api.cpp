@@ -69,11 +69,13 @@ struct Workspace {
 std::mutex g_ws_mu;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
+// The caller holds g_ws_mu until the work that uses the buffer is queued: another thread that
+// grows the same (device, stream) buffer then waits for that work before freeing it, instead of
+// freeing it between this call's lookup and its launches.
 int workspace(hipStream_t stream, size_t bytes, void** out) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  std::lock_guard<std::mutex> lock(g_ws_mu);
   Workspace& w = g_ws[{dev, stream}];
   if (w.bytes < bytes) {
     if (w.ptr) {
@@ -240,7 +242,9 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* slots = y;
+  std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);  // held through the launches
   if (gate_w) {
+    ws_lock.lock();
     void* ws = nullptr;
     if (int r = workspace(s, static_cast<size_t>(n_slots * m * 4), &ws)) return r;
     slots = static_cast<float*>(ws);

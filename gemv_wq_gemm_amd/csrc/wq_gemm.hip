@@ -37,6 +37,7 @@
 //    f32 atomics; the first one adds the bias.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdlib>
 #include <type_traits>
 
@@ -661,15 +662,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 }
 
 int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];  // filled on first use; concurrent callers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 constexpr int kLdsBytes = 160 * 1024;

@@ -47,6 +47,7 @@
 //    slots whose id is out of range.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <type_traits>
 
 #include "wq_decode.hpp"
@@ -340,15 +341,15 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
 }
 
 int mfma_device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];  // filled on first use; concurrent callers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 template <int WT, int NSTAGE, int SB, int PB>
@@ -357,11 +358,12 @@ hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
   const int nw = p.k / (32 * SB);
   const int ntiles = (p.m + kTileRows - 1) / kTileRows;
   auto kernel = matvec_mfma_kernel<WT, NSTAGE, SB, PB>;
-  static int per_cu = 0;
+  static std::atomic<int> per_cu_cache{0};  // filled on first use, as device_cus
+  int per_cu = per_cu_cache.load(std::memory_order_relaxed);
   if (per_cu <= 0) {
-    int v = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, 64 * kMaxWaves, 0) != hipSuccess || v <= 0) v = 1;
-    per_cu = v;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 64 * kMaxWaves, 0) != hipSuccess || per_cu <= 0)
+      per_cu = 1;
+    per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
   // As many workgroups as are resident at once, split over the experts.
   int groups = per_cu * mfma_device_cus() / p.n_exp;

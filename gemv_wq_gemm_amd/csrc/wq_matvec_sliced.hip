@@ -42,6 +42,8 @@
 //    additions per output -- far inside 1e-5 * sum |x w|.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
 #include "wq_lds_dma.hpp"
@@ -380,26 +382,26 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
 }
 
 int device_cus() {
-  static int cus[64];
+  static std::atomic<int> cus[64];  // filled on first use; concurrent callers store the same value
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] <= 0) {
-    int v = 0;
+  int v = cus[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
-    cus[dev] = v;
+    cus[dev].store(v, std::memory_order_relaxed);
   }
-  return cus[dev];
+  return v;
 }
 
 // Workgroups of `kernel` that fit on one CU at once; `cache` is the caller's
 // per-variant slot (filled on first use).
-int groups_per_cu(void (*kernel)(MatvecParams, int), int threads, int* cache) {
-  if (*cache <= 0) {
-    int v = 0;
+int groups_per_cu(void (*kernel)(MatvecParams, int), int threads, std::atomic<int>* cache) {
+  int v = cache->load(std::memory_order_relaxed);
+  if (v <= 0) {
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&v, kernel, threads, 0) != hipSuccess || v <= 0) v = 1;
-    *cache = v;
+    cache->store(v, std::memory_order_relaxed);
   }
-  return *cache;
+  return v;
 }
 
 template <int WT, int NTC, int R, int NSTAGE, int MAXW, int SLICE>
@@ -411,7 +413,7 @@ hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   // As many workgroups as are resident at once (no thin second round), split over the
   // experts; each walks a run of tiles with NSTAGE-1 of them in flight.
   const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
-  static int per_cu[17];  // per variant and wave count
+  static std::atomic<int> per_cu[17];  // per variant and wave count
   int groups = groups_per_cu(kernel, 64 * nw, &per_cu[nw]) * device_cus() / experts;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;

@@ -28,7 +28,10 @@
  *     synchronization, as for any HIP kernel.
  *   - The library allocates device memory only for the MoE gate combine
  *     (a per-device, per-stream workspace, grown on demand and kept until
- *     the process ends).
+ *     the process ends). Growing it is the one place a call waits: for the
+ *     work already queued on that stream, which may still read the old one.
+ *   - Every entry point may be called from several host threads at once, on
+ *     the same stream or on different ones.
  */
 #ifndef WQ_H
 #define WQ_H
