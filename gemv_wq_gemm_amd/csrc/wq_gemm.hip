@@ -759,7 +759,12 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
       if (wide_tiles >= cus) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
       if (small_tiles > 2LL * cus && tall_tiles <= 2LL * cus) return launch_bf16<64, 192, 2, 2, 2, 64>(p, stream);
       if (small_tiles > cus) return launch_bf16<64, 128, 2, 4, 2, 64>(p, stream);
-      if (small_tiles <= cus / 2 || p.k <= 1024) return launch_bf16<64, 64, 2, 2, 3, 64>(p, stream);
+      if (small_tiles <= cus / 2 || p.k <= 1024) {
+        // At most four k steps: a 2-slot ring (64 x 256 x 256 + bias + GELU 5.4 -> 5.0 us). At
+        // k = 1024 it is slower than 3 slots (the 24-layer chain 2.68 -> 2.72 ms).
+        if (p.k <= 256) return launch_bf16<64, 64, 2, 2, 2, 64>(p, stream);
+        return launch_bf16<64, 64, 2, 2, 3, 64>(p, stream);
+      }
       return launch_bf16<64, 128, 2, 4, 4, 64>(p, stream);
     }
     // k an odd multiple of 32 (k step 32): measured at n = 1500, 128 x 256 tiles win once they
