@@ -39,6 +39,11 @@ int hip_fail(hipError_t e, const char* what) {
 void clear_error() { g_err[0] = '\0'; }
 
 constexpr int64_t kIntMax = 0x7fffffff;
+// Row counts the kernels round up to whole tiles (at most 256 rows) in 32-bit ints.
+constexpr int64_t kMaxRows = kIntMax - 512;
+// Elements of an output: tile counts (64 x 64 and larger tiles) then fit in 28 bits, so the
+// GEMM's grid of tile numbers fits in an int. 2^40 floats are 4 TiB, beyond any device.
+constexpr int64_t kMaxOutputs = int64_t(1) << 40;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -111,9 +116,10 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     return fail(WQ_ERR_SHAPE, "unknown path %d", path);
   if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size n = %lld, m = %lld", (long long)n, (long long)m);
   if (int r = check_k(k)) return r;
-  if (n > kIntMax || m > kIntMax) return fail(WQ_ERR_SHAPE, "n or m exceeds 2^31 - 1");
+  if (n > kMaxRows || m > kMaxRows) return fail(WQ_ERR_SHAPE, "n or m exceeds 2^31 - 513");
   if (dual < 0 || dual > m) return fail(WQ_ERR_SHAPE, "dual must be in [0, m], got %lld", (long long)dual);
-  if (m + dual > kIntMax) return fail(WQ_ERR_SHAPE, "m + dual exceeds 2^31 - 1");
+  if (m + dual > kMaxRows) return fail(WQ_ERR_SHAPE, "m + dual exceeds 2^31 - 513");
+  if (n > 0 && (m + dual) > kMaxOutputs / n) return fail(WQ_ERR_SHAPE, "n * (m + dual) exceeds 2^40");
   if (path == WQ_PATH_AUTO) path = n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
   if (path == WQ_PATH_MATVEC && n > WQ_MATVEC_MAX_N)
     return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
@@ -121,9 +127,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     return fail(WQ_ERR_SHAPE, "n = %lld exceeds the GEMM grid (65535 x 128 rows)", (long long)n);
   if (n == 0 || m == 0) return WQ_OK;
   if (!x || !w || !y) return fail(WQ_ERR_NULL, "x, w and y must not be NULL");
-  if (!aligned(x, 16) || !aligned(w, 16) || !aligned(y, 16))
-    return fail(WQ_ERR_ALIGN, "x, w and y must be 16-byte aligned");
-  if (bias && !aligned(bias, 4)) return fail(WQ_ERR_ALIGN, "bias must be 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(w, 16)) return fail(WQ_ERR_ALIGN, "x and w must be 16-byte aligned");
+  if (!aligned(y, 4) || (bias && !aligned(bias, 4))) return fail(WQ_ERR_ALIGN, "y and bias must be 4-byte aligned");
   const int64_t wbytes = wq_weight_bytes(wtype, m, k);
   const int64_t ybytes = n * (m + dual) * 4;
   if (overlap(y, ybytes, x, n * k * 4) || overlap(y, ybytes, w, wbytes) || overlap(y, ybytes, bias, (m + dual) * 4))
@@ -225,14 +230,15 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
   if (n_experts < 1 || n_experts > 65534) return fail(WQ_ERR_SHAPE, "n_experts must be in [1, 65534]");
   if (top_k < 1 || top_k > n_experts) return fail(WQ_ERR_SHAPE, "top_k must be in [1, n_experts]");
   if (int r = check_k(k)) return r;
-  if (m > kIntMax) return fail(WQ_ERR_SHAPE, "m exceeds 2^31 - 1");
+  if (m > kMaxRows) return fail(WQ_ERR_SHAPE, "m exceeds 2^31 - 513");
   if (n_tok * top_k > 4096) return fail(WQ_ERR_SHAPE, "n_tok * top_k must be <= 4096");
+  if (n_tok * top_k * m > kMaxOutputs) return fail(WQ_ERR_SHAPE, "n_tok * top_k * m exceeds 2^40");
   if (n_tok == 0 || m == 0) return WQ_OK;
   if (!x || !w_experts || !expert_ids || !y) return fail(WQ_ERR_NULL, "x, w_experts, expert_ids and y must not be NULL");
-  if (!aligned(x, 16) || !aligned(w_experts, 16) || !aligned(y, 16))
-    return fail(WQ_ERR_ALIGN, "x, w_experts and y must be 16-byte aligned");
-  if (!aligned(expert_ids, 4) || (gate_w && !aligned(gate_w, 4)))
-    return fail(WQ_ERR_ALIGN, "expert_ids and gate_w must be 4-byte aligned");
+  if (!aligned(x, 16) || !aligned(w_experts, 16))
+    return fail(WQ_ERR_ALIGN, "x and w_experts must be 16-byte aligned");
+  if (!aligned(y, 4) || !aligned(expert_ids, 4) || (gate_w && !aligned(gate_w, 4)))
+    return fail(WQ_ERR_ALIGN, "y, expert_ids and gate_w must be 4-byte aligned");
   const int64_t n_slots = n_tok * top_k;
   const int64_t ebytes = wq_weight_bytes(wtype, m, k);
   const int64_t ybytes = (gate_w ? n_tok : n_slots) * m * 4;
@@ -284,7 +290,7 @@ int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, vo
   if (int r = check_wtype(wtype)) return r;
   if (m < 0) return fail(WQ_ERR_SHAPE, "negative m");
   if (int r = check_k(k)) return r;
-  if (m > kIntMax || m * (k / 32) > kIntMax * 128LL) return fail(WQ_ERR_SHAPE, "m * k too large");
+  if (m > kMaxRows || m * (k / 32) > kIntMax * 128LL) return fail(WQ_ERR_SHAPE, "m * k too large");
   if (m == 0) return WQ_OK;
   if (!w || !out) return fail(WQ_ERR_NULL, "w and out must not be NULL");
   if (!aligned(w, 16) || !aligned(out, 16)) return fail(WQ_ERR_ALIGN, "w and out must be 16-byte aligned");

@@ -292,18 +292,22 @@ hipError_t launch_wt(const MatvecParams& p, int max_tok, int n_exp_rows, hipStre
 }
 
 // ---- MoE gate combine ----------------------------------------------------------------------
+// A grid-stride loop over the n_tok * m outputs (the grid is capped, so its size stays in range
+// for any output size).
 __global__ __launch_bounds__(256) void moe_combine_kernel(const float* slots, const float* gates,
                                                           float* y, int n_tok, int top_k, int m) {
-  const long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= static_cast<long long>(n_tok) * m) return;
-  const int t = static_cast<int>(i / m);
-  const int j = static_cast<int>(i - static_cast<long long>(t) * m);
-  float v = 0.f;
-  for (int s = 0; s < top_k; ++s) {
-    const long long slot = static_cast<long long>(t) * top_k + s;
-    v = __builtin_fmaf(gates[slot], slots[slot * m + j], v);
+  const long long total = static_cast<long long>(n_tok) * m;
+  for (long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * 256) {
+    const int t = static_cast<int>(i / m);
+    const int j = static_cast<int>(i - static_cast<long long>(t) * m);
+    float v = 0.f;
+    for (int s = 0; s < top_k; ++s) {
+      const long long slot = static_cast<long long>(t) * top_k + s;
+      v = __builtin_fmaf(gates[slot], slots[slot * m + j], v);
+    }
+    y[i] = v;
   }
-  y[i] = v;
 }
 
 // ---- exact dequantization (test hook) --------------------------------------------------------
@@ -374,7 +378,8 @@ hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStrea
 hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, int n_tok, int top_k,
                               int m, hipStream_t stream) {
   const long long total = static_cast<long long>(n_tok) * m;
-  const unsigned blocks = static_cast<unsigned>((total + 255) / 256);
+  const long long want = (total + 255) / 256;
+  const unsigned blocks = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
   hipLaunchKernelGGL(moe_combine_kernel, dim3(blocks), dim3(256), 0, stream, slots, gates, y, n_tok,
                      top_k, m);
   return hipGetLastError();

@@ -47,6 +47,7 @@
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
 #include "wq_lds_dma.hpp"
+#include "wq_tile_math.hpp"
 
 namespace wq {
 namespace {
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
     const int row0 = tile * R;
     const uint8_t* base = wexp + static_cast<long long>(row0) * p.rowbytes;
     // Bytes past the end of W (last tile) re-read W's last 16 bytes; never stored.
-    const int last = min(tile_bytes, (p.m - row0) * rowbytes) - 16;
+    const int last = tile_last_load(tile_bytes, p.m, row0, p.rowbytes);
     const uint32_t dst = ring_addr + static_cast<uint32_t>((tile % NSTAGE) * kSlotBytes);
     for (int i = ld0; i < ld1; ++i)
       load_lds16<true>(base, static_cast<uint32_t>(min(i * 1024 + lane * 16, last)), dst + i * 1024);

@@ -28,10 +28,28 @@
  *     synchronization, as for any HIP kernel.
  *   - The library allocates device memory only for the MoE gate combine
  *     (a per-device, per-stream workspace, grown on demand and kept until
- *     the process ends). Growing it is the one place a call waits: for the
- *     work already queued on that stream, which may still read the old one.
+ *     the process ends). Growing it is the one place a call waits and
+ *     allocates: it synchronizes the stream (work already queued there may
+ *     still read the old buffer), frees that buffer and calls hipMalloc. A
+ *     gated wq_moe_matvec call that grows the workspace therefore cannot be
+ *     captured into a HIP graph; make one uncaptured call of the largest size
+ *     first.
  *   - Every entry point may be called from several host threads at once, on
  *     the same stream or on different ones.
+ *   - Alignment: x and w must be 16-byte aligned (the kernels move them with
+ *     16-byte vector loads and 16-byte direct-to-LDS loads); y, bias, the
+ *     MoE ids and gates need only 4 bytes (they are read and written one f32
+ *     or int32 at a time), so y may start at any element of a larger buffer.
+ *   - Sizes: n, m (and m + dual) at most 2^31 - 513 and n * (m + dual) at
+ *     most 2^40, so that every tile and grid count the kernels form fits in
+ *     32 bits. Byte offsets into W are 64-bit (a weight may pass 2 GiB).
+ *   - Determinism: every route sums in a fixed order and gives bit-identical
+ *     results run to run, except one: the quantized, f16 and f32 weight
+ *     types on the matrix cores, when the output has too few tiles to fill
+ *     the chip and the epilogue is WQ_RESIDUAL with no activation. That call
+ *     splits k across workgroups that add their partial sums into Y with f32
+ *     atomics, so the order of those additions (and the last bits of Y) may
+ *     differ between runs. bf16 weights never take it.
  */
 #ifndef WQ_H
 #define WQ_H
@@ -118,7 +136,7 @@ extern "C" {
 #define WQ_ERR_WTYPE (-3)  /* unknown weight type */
 #define WQ_ERR_FLAGS (-4)  /* unknown flag bits, two activations, WQ_BIAS without a bias (or a bias
                               without WQ_BIAS), or a non-finite alpha */
-#define WQ_ERR_ALIGN (-5)  /* x, w or y not 16-byte aligned; bias, ids or gates not 4-byte aligned */
+#define WQ_ERR_ALIGN (-5)  /* x or w not 16-byte aligned; y, bias, ids or gates not 4-byte aligned */
 #define WQ_ERR_ALIAS (-6)  /* y overlaps x, w, bias, ids or gates */
 #define WQ_ERR_HIP (-7)    /* a HIP call failed (launch, allocation, device query) */
 
@@ -126,8 +144,9 @@ extern "C" {
  * wq_gemm: Y = epilogue(X . W^T + bias) on `stream`, path chosen by n.
  *   x     f32 [n][k], 16-byte aligned.
  *   w     weight [m][k] in `wtype` storage (wq_weight_bytes bytes), 16-byte aligned.
- *   bias  f32 [m] when flags & WQ_BIAS, else NULL.
- *   y     f32 [n][m], 16-byte aligned; read first when flags & WQ_RESIDUAL.
+ *   bias  f32 [m] when flags & WQ_BIAS, else NULL; 4-byte aligned.
+ *   y     f32 [n][m], 4-byte aligned (wavo's `Pass::gemv` writes its output from an offset into
+ *         a larger buffer); read first when flags & WQ_RESIDUAL.
  *   n, m  >= 0 (n == 0 or m == 0: nothing to do, WQ_OK); k > 0, k % 32 == 0.
  * Returns WQ_OK or a WQ_ERR_* code.
  */
@@ -167,7 +186,9 @@ int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, 
 
 /*
  * wq_moe_matvec: the MoE matvec of hanzo-ml `moe_matvec_gpu`, expert-major.
- *   x          f32 [n_tok][k], 16-byte aligned.
+ *   x          f32 [n_tok][k], 16-byte aligned. Every routed slot of token t reads row t
+ *              (one activation row per token, shared by its top_k slots); hanzo-ml's page
+ *              gives x per routed slot, which is this with top_k = 1 or with the rows repeated.
  *   w_experts  one bank of n_experts weights, expert e at byte offset
  *              e * wq_weight_bytes(wtype, m, k); 16-byte aligned.
  *   expert_ids int32 [n_tok][top_k]: expert of slot s = t*top_k + j.
@@ -175,10 +196,14 @@ int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, 
  *              the ids live on the device). A slot with an id outside that
  *              range is never read from the bank; its output is NaN.
  *   gate_w     f32 [n_tok][top_k] or NULL.
- *   y          gate_w == NULL: f32 [n_tok*top_k][m], y[s] = W[ids[s]] . x[t].
+ *   y          4-byte aligned.
+ *              gate_w == NULL: f32 [n_tok*top_k][m], y[s] = W[ids[s]] . x[t].
  *              gate_w != NULL: f32 [n_tok][m], y[t] = sum_j gate_w[t][j] * W[ids[t][j]] . x[t],
  *              summed in j order.
- *   1 <= top_k <= n_experts; n_tok*top_k <= 4096; k % 32 == 0.
+ *   1 <= top_k <= n_experts <= 65534; n_tok*top_k <= 4096 (every workgroup scans all routed
+ *   slots' ids; callers with more slots split the call); k % 32 == 0.
+ * With gate_w, the per-slot products go to the library's workspace first (see the workspace
+ * note at the top), then the combine sums them per token.
  * Each expert's weights are streamed once per call for all tokens routed to
  * it; all arithmetic is f32 (the WQ_PATH_MATVEC bound per slot).
  */
@@ -189,20 +214,30 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
 /*
  * wq_dequantize: out[m][k] = the exact f32 value of every weight (bf16: the
  * upper-half bit pattern; Q8_0: d*q; Q4_0: d*(q-8); f32 as stored; f16
- * widened; all exact in f32).
- *   w    weight in `wtype` storage, 16-byte aligned; out f32 [m][k], 16-byte aligned.
+ * widened; all exact in f32) -- the per-type unpacking of the formats above
+ * (cortiq-engine `ae_gemm`'s weight pairs, wavo `Gpu::upload_linear`, hanzo-ml
+ * `upload_qweight`), written out in full so it can be compared bit for bit.
+ *   w    weight in `wtype` storage, 16-byte aligned; out f32 [m][k], 16-byte aligned
+ *        (written with 16-byte stores).
  */
 int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream);
 
 /* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32); f32 4*m*k; f16 2*m*k;
- * -1 for an unknown type, negative sizes or k % 32 != 0. */
+ * -1 for an unknown type, negative sizes or k % 32 != 0. The block sizes are those of the formats
+ * above (wavo `Gpu::upload_linear` sizes a Q8_0 row as k/32 blocks of 34 bytes; hanzo-ml
+ * `matvec_q4_0_gpu` / `matvec_q8_0_gpu` refuse a buffer shorter than the blocks of nout rows). */
 int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k);
 
 /* The path wq_gemm takes for these sizes: WQ_PATH_MATVEC or WQ_PATH_MFMA
- * (negative WQ_ERR_* for invalid sizes or type). */
+ * (negative WQ_ERR_* for invalid sizes or type). The pages put the split between
+ * a matrix path for many rows of X (cortiq-engine `ae_gemm`, wavo `Pass::gemm`) and
+ * a vector path for a few (wavo `Pass::gemv`, hanzo-ml `matvec_*_gpu`) without a
+ * number; the reading taken is n <= 16 (WQ_MATVEC_MAX_N) on the f32 matvec. */
 int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype);
 
-/* Message of the last failed call on this thread ("" when none). */
+/* Message of the last failed call on this thread ("" when none): the text of the
+ * checks above, in the manner of the messages hanzo-ml's host functions return
+ * on a refused call (`bail!` with the offending sizes). */
 const char* wq_last_error(void);
 
 /* Library version string. */

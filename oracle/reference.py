@@ -144,13 +144,6 @@ def decode_q4_0(raw: np.ndarray, m: int, k: int) -> np.ndarray:
     return (d[:, :, None] * (q - 8.0)).reshape(m, k)
 
 
-def decode_bf16(raw: np.ndarray, m: int, k: int) -> np.ndarray:
-    a = np.ascontiguousarray(raw).view(np.uint16).reshape(-1)
-    if a.size < m * k:
-        raise ValueError(f"weight has {a.size} bf16 values, needs {m * k}")
-    return bf16_bits_to_f64(a[: m * k]).reshape(m, k)
-
-
 def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray:
     """Exact f64 values of an ``m x k`` weight (optionally only the listed rows).
 

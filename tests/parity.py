@@ -90,3 +90,36 @@ def oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, bound, rows=None, alp
         yo = np.asarray(y_old, np.float64).reshape(-1, m)
         yo = yo[:, rows] if rows is not None else yo
     return y_ref, tolerance(S, y_ref, bound, flags, v, b, yo, alpha)
+
+
+def literal_ratio(got, y_ref, S, bound) -> float:
+    """max |y - y_ref| / (bound * S) over the outputs with S > 0: the error against the bound as
+    the workload states it (B * S alone, with no slope or f32 epilogue slack added)."""
+    got = np.asarray(got, np.float64)
+    S = np.asarray(S, np.float64)
+    pos = S > 0
+    if not pos.any():
+        return 0.0
+    return float((np.abs(got - y_ref)[pos] / (bound * S[pos])).max())
+
+
+def guarded_at_offset(rows: int, cols: int, offset: int, y_old=None, guard: int = 64):
+    """An output that starts `offset` floats into its buffer: canaries before and after it, NaN
+    (or y_old) inside. Returns (buffer, the [rows x cols] view)."""
+    import torch
+    total = offset + rows * cols + guard
+    buf = torch.full((total,), CANARY, dtype=torch.float32, device="cuda")
+    inner = buf[offset: offset + rows * cols]
+    inner.fill_(float("nan"))
+    if y_old is not None:
+        inner.copy_(dev(np.asarray(y_old, np.float32).reshape(-1)))
+    return buf, inner.view(rows, cols)
+
+
+def read_at_offset(buf, rows: int, cols: int, offset: int) -> np.ndarray:
+    import torch
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert (host[:offset] == CANARY).all(), "write before the start of the output"
+    assert (host[offset + rows * cols:] == CANARY).all(), "write past the end of the output"
+    return host[offset: offset + rows * cols].reshape(rows, cols)

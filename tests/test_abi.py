@@ -120,7 +120,8 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
     (dict(y=None), -1, "NULL"),
     (dict(x=X + 4), -5, "aligned"),
     (dict(w=W + 2), -5, "aligned"),
-    (dict(y=Y + 8), -5, "aligned"),
+    (dict(y=Y + 2), -5, "aligned"),
+    (dict(y=Y + 1), -5, "aligned"),
     (dict(bias=B + 2, flags=1), -5, "aligned"),
     (dict(y=X), -6, "overlaps"),
     (dict(y=W + 16), -6, "overlaps"),
