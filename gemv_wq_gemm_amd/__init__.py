@@ -36,6 +36,7 @@ SIGNATURES = [
     ("wq_linear", _I, [_P, _P, _I, _P, _U, ctypes.c_float, _P, _I64, _I64, _I64, _I, _P]),
     ("wq_linear_dual", _I, [_P, _P, _I, _P, _U, ctypes.c_float, _P, _I64, _I64, _I64, _I64, _I, _P]),
     ("wq_moe_matvec", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
+    ("wq_moe_matvec_noalloc", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     ("wq_dequantize", _I, [_P, _I, _P, _I64, _I64, _P]),
     ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
     ("wq_gemm_path", _I, [_I64, _I64, _I64, _I]),
@@ -198,12 +199,14 @@ def bind_gemm(x, w, wtype: int, *, m: int, k: int, out, bias=None, gelu: bool = 
     return BoundGemm(lib().wq_linear, args)
 
 
-def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: int, k: int, out=None):
-    """Expert-major MoE matvec via ``wq_moe_matvec``.
+def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: int, k: int, out=None,
+               noalloc: bool = False):
+    """Expert-major MoE matvec via ``wq_moe_matvec`` (``wq_moe_matvec_noalloc`` with ``noalloc``).
 
     ``ids`` int32 ``[n_tok][top_k]``. Without ``gates`` the result is per slot
     ``[n_tok*top_k][m]``; with ``gates`` (f32 ``[n_tok][top_k]``) it is the
-    gate-weighted sum per token, ``[n_tok][m]``.
+    gate-weighted sum per token, ``[n_tok][m]``. ``noalloc`` takes the entry point
+    that never allocates device memory (give ``out`` as well, so this call allocates nothing).
     """
     import torch
     if ids.dtype != torch.int32:
@@ -213,7 +216,8 @@ def moe_matvec(x, w_experts, wtype: int, ids, gates=None, *, n_experts: int, m: 
     if out is None:
         out = torch.empty((rows, m), dtype=torch.float32, device=x.device)
     nbytes = weight_bytes(wtype, m, k)
-    st = lib().wq_moe_matvec(
+    fn = lib().wq_moe_matvec_noalloc if noalloc else lib().wq_moe_matvec
+    st = fn(
         _f32(x, "x", n_tok * k), _weight(w_experts, wtype, max(nbytes, 0) * n_experts, "w_experts"), wtype,
         _dev(ids, "ids"), None if gates is None else _f32(gates, "gates", n_tok * top_k),
         _f32(out, "out", rows * m), n_tok, top_k, n_experts, m, k, _stream())

@@ -101,6 +101,34 @@ int workspace(hipStream_t stream, size_t bytes, void** out) {
   return WQ_OK;
 }
 
+// ---- no-allocation scratch (wq_moe_matvec_noalloc) ----
+// The per-slot products of a gated MoE call, before the combine. A file-scope device array: each
+// GPU the library runs on holds its own copy from the module's load until the process ends. Host
+// code never uses the name itself (in host code it is a stand-in, not a device address); it takes
+// the address from hipGetSymbolAddress once per device, with that device current.
+constexpr size_t kScratchFloats = size_t(8) << 20;  // 32 MiB
+static __device__ __align__(256) float scratch[kScratchFloats];
+
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[64] = {};
+
+int scratch_address(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(WQ_ERR_HIP, "device index %d outside the scratch table", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress (MoE scratch)");
+    if (ptr == nullptr) return fail(WQ_ERR_HIP, "hipGetSymbolAddress gave a null scratch address");
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
+  return WQ_OK;
+}
+
 int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
                  float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream) {
   clear_error();
@@ -221,9 +249,15 @@ int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, 
   return gemm_checked(x, w, wtype, bias, flags, alpha, y, n, m, k, dual, path, stream);
 }
 
-int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
-                  const float* gate_w, float* y, int64_t n_tok, int64_t top_k, int64_t n_experts, int64_t m,
-                  int64_t k, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Both MoE entry points: `noalloc` takes the per-slot products into the library's fixed scratch
+// array instead of the grown workspace.
+int moe_checked(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                const float* gate_w, float* y, int64_t n_tok, int64_t top_k, int64_t n_experts, int64_t m,
+                int64_t k, void* stream, bool noalloc) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   if (n_tok < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size");
@@ -246,10 +280,16 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
       overlap(y, ybytes, expert_ids, n_slots * 4) || overlap(y, ybytes, gate_w, n_slots * 4))
     return fail(WQ_ERR_ALIAS, "y overlaps x, w_experts, expert_ids or gate_w");
 
+  if (noalloc && gate_w && n_slots * m > static_cast<int64_t>(kScratchFloats))
+    return fail(WQ_ERR_SHAPE, "n_tok * top_k * m = %lld exceeds the %lld floats of the no-allocation scratch",
+                (long long)(n_slots * m), (long long)kScratchFloats);
+
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* slots = y;
   std::unique_lock<std::mutex> ws_lock(g_ws_mu, std::defer_lock);  // held through the launches
-  if (gate_w) {
+  if (gate_w && noalloc) {
+    if (int r = scratch_address(&slots)) return r;
+  } else if (gate_w) {
     ws_lock.lock();
     void* ws = nullptr;
     if (int r = workspace(s, static_cast<size_t>(n_slots * m * 4), &ws)) return r;
@@ -283,6 +323,22 @@ int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_
     if (e != hipSuccess) return hip_fail(e, "MoE combine launch");
   }
   return WQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                  const float* gate_w, float* y, int64_t n_tok, int64_t top_k, int64_t n_experts, int64_t m,
+                  int64_t k, void* stream) {
+  return moe_checked(x, w_experts, wtype, expert_ids, gate_w, y, n_tok, top_k, n_experts, m, k, stream, false);
+}
+
+int wq_moe_matvec_noalloc(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                          const float* gate_w, float* y, int64_t n_tok, int64_t top_k, int64_t n_experts,
+                          int64_t m, int64_t k, void* stream) {
+  return moe_checked(x, w_experts, wtype, expert_ids, gate_w, y, n_tok, top_k, n_experts, m, k, stream, true);
 }
 
 int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream) {

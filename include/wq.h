@@ -33,7 +33,7 @@
  *     still read the old buffer), frees that buffer and calls hipMalloc. A
  *     gated wq_moe_matvec call that grows the workspace therefore cannot be
  *     captured into a HIP graph; make one uncaptured call of the largest size
- *     first.
+ *     first, or use wq_moe_matvec_noalloc, which never allocates.
  *   - Every entry point may be called from several host threads at once, on
  *     the same stream or on different ones.
  *   - Alignment: x and w must be 16-byte aligned (the kernels move them with
@@ -210,6 +210,24 @@ int wq_linear_dual(const float* x, const void* w, int wtype, const float* bias, 
 int wq_moe_matvec(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
                   const float* gate_w, float* y, int64_t n_tok, int64_t top_k,
                   int64_t n_experts, int64_t m, int64_t k, void* stream);
+
+/*
+ * wq_moe_matvec_noalloc: wq_moe_matvec for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). Same arguments,
+ * checks and results (bit for bit: the same kernels). It never allocates or frees: a gated
+ * call's per-slot products go to a fixed scratch array that the library holds per GPU (32 MiB,
+ * kept until the process ends) instead of the grown workspace.
+ *   - A gated call needs n_tok * top_k * m <= 8,388,608 (2^23 floats); a larger one returns
+ *     WQ_ERR_SHAPE. Ungated calls use no scratch and have no extra limit.
+ *   - Every call on a GPU shares that GPU's scratch array: calls of this entry point that overlap
+ *     on one GPU (on different streams, or from several threads without ordering) race on it.
+ *     Calls on one stream are ordered and safe. Nothing in the scratch must start at zero: every
+ *     value the combine reads is written by the same call first.
+ *   - The first call on a device looks up the array's device address (hipGetSymbolAddress).
+ */
+int wq_moe_matvec_noalloc(const float* x, const void* w_experts, int wtype, const int32_t* expert_ids,
+                          const float* gate_w, float* y, int64_t n_tok, int64_t top_k,
+                          int64_t n_experts, int64_t m, int64_t k, void* stream);
 
 /*
  * wq_dequantize: out[m][k] = the exact f32 value of every weight (bf16: the

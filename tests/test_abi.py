@@ -203,6 +203,20 @@ def test_moe_argument_errors(kwargs, code):
     assert st == code, err
 
 
+def test_moe_noalloc_checks_like_moe():
+    lib = wq.lib()
+    for kwargs, code in [(dict(wtype=5), -3), (dict(top_k=0), -2), (dict(ids=None), -1), (dict(y=B), -6)]:
+        a = dict(x=X, w=W, wtype=2, ids=B, gates=None, y=Y, n_tok=4, top_k=2, n_exp=8, m=16, k=32)
+        a.update(kwargs)
+        st = lib.wq_moe_matvec_noalloc(a["x"], a["w"], a["wtype"], a["ids"], a["gates"], a["y"], a["n_tok"],
+                                       a["top_k"], a["n_exp"], a["m"], a["k"], None)
+        assert st == code, lib.wq_last_error().decode()
+    # Gated calls beyond the 2^23-float scratch are refused on the host.
+    st = lib.wq_moe_matvec_noalloc(X, W, 1, B, B + 0x10000, 0x10000000, 4096, 1, 1, 4096, 32, None)
+    assert st == -2 and "scratch" in lib.wq_last_error().decode()
+    assert lib.wq_moe_matvec_noalloc(None, None, 2, None, None, None, 0, 2, 8, 16, 32, None) == 0
+
+
 @pytest.mark.parametrize("args,code", [
     ((W, 9, Y, 4, 32), -3),
     ((W, 1, Y, 4, 31), -2),
