@@ -171,6 +171,30 @@ def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray
     return dec(a, mm, k)
 
 
+def padded_k(k: int) -> int:
+    """The inner size a weight with ``k`` columns is padded to: the next multiple of 32 (the
+    GEMM's k step; wavo ``Gpu::upload_linear``, ``kp = k.next_multiple_of(32)``)."""
+    return -(-int(k) // QBLOCK) * QBLOCK
+
+
+def pad_weight(raw, wtype: int, m: int, k: int):
+    """``(W_padded, kp)``: an ``m x k`` weight of a plain type (f32, f16 or bf16), decoded to its
+    exact values and zero-padded to ``kp = padded_k(k)`` columns.
+
+    This is wavo ``Gpu::upload_linear``'s load path for conv weights (``Gpu::conv``) whose inner
+    size is not a multiple of 32: the rows are converted to f32, each row gets zero columns up to
+    the next multiple of 32, and the result is stored as an f32 (type 0) linear layer, which then
+    multiplies im2col rows that are zero past ``k`` as well. Every decoded value is exact in f32.
+    """
+    if wtype not in PLAIN_BYTES:
+        raise ValueError("only f32, f16 and bf16 weights are padded (block types need k % 32 == 0)")
+    kp = padded_k(k)
+    w = decode(raw, wtype, m, k)
+    out = np.zeros((m, kp), dtype=np.float64)
+    out[:, :k] = w
+    return out, kp
+
+
 # ---------------------------------------------------------------------------
 # Epilogue
 # ---------------------------------------------------------------------------
