@@ -38,6 +38,8 @@ SIGNATURES = [
     ("wq_moe_matvec", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     ("wq_moe_matvec_noalloc", _I, [_P, _P, _I, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _P]),
     ("wq_dequantize", _I, [_P, _I, _P, _I64, _I64, _P]),
+    ("wq_pad_weight", _I, [_P, _I, _P, _I64, _I64, _P]),
+    ("wq_padded_k", _I64, [_I64]),
     ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
     ("wq_gemm_path", _I, [_I64, _I64, _I64, _I]),
     ("wq_last_error", ctypes.c_char_p, []),
@@ -232,5 +234,28 @@ def dequantize(w, wtype: int, *, m: int, k: int, out=None):
         out = torch.empty((m, k), dtype=torch.float32, device=w.device)
     nbytes = weight_bytes(wtype, m, k)
     st = lib().wq_dequantize(_weight(w, wtype, max(nbytes, 0)), wtype, _f32(out, "out", m * k), m, k, _stream())
+    _check(st)
+    return out
+
+
+def padded_k(k: int) -> int:
+    """The inner size :func:`pad_weight` pads ``k`` to (the next multiple of 32)."""
+    r = int(lib().wq_padded_k(k))
+    if r < 0:
+        raise ValueError(f"k = {k} is outside [1, 2^29 - 1]")
+    return r
+
+
+def pad_weight(w, wtype: int, *, m: int, k: int, out=None):
+    """``out[m][kp]`` f32: the f32/f16/bf16 weight ``w[m][k]`` zero-padded to ``kp = padded_k(k)``
+    columns, via ``wq_pad_weight`` (wavo's conv weights with k % 32 != 0)."""
+    import torch
+    kp = padded_k(k)
+    if out is None:
+        out = torch.empty((m, kp), dtype=torch.float32, device=w.device)
+    width = 4 if wtype == W_F32 else 2
+    if w.numel() * w.element_size() < m * k * width:
+        raise ValueError(f"w has {w.numel() * w.element_size()} bytes, needs {m * k * width}")
+    st = lib().wq_pad_weight(_dev(w, "w"), wtype, _f32(out, "out", m * kp), m, k, _stream())
     _check(st)
     return out

@@ -357,6 +357,28 @@ int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, vo
   return WQ_OK;
 }
 
+int64_t wq_padded_k(int64_t k) { return k < 1 || k > kIntMax / 4 ? -1 : (k + 31) / 32 * 32; }
+
+int wq_pad_weight(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream) {
+  clear_error();
+  if (wtype != WQ_W_F32 && wtype != WQ_W_F16 && wtype != WQ_W_BF16)
+    return fail(WQ_ERR_WTYPE, "padding takes f32, f16 or bf16 weights (3, 4 or 0), got %d", wtype);
+  if (m < 0) return fail(WQ_ERR_SHAPE, "negative m");
+  const int64_t kp = wq_padded_k(k);
+  if (kp < 0) return fail(WQ_ERR_SHAPE, "k must be in [1, 2^29 - 1], got %lld", (long long)k);
+  if (m > kMaxRows || m * kp > kMaxOutputs) return fail(WQ_ERR_SHAPE, "m * k too large");
+  if (m == 0) return WQ_OK;
+  if (!w || !out) return fail(WQ_ERR_NULL, "w and out must not be NULL");
+  const int64_t width = wtype == WQ_W_F32 ? 4 : 2;
+  if (!aligned(w, static_cast<uintptr_t>(width)) || !aligned(out, 4))
+    return fail(WQ_ERR_ALIGN, "w must be aligned to its element size and out to 4 bytes");
+  if (overlap(out, m * kp * 4, w, m * k * width)) return fail(WQ_ERR_ALIAS, "out overlaps w");
+  hipError_t e = wq::launch_pad_weight(wtype, static_cast<const uint8_t*>(w), out, m, static_cast<int>(k),
+                                       static_cast<int>(kp), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "pad weight launch");
+  return WQ_OK;
+}
+
 const char* wq_last_error(void) { return g_err; }
 
 const char* wq_version(void) { return "wq 0.1.0 (gfx950)"; }

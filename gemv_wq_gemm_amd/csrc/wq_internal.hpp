@@ -66,6 +66,10 @@ hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, 
 hipError_t launch_dequantize(int wtype, const uint8_t* w, float* out, int m, int k,
                              hipStream_t stream);
 
+// out[m][kp] f32 = w[m][k] (f32, f16 or bf16) decoded and zero-padded to kp columns.
+hipError_t launch_pad_weight(int wtype, const uint8_t* w, float* out, long long m, int k, int kp,
+                             hipStream_t stream);
+
 // ---- MFMA GEMM ---------------------------------------------------------------------------------
 struct GemmParams {
   const float* x;     // [n][k]

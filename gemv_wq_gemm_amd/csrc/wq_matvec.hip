@@ -350,7 +350,42 @@ __global__ __launch_bounds__(256) void dequantize_kernel(const uint8_t* w, float
   for (int i = 0; i < 8; ++i) o[i] = make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3]);
 }
 
+// ---- padded-k weights (load-time conversion) -------------------------------------------------
+// out[r][c] = the exact f32 value of w[r][c] for c < k, 0 for k <= c < kp: wavo's conv weights
+// (`Gpu::upload_linear` with k % 32 != 0) as an f32 weight the layer can take. A grid-stride loop
+// over the m * kp outputs, one element per thread per step: w need only be 2- or 4-byte aligned.
+template <int WT>
+__global__ __launch_bounds__(256) void pad_weight_kernel(const uint8_t* w, float* out, long long m, int k, int kp) {
+  const long long total = m * kp;
+  for (long long i = static_cast<long long>(blockIdx.x) * 256 + threadIdx.x; i < total;
+       i += static_cast<long long>(gridDim.x) * 256) {
+    const long long r = i / kp;
+    const int c = static_cast<int>(i - r * kp);
+    float v = 0.f;
+    if (c < k) {
+      const long long at = r * k + c;
+      if constexpr (WT == kF32) v = reinterpret_cast<const float*>(w)[at];
+      else if constexpr (WT == kF16) v = f16_to_f32(reinterpret_cast<const uint16_t*>(w)[at]);
+      else v = __uint_as_float(static_cast<uint32_t>(reinterpret_cast<const uint16_t*>(w)[at]) << 16);
+    }
+    out[i] = v;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_pad_weight(int wtype, const uint8_t* w, float* out, long long m, int k, int kp,
+                             hipStream_t stream) {
+  const long long want = (m * kp + 255) / 256;
+  const unsigned grid = static_cast<unsigned>(want < (1 << 20) ? want : (1 << 20));
+  switch (wtype) {
+    case kF32: hipLaunchKernelGGL(pad_weight_kernel<kF32>, dim3(grid), dim3(256), 0, stream, w, out, m, k, kp); break;
+    case kF16: hipLaunchKernelGGL(pad_weight_kernel<kF16>, dim3(grid), dim3(256), 0, stream, w, out, m, k, kp); break;
+    case kBF16: hipLaunchKernelGGL(pad_weight_kernel<kBF16>, dim3(grid), dim3(256), 0, stream, w, out, m, k, kp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStream_t stream) {
   // MoE: matrix cores (each workgroup walks many tiles, which repays building the activation

@@ -240,6 +240,24 @@ int wq_moe_matvec_noalloc(const float* x, const void* w_experts, int wtype, cons
  */
 int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream);
 
+/*
+ * wq_pad_weight: out[m][kp] = w[m][k] as exact f32 values, each row followed by kp - k zeros,
+ * kp = wq_padded_k(k). wavo's load path for conv weights whose inner size is not a multiple of
+ * 32 (`Gpu::upload_linear` with its `kp != k` branch, reached through `Gpu::conv`): the rows are
+ * converted to f32 and zero-padded, and the layer then runs as an f32 weight of inner size kp on
+ * input rows that are zero past k (wavo's im2col rows). wq_gemm itself still refuses
+ * k % 32 != 0; pad once at load, then call wq_gemm(..., WQ_W_F32, ..., k = kp).
+ *   w     f32, f16 or bf16 [m][k] (WQ_W_F32, WQ_W_F16, WQ_W_BF16; other types WQ_ERR_WTYPE),
+ *         aligned to its element size.
+ *   out   f32 [m][kp], 4-byte aligned, not overlapping w.
+ *   k     1 <= k <= 2^29 - 1, any value (a multiple of 32 just copies).
+ */
+int wq_pad_weight(const void* w, int wtype, float* out, int64_t m, int64_t k, void* stream);
+
+/* The inner size wq_pad_weight pads k to: the next multiple of 32 (the GEMM's k step), or -1 for
+ * k outside [1, 2^29 - 1]. */
+int64_t wq_padded_k(int64_t k);
+
 /* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32); f32 4*m*k; f16 2*m*k;
  * -1 for an unknown type, negative sizes or k % 32 != 0. The block sizes are those of the formats
  * above (wavo `Gpu::upload_linear` sizes a Q8_0 row as k/32 blocks of 34 bytes; hanzo-ml

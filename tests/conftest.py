@@ -9,6 +9,11 @@ if ROOT not in sys.path:
 
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
+# A test build of the library (the host-sanitizer test runs test_abi.py against one).
+if os.environ.get("WQ_TEST_LIB"):
+    import gemv_wq_gemm_amd
+    gemv_wq_gemm_amd.LIB_PATH = os.environ["WQ_TEST_LIB"]
+
 
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")

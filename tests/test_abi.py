@@ -229,6 +229,29 @@ def test_dequantize_argument_errors(args, code):
     assert lib.wq_dequantize(*args, None) == code
 
 
+@pytest.mark.parametrize("k,kp", [(1, 32), (40, 64), (64, 64), (100, 128), (0, -1), (-3, -1)])
+def test_padded_k(k, kp):
+    assert wq.lib().wq_padded_k(k) == kp
+
+
+@pytest.mark.parametrize("args,code", [
+    ((W, 1, Y, 4, 40), -3),            # Q8_0 cannot be padded
+    ((W, 2, Y, 4, 40), -3),
+    ((W, 9, Y, 4, 40), -3),
+    ((W, 3, Y, 4, 0), -2),
+    ((W, 3, Y, -1, 40), -2),
+    ((None, 3, Y, 4, 40), -1),
+    ((W + 2, 3, Y, 4, 40), -5),        # f32 weight on a 2-byte boundary
+    ((W + 1, 4, Y, 4, 40), -5),
+    ((W, 3, Y + 2, 4, 40), -5),
+    ((W, 3, W + 64, 4, 40), -6),
+])
+def test_pad_weight_argument_errors(args, code):
+    lib = wq.lib()
+    assert lib.wq_pad_weight(*args, None) == code, lib.wq_last_error().decode()
+    assert lib.wq_pad_weight(None, 3, None, 0, 40, None) == 0
+
+
 def test_error_message_is_per_call():
     st, err = _gemm(k=40)
     assert st == -2 and err
