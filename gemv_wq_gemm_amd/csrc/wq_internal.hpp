@@ -39,6 +39,7 @@ struct MatvecParams {
   int ystride;              // floats from one row of y to the next: m + dual (MoE: m); the sliced
                             // and matrix-core kernels take only dual == 0 (stride m)
   int dual;                 // plain layer: outputs 0..dual-1 stored again at m + j (bias[m + j])
+  int moe_compact;          // MoE: 1 when the grid is dealt over the touched experts (wq_moe_sched.hpp)
 };
 
 // Picks the kernel variant (tokens per pass, rows per wave) and launches it.

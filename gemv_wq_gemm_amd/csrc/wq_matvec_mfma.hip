@@ -42,9 +42,10 @@
 //    From a 4-byte aligned per-lane base, every block's LDS offsets are compile-time constants.
 //  * Each wave writes its 16x16 partial sums to LDS; after the next tile's barrier the workgroup
 //    adds the k-slices in wave order and stores.
-//  * blockIdx.y is the expert; a ballot over the ids picks its slots, 16 per pass, so each
-//    touched expert's rows stream once per 16 of its slots. One extra grid row writes NaN for
-//    slots whose id is out of range.
+//  * MoE: the grid is dealt over the experts the ids touch (wq_moe_sched.hpp; for banks of more
+//    than 256 experts blockIdx.y is the expert); a ballot over the ids picks the expert's slots,
+//    16 per pass, so each touched expert's rows stream once per 16 of its slots. A second grid row
+//    writes NaN for slots whose id is out of range.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -53,6 +54,7 @@
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
 #include "wq_lds_dma.hpp"
+#include "wq_moe_sched.hpp"
 
 namespace wq {
 namespace {
@@ -166,12 +168,20 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int e = blockIdx.y;
+  __shared__ uint32_t touched_lds[kMoeCompactMax / 32];
+  int e = blockIdx.y;
   const int ntiles = (p.m + kTileRows - 1) / kTileRows;
-  const int t_begin = blockIdx.x * tiles_per_wg;
-  const int t_end = min(ntiles, t_begin + tiles_per_wg);
-  if (t_begin >= ntiles) return;  // workgroup-uniform
   const bool moe = p.ids != nullptr;
+  int t_begin = blockIdx.x * tiles_per_wg;
+  int t_end = min(ntiles, t_begin + tiles_per_wg);
+  if (moe && p.moe_compact) {
+    const MoeAssign a = moe_assign(p, ntiles, tiles_per_wg, touched_lds);
+    e = a.e;
+    t_begin = a.t_begin;
+    t_end = a.t_end;
+    if (e < 0) return;  // workgroup-uniform: no expert is touched
+  }
+  if (t_begin >= ntiles) return;  // workgroup-uniform
 
   if (moe && e == p.n_exp) {
     // Slots routed outside the bank: their outputs in this run of rows become NaN.
@@ -365,8 +375,17 @@ hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
       per_cu = 1;
     per_cu_cache.store(per_cu, std::memory_order_relaxed);
   }
-  // As many workgroups as are resident at once, split over the experts.
-  int groups = per_cu * mfma_device_cus() / p.n_exp;
+  // As many workgroups as are resident at once. MoE: dealt over the touched experts on the device
+  // (wq_moe_sched.hpp), or split evenly over all experts where the bitmap cannot hold them.
+  const int resident = per_cu * mfma_device_cus();
+  if (p.ids != nullptr && p.n_exp <= kMoeCompactMax && resident >= p.n_exp) {
+    MatvecParams q = p;
+    q.moe_compact = 1;
+    const int tpw = (ntiles + resident - 1) / resident;
+    hipLaunchKernelGGL(kernel, dim3(resident, 2), dim3(64 * nw), 0, stream, q, tpw);
+    return hipGetLastError();
+  }
+  int groups = resident / p.n_exp;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   const int tpw = (ntiles + groups - 1) / groups;

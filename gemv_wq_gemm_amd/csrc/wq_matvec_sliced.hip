@@ -38,6 +38,8 @@
 //    and stores. An epilogue that reads memory (bias, residual) would make
 //    the compiler wait for every ring load in flight, so such launches give each
 //    workgroup at most one flush of rows.
+//  * MoE: the grid is dealt over the experts the ids touch (wq_moe_sched.hpp; for banks of more
+//    than 256 experts blockIdx.y is the expert), and a ballot over the ids finds the expert's slots.
 //  * Rounding: an E-term chain, one scale, a 6-level tree and at most 16 slice
 //    additions per output -- far inside 1e-5 * sum |x w|.
 #include <hip/hip_runtime.h>
@@ -47,6 +49,7 @@
 #include "wq_decode.hpp"
 #include "wq_internal.hpp"
 #include "wq_lds_dma.hpp"
+#include "wq_moe_sched.hpp"
 #include "wq_tile_math.hpp"
 
 namespace wq {
@@ -230,11 +233,19 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
-  const int e = blockIdx.y;
+  __shared__ uint32_t touched_lds[kMoeCompactMax / 32];
+  int e = blockIdx.y;
   const bool moe = p.ids != nullptr;
   const int ntiles = (p.m + R - 1) / R;
-  const int t_begin = blockIdx.x * tiles_per_wg;
-  const int t_end = min(ntiles, t_begin + tiles_per_wg);
+  int t_begin = blockIdx.x * tiles_per_wg;
+  int t_end = min(ntiles, t_begin + tiles_per_wg);
+  if (moe && p.moe_compact) {
+    const MoeAssign a = moe_assign(p, ntiles, tiles_per_wg, touched_lds);
+    e = a.e;
+    t_begin = a.t_begin;
+    t_end = a.t_end;
+    if (e < 0) return;  // workgroup-uniform: no expert is touched
+  }
   if (t_begin >= ntiles) return;  // workgroup-uniform
 
   if (moe && e == p.n_exp) {
@@ -411,11 +422,20 @@ hipError_t launch_r(const MatvecParams& p, int n_exp_rows, hipStream_t stream) {
   const int nw = p.k / SLICE;
   const int ntiles = (p.m + R - 1) / R;
   auto kernel = matvec_sliced_kernel<WT, NTC, R, NSTAGE, MAXW, SLICE>;
-  // As many workgroups as are resident at once (no thin second round), split over the
-  // experts; each walks a run of tiles with NSTAGE-1 of them in flight.
-  const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
+  // As many workgroups as are resident at once (no thin second round); each walks a run of tiles
+  // with NSTAGE-1 of them in flight. MoE: dealt over the touched experts on the device
+  // (wq_moe_sched.hpp), or split evenly over all experts where the bitmap cannot hold them.
   static std::atomic<int> per_cu[17];  // per variant and wave count
-  int groups = groups_per_cu(kernel, 64 * nw, &per_cu[nw]) * device_cus() / experts;
+  const int resident = groups_per_cu(kernel, 64 * nw, &per_cu[nw]) * device_cus();
+  if (p.ids != nullptr && p.n_exp <= kMoeCompactMax && resident >= p.n_exp) {
+    MatvecParams q = p;
+    q.moe_compact = 1;
+    const int tpw = (ntiles + resident - 1) / resident;
+    hipLaunchKernelGGL(kernel, dim3(resident, 2), dim3(64 * nw), 0, stream, q, tpw);
+    return hipGetLastError();
+  }
+  const int experts = n_exp_rows > 1 ? n_exp_rows - 1 : 1;
+  int groups = resident / experts;
   if (groups < 1) groups = 1;
   if (groups > ntiles) groups = ntiles;
   int tpw = (ntiles + groups - 1) / groups;
