@@ -1,38 +1,41 @@
 """Throughput of the weight-dequantizing linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-others]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-cpu-baseline] [--no-others]
 
-A step is one pass of the decode workload: the Q8_0 matvec with W 4096x4096
-(34-byte blocks) at n = 1 and at n = 4, i.e. two wq_gemm calls. `value` is
-weight GB/s: the algorithmic weight bytes of the step (2 x 17,825,792) over
-the step's time, with every input resident in HBM. To keep the 256 MB
-Infinity Cache from serving the weights, the calls rotate over 36 distinct
-copies of W (641 MB), so every call streams its weight from HBM.
-
-The timed region runs the K steps' calls as two back-to-back phases on one
-stream (the K n=1 calls, then the K n=4 calls), with a HIP event at the start,
-between the phases and at the end. No event sits between two launches, so each
-phase's time over K is that kernel's mean launch duration (as a kernel trace
-sees it, plus the gap between back-to-back dispatches). Calls go through
-bound calls (argument conversion done once), so the host keeps ahead of the GPU.
+The step is one pass of the encoder GEMM chain, the largest workload: 24 layers of four wq_gemm
+calls at n = 1500 frames, d = 1024 (QKV 3072x1024 + bias; output projection 1024x1024 + bias +
+residual; MLP up 4096x1024 + bias + erf-GELU; MLP down 1024x4096 + bias + residual), bf16 weights
+(24 x 25 MB, distinct per layer), f32 activations. `value` is its TFLOP/s: 905,969,664,000 FLOP
+per step over the step time, with every input resident in HBM. The K timed steps run back to back
+in 5 equal blocks with a HIP event between blocks (and none between launches); ms_per_step is the
+whole region over K, and `spread` gives the median, min and max over the blocks.
 
 The same JSON line carries:
-  roofline      the dominant kernel's weight bytes per launch over its mean
-                launch time, against the 8 TB/s HBM peak; `traffic` is the HBM
-                bytes per launch that FETCH_SIZE / WRITE_SIZE counted for that
-                kernel (profiles/, scaled by a copy kernel of known size), or
-                null when the kernel sources changed since they were counted;
-  cpu_baseline  the f64 oracle (decode + product, numpy/OpenBLAS) on a
-                bounded sample of the same workload, on the host's cores;
-  others        the remaining workloads (bf16 GEMM 64x256x256, Q4_0 matvec
-                14336x4096, f16 matvec 4096x4096, MoE 16 tokens top-2 of 8, the
-                24-layer encoder chain, also on the f32-accurate matrix-core
-                path, and the MLP-up GEMM with f16 / f32 / Q8_0 / Q4_0 weights)
-                with their own TFLOP/s or GB/s and roofline fractions.
+  roofline      the chain's dominant kernel (the GEMM that takes the most time per step, the MLP down
+                projection): its FLOP per launch over its mean launch time, measured here with events
+                around back-to-back launches of it alone on the same stream, against the bf16 MFMA
+                peak; `traffic` is the HBM bytes per launch that FETCH_SIZE / WRITE_SIZE counted for it
+                (profiles/, scaled by a copy kernel of known size), or null when the kernel sources
+                changed since they were counted;
+  cpu_baseline  the f64 oracle (decode + numpy product + epilogue) on two of the chain's 24 layers,
+                all 1500 frames, on the host's cores;
+  rooflines     every other workload at its full size: the bf16 GEMM 64x256x256 + GELU, the Q8_0
+                matvec 4096x4096 at n = 1 and n = 4, the Q4_0 matvec 14336x4096, the MoE (16 tokens
+                top-2 of 8 Q4_0 14336x4096 experts, gated), and the MoE at sparse routing (1 token top-2
+                of 8; 16 tokens top-2 of 64). Each has the median / min / max of R repetitions of
+                back-to-back calls, its GB/s (weight bytes of the experts it touches) or TFLOP/s and
+                fraction of peak, the streaming-read floor for the same bytes (a plain read kernel,
+                libwq_bench.so) and the fraction of it reached (frac_of_sol), counted traffic and a CPU
+                baseline of its own;
+  others        the chain on the f32-accurate matrix-core path, f16 weights at 4096x4096 n = 1, and
+                the MLP-up shape with f16 / f32 / Q8_0 / Q4_0 weights.
+Weights of the matvec and MoE workloads rotate over copies of at least 600 MB, so the 256 MB
+Infinity Cache cannot serve them; the floors read the same amounts from rotating windows.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -44,24 +47,119 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 ROTATE_BYTES = 600 * 2 ** 20
+COUNTERS = os.path.join(ROOT, "profiles", "bench_hbm_counters.md")
 
 
 def _parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=5, help="repetitions behind each median / min / max")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--legs", default="all",
+                    help="comma list of workload groups to run (chain, c1, c2, c3, c4, moe1, moe64, others; "
+                         "default all): profiling runs select one so its kernels' counters are its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run an elementwise copy of 256 MiB (reads and writes that many bytes), "
                          "the reference for scaling HBM byte counters")
     return ap.parse_args()
 
 
-def _copies(make, nbytes):
-    return max(2, -(-ROTATE_BYTES // nbytes))
+class Timer:
+    """Back-to-back calls on the current stream, timed with HIP events only around whole runs."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.stream = torch.cuda.current_stream()
+
+    def runs(self, fn, calls, reps, warm=2):
+        """ms per call of each of `reps` runs of `calls` back-to-back calls."""
+        torch = self.torch
+        for i in range(warm):
+            fn(i)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        i = 0
+        ev[0].record(self.stream)
+        for r in range(reps):
+            for _ in range(calls):
+                fn(i)
+                i += 1
+            ev[r + 1].record(self.stream)
+        torch.cuda.synchronize()
+        return [ev[r].elapsed_time(ev[r + 1]) / calls for r in range(reps)]
+
+
+def _stats(ms_list):
+    a = np.array(ms_list)
+    return {"median_us": round(float(np.median(a)) * 1e3, 3), "min_us": round(float(a.min()) * 1e3, 3),
+            "max_us": round(float(a.max()) * 1e3, 3), "reps": len(a)}
+
+
+def _threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max((i.get("num_threads", 0) for i in threadpool_info()), default=0) or len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
+class Floor:
+    """The streaming-read floor: a plain read of `nbytes` (libwq_bench.so), from rotating windows of
+    one large buffer so the reads come from HBM."""
+
+    def __init__(self, torch, timer, dev):
+        path = os.path.join(ROOT, "gemv_wq_gemm_amd", "libwq_bench.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with `python -m gemv_wq_gemm_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        self.lib.wq_bench_stream_read.restype = ctypes.c_int
+        self.lib.wq_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                                                  ctypes.c_void_p]
+        self.lib.wq_bench_stream_read_lds.restype = ctypes.c_int
+        self.lib.wq_bench_stream_read_lds.argtypes = self.lib.wq_bench_stream_read.argtypes
+        self.lib.wq_bench_stream_read_blocks.restype = ctypes.c_int
+        self.blocks = self.lib.wq_bench_stream_read_blocks(4)
+        self.torch, self.timer = torch, timer
+        self.buf = torch.randint(0, 2 ** 31 - 1, (1024 * 2 ** 20 // 4,), dtype=torch.int32, device=dev)
+        self.out = torch.empty(self.blocks, dtype=torch.int32, device=dev)
+
+    def us(self, nbytes, reps):
+        """The faster of the two plain reads (register loads, direct-to-LDS loads) of `nbytes`."""
+        nbytes = nbytes // 1024 * 1024
+        windows = max(1, (self.buf.numel() * 4) // max(nbytes, 1))
+        base = self.buf.data_ptr()
+        stream = ctypes.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        out = ctypes.c_void_p(self.out.data_ptr())
+        best = None
+        for kind, fn_c in (("vgpr", self.lib.wq_bench_stream_read), ("lds", self.lib.wq_bench_stream_read_lds)):
+            def fn(i, fn_c=fn_c):
+                off = (i % windows) * nbytes
+                r = fn_c(ctypes.c_void_p(base + off), nbytes, out, self.blocks, stream)
+                if r != 0:
+                    raise RuntimeError(f"stream read launch failed: {r}")
+            calls = max(4, min(100, int(2e9 // max(nbytes, 1))))
+            st = {**_stats(self.timer.runs(fn, calls, reps)), "kind": kind}
+            if best is None or st["median_us"] < best["median_us"]:
+                best = st
+        return best
+
+
+def _hbm_entry(stats, weight_bytes, floor_stats, traffic, cpu=None, extra=None):
+    med = stats["median_us"] * 1e-6
+    gbs = weight_bytes / med / 1e9
+    floor = weight_bytes / (floor_stats["median_us"] * 1e-6) / 1e9
+    e = {**stats, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+         "floor_GB/s": round(floor, 1), "floor_us": floor_stats["median_us"], "floor_read": floor_stats["kind"],
+         "frac_of_sol": round(gbs / floor, 4),
+         "weight_bytes": weight_bytes, "traffic": None if traffic is None else round(traffic)}
+    if extra:
+        e.update(extra)
+    if cpu is not None:
+        e["cpu_baseline"] = cpu
+    return e
 
 
 def main():
@@ -70,16 +168,26 @@ def main():
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this path has no "
               f"multi-GPU mode)", file=sys.stderr)
         sys.exit(2)
+    if args.steps % 5 != 0 or args.steps <= 0:
+        print("--steps must be a positive multiple of 5 (the timed steps run in 5 equal blocks)", file=sys.stderr)
+        sys.exit(2)
 
     import torch
 
     import gemv_wq_gemm_amd as wq
     import synth
+    from gemv_wq_gemm_amd.rocprof_summary import read_traffic
 
+    all_legs = {"chain", "c1", "c2", "c3", "c4", "moe1", "moe64", "others"}
+    legs = all_legs if args.legs == "all" else set(args.legs.split(","))
+    if legs - all_legs:
+        print(f"unknown legs {sorted(legs - all_legs)}; choose from {sorted(all_legs)}", file=sys.stderr)
+        sys.exit(2)
+    args.legs_set = legs
     wq.lib()  # fail loudly if the library is not built
     dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream()
     props = torch.cuda.get_device_properties(dev)
+    timer = Timer(torch)
 
     if args.copy_calibration:
         src = torch.ones(64 * 2 ** 20, dtype=torch.float32, device=dev)
@@ -92,163 +200,32 @@ def main():
     def to_dev(a):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
 
-    # ---------------- the decode workload: Q8_0 4096x4096 at n = 1 and n = 4 ----------------
-    m = k = 4096
-    wbytes = wq.weight_bytes(wq.W_Q8_0, m, k)
-    ncopy = _copies(None, wbytes)
-    g = synth.rng(0, 2, 1, 0)
-    first = synth.q8_0_weight(g, m, k)
-    W = torch.empty((ncopy, first.size), dtype=torch.uint8, device=dev)
-    W[0] = to_dev(first.reshape(-1))
-    for c in range(1, ncopy):  # distinct bytes per copy: rows rolled, so no two copies share content
-        W[c] = torch.roll(W[0].view(m, -1), shifts=c * 7, dims=0).reshape(-1)
-    xs = {n: to_dev(synth.config_q8_matvec(n)["x"]) for n in (1, 4)}
-    ys = {n: torch.empty((n, m), dtype=torch.float32, device=dev) for n in (1, 4)}
-
-    binds = {n: [wq.bind_gemm(xs[n], W[c], wq.W_Q8_0, m=m, k=k, out=ys[n]) for c in range(ncopy)]
-             for n in (1, 4)}
-
-    for i in range(args.warmup):
-        for n in (1, 4):
-            binds[n][i % ncopy]()
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        binds[1][i % ncopy]()
-    ev[1].record(stream)
-    for i in range(args.steps):
-        binds[4][i % ncopy]()
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_total = ev[0].elapsed_time(ev[2])
-    ms_step = ms_total / args.steps
-    value = 2 * wbytes / (ms_step * 1e-3) / 1e9
-    kern = {"n1": ev[0].elapsed_time(ev[1]) / args.steps, "n4": ev[1].elapsed_time(ev[2]) / args.steps}
-    dom = max(kern, key=kern.get)
-    achieved = wbytes / (kern[dom] * 1e-3) / 1e9
-    from gemv_wq_gemm_amd.rocprof_summary import read_traffic
-    traffic = read_traffic(os.path.join(ROOT, "profiles", "matvec_q8_0_4096x4096_hbm_counters.md"), dom)
-
-    line = {
-        "metric": "matvec weight GB/s (Q8_0 decode, 1 MI355X)",
-        "value": round(value, 2),
-        "unit": "GB/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 6),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f32 (Q8_0 weights)",
-        "data": "synthetic",
-        "config": {
-            "workload": "Q8_0 matvec decode, W 4096x4096 (34-byte blocks), X f32 [n x 4096], n in {1, 4}; "
-                        "one step = the n=1 and n=4 calls",
-            "weight_bytes_per_call": wbytes,
-            "weight_copies_rotated": ncopy,
-            "parallelism": "single GPU",
-        },
-        "roofline": {
-            "bound": "hbm",
-            "kernel": f"matvec {dom} (wq_gemm, Q8_0)",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4),
-            "traffic": None if traffic is None else round(traffic),
-            "mean_launch_us": {t: round(v * 1e3, 3) for t, v in kern.items()},
-        },
-        "device": props.name,
-        "wall_s_timed_region": round(wall, 4),
-    }
-
-    if not args.no_others:
-        line["others"] = _others(torch, wq, synth, dev, stream, to_dev)
+    line, others = {}, {}
+    if "chain" in legs:
+        line, others, acts = _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic)
+    else:
+        acts = None
+        line = {"metric": "GEMM TFLOP/s (encoder chain) on 1 MI355X", "value": None, "unit": "TFLOP/s",
+                "note": f"profiling run of legs {sorted(legs)}; the step (the chain) was not run"}
+    line["rooflines"] = _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic)
+    if not args.no_others and "others" in legs:
+        others.update(_others(torch, wq, synth, dev, timer, to_dev, args))
+    if others:
+        line["others"] = others
 
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = _cpu_baseline(synth, args.cpu_seconds)
+        if acts is not None:
+            line["cpu_baseline"] = _cpu_chain(synth, acts)
+        for key, cpu in _cpu_configs(synth).items():
+            if key in line["rooflines"]:
+                line["rooflines"][key]["cpu_baseline"] = cpu
 
     print(json.dumps(line), flush=True)
 
 
-def _time_calls(torch, stream, fn, reps, warm=3):
-    """Mean ms per call of `reps` back-to-back calls (events only around the whole run)."""
-    for i in range(warm):
-        fn(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(reps):
-        fn(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
-
-
-def _others(torch, wq, synth, dev, stream, to_dev):
-    out = {}
-    # bf16 GEMM 64x256x256 + bias + GELU (launch-bound by size)
-    c = synth.config_gemm_small()
-    x, w, b = to_dev(c["x"]), to_dev(c["w"]), to_dev(c["bias"])
-    y = torch.empty((64, 256), device=dev)
-    g = wq.bind_gemm(x, w, wq.W_BF16, m=256, k=256, bias=b, gelu=True, out=y)
-    med = _time_calls(torch, stream, lambda i: g(), 200)
-    fl = 2 * 64 * 256 * 256
-    out["gemm_bf16_64x256x256"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 3),
-                                   "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 5)}
-
-    # Q4_0 14336x4096, n = 1, rotated copies
-    m, k = 14336, 4096
-    wb = wq.weight_bytes(wq.W_Q4_0, m, k)
-    nc = max(2, -(-ROTATE_BYTES // wb))
-    base = to_dev(synth.config_q4_matvec()["w"].reshape(-1))
-    Wc = torch.stack([torch.roll(base.view(m, -1), shifts=7 * i, dims=0).reshape(-1) for i in range(nc)])
-    x = to_dev(synth.config_q4_matvec()["x"])
-    y = torch.empty((1, m), device=dev)
-    gs = [wq.bind_gemm(x, Wc[i], wq.W_Q4_0, m=m, k=k, out=y) for i in range(nc)]
-    med = _time_calls(torch, stream, lambda i: gs[i % nc](), 100)
-    out["matvec_q4_0_14336x4096_n1"] = {"us": round(med * 1e3, 3), "GB/s": round(wb / (med * 1e-3) / 1e9, 1),
-                                        "frac_hbm": round(wb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                        "copies": nc}
-    del Wc
-
-    # f16 weights 4096 x 4096 at n = 1 (wavo Linear type 1), rotated copies
-    m16 = 4096
-    wb16 = wq.weight_bytes(wq.W_F16, m16, k)
-    nc16 = max(2, -(-ROTATE_BYTES // wb16))
-    base = to_dev(synth.weight(synth.rng(53), wq.W_F16, m16, k).reshape(-1).view(np.uint8))
-    Wc = torch.stack([torch.roll(base.view(m16, -1), shifts=7 * i, dims=0).reshape(-1) for i in range(nc16)])
-    x = to_dev(synth.normal_f32(synth.rng(54), (1, k), 1.0))
-    y = torch.empty((1, m16), device=dev)
-    gs = [wq.bind_gemm(x, Wc[i], wq.W_F16, m=m16, k=k, out=y) for i in range(nc16)]
-    med = _time_calls(torch, stream, lambda i: gs[i % nc16](), 100)
-    out["matvec_f16_4096x4096_n1"] = {"us": round(med * 1e3, 3), "GB/s": round(wb16 / (med * 1e-3) / 1e9, 1),
-                                      "frac_hbm": round(wb16 / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                      "copies": nc16}
-    del Wc
-
-    # MoE: 16 tokens, top-2 of 8 Q4_0 experts, gated; 3 banks rotated
-    banks = []
-    for bank in range(3):
-        cm = synth.config_moe(bank=bank)
-        banks.append(to_dev(cm["w"].reshape(-1)))
-    cm = synth.config_moe()
-    x, ids, gates = to_dev(cm["x"]), to_dev(cm["ids"]), to_dev(cm["gates"])
-    y = torch.empty((16, m), device=dev)
-    touched = len(np.unique(cm["ids"]))
-    med = _time_calls(torch, stream, lambda i: wq.moe_matvec(x, banks[i % 3], wq.W_Q4_0, ids, gates,
-                                                             n_experts=8, m=m, k=k, out=y), 60)
-    mb = touched * wb
-    out["moe_q4_0_16tok_top2_of_8"] = {"us": round(med * 1e3, 3), "GB/s": round(mb / (med * 1e-3) / 1e9, 1),
-                                       "frac_hbm": round(mb / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                                       "experts_touched": touched}
-    del banks
-
-    # Encoder chain: 24 layers x {QKV, out+res, fc1+GELU, fc2+res}, n = 1500
+def _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic):
+    """The step: the 24-layer encoder GEMM chain, timed; its layers one kind at a time; and (unless
+    --no-others) the chain on the f32-accurate path. Returns (line, others, activations)."""
     n, d, ff = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_FF
     acts = synth.encoder_activations()
     a1, a2, a3 = (to_dev(acts[nm]) for nm in ("a1", "a2", "a3"))
@@ -259,94 +236,343 @@ def _others(torch, wq, synth, dev, stream, to_dev):
         layers.append({nm: (to_dev(v["w"]), to_dev(v["bias"])) for nm, v in lw.items()})
     qkv = torch.empty((n, 3 * d), device=dev)
     f = torch.empty((n, ff), device=dev)
+    shapes = {"qkv": (a1, 3 * d, d, qkv, {}), "out": (a2, d, d, h, {"residual": True}),
+              "fc1": (a3, ff, d, f, {"gelu": True}), "fc2": (f, d, ff, h, {"residual": True})}
+
+    def bind_layer(W_, name, path):
+        x, m, k, out, kw = shapes[name]
+        return wq.bind_gemm(x, W_[name][0], wq.W_BF16, m=m, k=k, bias=W_[name][1], out=out, path=path, **kw)
 
     def bind_chain(path):
-        calls = []
-        for W_ in layers:
-            calls.append(wq.bind_gemm(a1, W_["qkv"][0], wq.W_BF16, m=3 * d, k=d, bias=W_["qkv"][1], out=qkv,
-                                      path=path))
-            calls.append(wq.bind_gemm(a2, W_["out"][0], wq.W_BF16, m=d, k=d, bias=W_["out"][1], residual=True,
-                                      out=h, path=path))
-            calls.append(wq.bind_gemm(a3, W_["fc1"][0], wq.W_BF16, m=ff, k=d, bias=W_["fc1"][1], gelu=True,
-                                      out=f, path=path))
-            calls.append(wq.bind_gemm(f, W_["fc2"][0], wq.W_BF16, m=d, k=ff, bias=W_["fc2"][1], residual=True,
-                                      out=h, path=path))
+        calls = [bind_layer(W_, nm, path) for W_ in layers for nm in ("qkv", "out", "fc1", "fc2")]
 
         def chain(_):
             for c in calls:
                 c()
         return chain
 
-    fl = 24 * 2 * n * (3 * d * d + d * d + ff * d + d * ff)
-    # bf16(X) on the matrix cores (the 2^-8 bound), then X as bf16 hi + lo parts (the f32 bound;
-    # twice the MFMA work, FLOP counted once).
-    for path, name in ((wq.PATH_AUTO, "encoder_chain_bf16_24x4_n1500"),
-                       (wq.PATH_MFMA_F32, "encoder_chain_bf16_f32acc_24x4_n1500")):
-        med = _time_calls(torch, stream, bind_chain(path), 10, warm=2)
-        out[name] = {"ms": round(med, 4), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
-                     "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-    del layers
+    flop_layer = 2 * n * (3 * d * d + d * d + ff * d + d * ff)
+    flop_step = synth.ENCODER_LAYERS * flop_layer
+    chain = bind_chain(wq.PATH_AUTO)
+    for i in range(args.warmup):
+        chain(i)
+    torch.cuda.synchronize()
+    blocks = 5
+    per_block = args.steps // blocks
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(blocks + 1)]
+    t0 = time.perf_counter()
+    ev[0].record(timer.stream)
+    for b in range(blocks):
+        for _ in range(per_block):
+            chain(0)
+        ev[b + 1].record(timer.stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = ev[0].elapsed_time(ev[blocks]) / args.steps
+    block_ms = [ev[b].elapsed_time(ev[b + 1]) / per_block for b in range(blocks)]
+    value = flop_step / (ms_step * 1e-3) / 1e12
 
-    # f16 / f32 weights (two / three exact bf16 parts on the matrix cores) at the same shape.
-    for wt, name in ((wq.W_F16, "f16"), (wq.W_F32, "f32")):
-        ws = [to_dev(synth.weight(synth.rng(50 + i, wt), wt, ff, d).reshape(-1)) for i in range(2)]
-        bq = to_dev(synth.normal_f32(synth.rng(52, wt), (ff,), 0.1))
-        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f) for w_ in ws]
-        med = _time_calls(torch, stream, lambda i: gq[i % 2](), 20)
-        fl = 2 * n * ff * d
-        out[f"gemm_{name}_{n}x{ff}x{d}_gelu"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
-                                                 "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        del ws, gq
+    # Per layer type: each layer kind alone, back to back over the 24 layers' weights.
+    layer_us = {}
+    for nm in ("qkv", "out", "fc1", "fc2"):
+        calls = [bind_layer(W_, nm, wq.PATH_AUTO) for W_ in layers]
+        layer_us[nm] = _stats(timer.runs(lambda i: calls[i % len(calls)](), len(calls), args.reps))
+    dom = max(layer_us, key=lambda k_: layer_us[k_]["median_us"])
+    x_, m_, k_, _, kw_ = shapes[dom]
+    dom_flop = 2 * n * m_ * k_
+    dom_tflops = dom_flop / (layer_us[dom]["median_us"] * 1e-6) / 1e12
+    dom_kernels = {"qkv": "gemm_bf16_kernel<64, 192, 2, 2, 2, 64, false>", "out": "gemm_bf16_kernel<64, 64, 2, 2, 3, 64, false>",
+                   "fc1": "gemm_bf16_kernel<64, 128, 2, 4, 2, 64, false>", "fc2": "gemm_bf16_kernel<64, 128, 2, 4, 4, 64, false>"}
+    traffic = read_traffic(COUNTERS, f"gemm_{dom}")
 
-    # Quantized weights on the matrix cores: the encoder's MLP-up shape (X[1500 x 1024], W[4096 x 1024]
-    # as Q8_0 / Q4_0 blocks, bias + GELU), 4 weight copies rotated.
-    for wt, name in ((wq.W_Q8_0, "q8_0"), (wq.W_Q4_0, "q4_0")):
-        ws = [to_dev(synth.weight(synth.rng(40 + i, wt), wt, ff, d).reshape(-1)) for i in range(4)]
-        bq = to_dev(synth.normal_f32(synth.rng(44, wt), (ff,), 0.1))
-        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f) for w_ in ws]
-        med = _time_calls(torch, stream, lambda i: gq[i % 4](), 40)
-        fl = 2 * n * ff * d
-        out[f"gemm_{name}_{n}x{ff}x{d}_gelu"] = {"us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
-                                                 "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f, path=wq.PATH_MFMA_F32) for w_ in ws]
-        med = _time_calls(torch, stream, lambda i: gq[i % 4](), 40)
-        out[f"gemm_{name}_f32acc_{n}x{ff}x{d}_gelu"] = {
-            "us": round(med * 1e3, 3), "TFLOP/s": round(fl / (med * 1e-3) / 1e12, 1),
-            "frac_mfma": round(fl / (med * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
-        del ws, gq
+    line = {
+        "metric": "GEMM TFLOP/s (encoder chain, bf16 weights, X rounded to bf16) on 1 MI355X; matvec weight GB/s in rooflines",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 x bf16 -> f32 (f32 activations rounded to bf16, bf16 weights as stored)",
+        "data": "synthetic",
+        "config": {
+            "workload": "encoder GEMM chain: 24 layers x {QKV 1500x3072x1024 +bias, out 1500x1024x1024 +bias+residual, "
+                        "MLP up 1500x4096x1024 +bias+erf-GELU, MLP down 1500x1024x4096 +bias+residual}; "
+                        "bf16 weights N(0,0.02) distinct per layer, f32 activations N(0,1)",
+            "flop_per_step": flop_step,
+            "weight_bytes_per_step": 24 * 2 * (3 * d * d + d * d + ff * d + d * ff),
+            "parallelism": "single GPU",
+        },
+        "spread": {**_stats(block_ms), "unit": "per step, over 5 blocks of the timed steps"},
+        "roofline": {
+            "bound": "mfma",
+            "kernel": f"{dom_kernels[dom]} ({dom}: {n}x{m_}x{k_})",
+            "achieved": round(dom_tflops, 1),
+            "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(dom_tflops / BF16_PEAK_TFLOPS, 4),
+            "traffic": None if traffic is None else round(traffic),
+            "flop_per_launch": dom_flop,
+            "mean_launch_us": layer_us[dom]["median_us"],
+        },
+        "layers": {nm: {**st, "TFLOP/s": round(2 * n * shapes[nm][1] * shapes[nm][2] / (st["median_us"] * 1e-6) / 1e12, 1),
+                        "frac": round(2 * n * shapes[nm][1] * shapes[nm][2] / (st["median_us"] * 1e-6) / 1e12
+                                      / BF16_PEAK_TFLOPS, 4)}
+                   for nm, st in layer_us.items()},
+        "device": props.name,
+        "wall_s_timed_region": round(wall, 4),
+    }
+
+    others = {}
+    if not args.no_others:
+        med = timer.runs(bind_chain(wq.PATH_MFMA_F32), 2, args.reps, warm=1)
+        st = _stats(med)
+        others["encoder_chain_f32_accurate"] = {**st, "ms": round(st["median_us"] / 1e3, 4),
+                                                "TFLOP/s": round(flop_step / (st["median_us"] * 1e-6) / 1e12, 1),
+                                                "frac": round(flop_step / (st["median_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+    del layers, qkv, f, h
+    torch.cuda.empty_cache()
+
+    return line, others, acts
+
+
+def _rotated(torch, base, rows, copies):
+    """`copies` distinct weights: the rows of `base` rolled by 7 c (no two copies share content)."""
+    return torch.stack([torch.roll(base.view(rows, -1), shifts=7 * c, dims=0).reshape(-1) for c in range(copies)])
+
+
+def _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic):
+    out = {}
+    legs = args.legs_set
+    R = args.reps
+    floor = Floor(torch, timer, dev) if legs & {"c2", "c3", "c4", "moe1", "moe64"} else None
+
+    # C1: bf16 GEMM 64x256x256 + bias + GELU (launch-bound by size)
+    if "c1" in legs:
+        _c1(torch, wq, synth, dev, timer, to_dev, R, out, read_traffic)
+    if "c2" in legs:
+        _c2(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic)
+    if "c3" in legs:
+        _c3(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic)
+    if legs & {"c4", "moe1", "moe64"}:
+        _moe(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic, legs)
+    torch.cuda.empty_cache()
     return out
 
 
-def _cpu_baseline(synth, seconds):
-    """The f64 oracle on a row sample of the decode workload (decode + product per call)."""
+def _c1(torch, wq, synth, dev, timer, to_dev, R, out, read_traffic):
+    c = synth.config_gemm_small()
+    x, w, b = to_dev(c["x"]), to_dev(c["w"]), to_dev(c["bias"])
+    y = torch.empty((64, 256), device=dev)
+    g = wq.bind_gemm(x, w, wq.W_BF16, m=256, k=256, bias=b, gelu=True, out=y)
+    st = _stats(timer.runs(lambda i: g(), 200, R))
+    fl = 2 * 64 * 256 * 256
+    tf = fl / (st["median_us"] * 1e-6) / 1e12
+    out["C1_gemm_bf16_64x256x256_gelu"] = {**st, "TFLOP/s": round(tf, 3), "frac": round(tf / BF16_PEAK_TFLOPS, 5),
+                                           "bound": "mfma (launch-bound by size)",
+                                           "traffic": read_traffic(COUNTERS, "c1_64x256x256")}
+
+
+def _c2(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic):
+    """Q8_0 4096x4096 at n = 1 and n = 4."""
+    m = k = 4096
+    wb = wq.weight_bytes(wq.W_Q8_0, m, k)
+    nc = max(2, -(-ROTATE_BYTES // wb))
+    W = _rotated(torch, to_dev(synth.q8_0_weight(synth.rng(0, 2, 1, 0), m, k).reshape(-1)), m, nc)
+    fl_st = floor.us(wb, R)
+    for n_ in (1, 4):
+        x = to_dev(synth.config_q8_matvec(n_)["x"])
+        y = torch.empty((n_, m), device=dev)
+        gs = [wq.bind_gemm(x, W[i], wq.W_Q8_0, m=m, k=k, out=y) for i in range(nc)]
+        st = _stats(timer.runs(lambda i: gs[i % nc](), 200, R))
+        out[f"C2_q8_0_4096x4096_n{n_}"] = _hbm_entry(st, wb, fl_st, read_traffic(COUNTERS, f"q8_0_n{n_}"),
+                                                      extra={"copies": nc})
+    del W
+
+
+def _c3(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic):
+    """Q4_0 14336x4096 at n = 1."""
+    m, k = 14336, 4096
+    wb = wq.weight_bytes(wq.W_Q4_0, m, k)
+    nc = max(2, -(-ROTATE_BYTES // wb))
+    cfg = synth.config_q4_matvec()
+    W = _rotated(torch, to_dev(cfg["w"].reshape(-1)), m, nc)
+    x = to_dev(cfg["x"])
+    y = torch.empty((1, m), device=dev)
+    gs = [wq.bind_gemm(x, W[i], wq.W_Q4_0, m=m, k=k, out=y) for i in range(nc)]
+    st = _stats(timer.runs(lambda i: gs[i % nc](), 100, R))
+    out["C3_q4_0_14336x4096_n1"] = _hbm_entry(st, wb, floor.us(wb, R), read_traffic(COUNTERS, "q4_0_n1"),
+                                              extra={"copies": nc})
+    del W
+
+
+def _moe(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic, legs):
+    """The MoE workload (C4) and the sparse routings: Q4_0 experts 14336x4096, gated; banks rotated."""
+    m, k = 14336, 4096
+    wb = wq.weight_bytes(wq.W_Q4_0, m, k)
+    cm = synth.config_moe()
+    banks = [to_dev(synth.config_moe(bank=bank)["w"].reshape(-1)) for bank in range(3)]
+    eb = wb
+    x16 = to_dev(cm["x"])
+
+    def moe_entry(key, n_exp, ids, gates, bank_list):
+        n_tok, top_k = ids.shape
+        x = x16[:n_tok]
+        ids_d, gates_d = to_dev(ids), to_dev(gates)
+        y = torch.empty((n_tok, m), device=dev)
+        touched = len(np.unique(ids))
+        calls = max(10, min(60, int(4e9 // (touched * eb))))
+        st = _stats(timer.runs(lambda i: wq.moe_matvec(x, bank_list[i % len(bank_list)], wq.W_Q4_0, ids_d, gates_d,
+                                                       n_experts=n_exp, m=m, k=k, out=y), calls, R))
+        out[key] = _hbm_entry(st, touched * eb, floor.us(touched * eb, R), read_traffic(COUNTERS, key),
+                              extra={"experts_touched": touched, "n_experts": n_exp, "tokens": n_tok, "top_k": top_k})
+
+    if "c4" in legs:
+        moe_entry("C4_moe_q4_0_16tok_top2_of_8", 8, cm["ids"], cm["gates"], banks)
+    if "moe1" in legs:
+        ids, gates = synth.moe_routing(synth.rng(0, 4, 10), 1, 8, 2)
+        moe_entry("moe_q4_0_1tok_top2_of_8", 8, ids, gates, banks)
+    if "moe64" not in legs:
+        return
+    # 64 experts per bank, two banks: expert e of bank c is expert e % 8 of the 8-expert bank
+    # (c + e) % 3 with its rows rolled by 13 (e // 8) + 5 c, so no two experts share content.
+    big = []
+    for c in range(2):
+        parts = []
+        for e in range(64):
+            src = banks[(c + e) % 3][(e % 8) * eb:(e % 8 + 1) * eb].view(m, -1)
+            parts.append(torch.roll(src, shifts=13 * (e // 8) + 5 * c, dims=0).reshape(-1))
+        big.append(torch.cat(parts))
+        del parts
+    del banks
+    ids, gates = synth.moe_routing(synth.rng(0, 4, 11), 16, 64, 2)
+    moe_entry("moe_q4_0_16tok_top2_of_64", 64, ids, gates, big)
+    del big
+
+
+def _others(torch, wq, synth, dev, timer, to_dev, args):
+    out = {}
+    R = args.reps
+    k = 4096
+    # f16 weights 4096 x 4096 at n = 1 (wavo Linear type 1), rotated copies
+    m16 = 4096
+    wb16 = wq.weight_bytes(wq.W_F16, m16, k)
+    nc16 = max(2, -(-ROTATE_BYTES // wb16))
+    base = to_dev(synth.weight(synth.rng(53), wq.W_F16, m16, k).reshape(-1).view(np.uint8))
+    Wc = _rotated(torch, base, m16, nc16)
+    x = to_dev(synth.normal_f32(synth.rng(54), (1, k), 1.0))
+    y = torch.empty((1, m16), device=dev)
+    gs = [wq.bind_gemm(x, Wc[i], wq.W_F16, m=m16, k=k, out=y) for i in range(nc16)]
+    st = _stats(timer.runs(lambda i: gs[i % nc16](), 100, R))
+    gbs = wb16 / (st["median_us"] * 1e-6) / 1e9
+    out["matvec_f16_4096x4096_n1"] = {**st, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    del Wc
+
+    # The MLP-up shape (X[1500 x 1024], W[4096 x 1024], bias + GELU) with other weight types.
+    n, d, ff = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_FF
+    a3 = to_dev(synth.encoder_activations()["a3"])
+    f = torch.empty((n, ff), device=dev)
+    fl = 2 * n * ff * d
+    for wt, name in ((wq.W_F16, "f16"), (wq.W_F32, "f32"), (wq.W_Q8_0, "q8_0"), (wq.W_Q4_0, "q4_0")):
+        ws = [to_dev(synth.weight(synth.rng(40 + i, wt), wt, ff, d).reshape(-1)) for i in range(4)]
+        bq = to_dev(synth.normal_f32(synth.rng(44, wt), (ff,), 0.1))
+        for path, suffix in ((wq.PATH_AUTO, ""), (wq.PATH_MFMA_F32, "_f32acc")):
+            if wt in (wq.W_F16, wq.W_F32) and suffix:
+                continue
+            gq = [wq.bind_gemm(a3, w_, wt, m=ff, k=d, bias=bq, gelu=True, out=f, path=path) for w_ in ws]
+            st = _stats(timer.runs(lambda i: gq[i % 4](), 20, R))
+            tf = fl / (st["median_us"] * 1e-6) / 1e12
+            out[f"gemm_{name}{suffix}_{n}x{ff}x{d}_gelu"] = {**st, "TFLOP/s": round(tf, 1),
+                                                              "frac": round(tf / BF16_PEAK_TFLOPS, 4)}
+        del ws
+    return out
+
+
+def _cpu_time(fn, runs):
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return float(np.median(ts))
+
+
+def _cpu_chain(synth, acts):
+    """The oracle on 2 of the chain's 24 layers, all 1500 frames: decode + f64 product + epilogue."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads", 0) for i in threadpool_info()), default=0)
-    except Exception:  # pragma: no cover
-        threads = 0
-    cores = len(os.sched_getaffinity(0))
-    rows = 512
-    c1, c4 = synth.config_q8_matvec(1), synth.config_q8_matvec(4)
-    w = c1["w"][:rows]
-    per_call = wq_bytes = 34 * rows * (4096 // 32)
-    done, t0 = 0, time.perf_counter()
-    while True:
-        for c in (c1, c4):
-            wf = oracle.decode(w, oracle.W_Q8_0, rows, 4096)
-            _ = oracle.epilogue(np.asarray(c["x"], np.float64) @ wf.T, 0)
-            done += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {
-        "value": round(done * per_call / el / 1e9, 4),
-        "unit": "GB/s",
-        "cores": threads or cores,
-        "kind": "oracle",
-        "sample": f"{rows} of 4096 weight rows of the Q8_0 4096x4096 decode workload, calls at n=1 and n=4 "
-                  f"alternating, {done} calls in {el:.1f} s (f64 decode + numpy product)",
-    }
+    n, d, ff = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_FF
+    x = {nm: np.asarray(acts[nm], np.float64) for nm in ("a1", "a2", "a3")}
+    h0 = np.asarray(acts["h0"], np.float64)
+    layers = [synth.encoder_layer_weights(L) for L in range(2)]
+
+    def run():
+        h = h0
+        for lw in layers:
+            def lin(a, key, flags, y_old=None):
+                w = oracle.decode(lw[key]["w"], oracle.W_BF16, lw[key]["m"], lw[key]["k"])
+                return oracle.epilogue(a @ w.T, flags, lw[key]["bias"], y_old)
+            lin(x["a1"], "qkv", 1)
+            h = lin(x["a2"], "out", 5, h)
+            fo = lin(x["a3"], "fc1", 3)
+            h = lin(fo, "fc2", 5, h)
+        return h
+
+    sec = _cpu_time(run, 1)
+    fl = 2 * 2 * n * (3 * d * d + d * d + ff * d + d * ff)
+    return {"value": round(fl / sec / 1e9, 2), "unit": "GFLOP/s", "cores": _threads(), "kind": "oracle",
+            "sample": f"2 of the 24 layers (all 1500 frames, all four GEMMs): {fl / 1e9:.1f} GFLOP in {sec:.2f} s, "
+                      "f64 decode + numpy product + epilogue"}
+
+
+def _cpu_configs(synth):
+    """The oracle on each matvec / MoE workload (C4: 2 of its 8 experts), median of 3 runs."""
+    import oracle
+    res = {}
+    cores = _threads()
+
+    def entry(sec, nbytes, sample, flop=None):
+        e = {"value": round(nbytes / sec / 1e9, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+             "sample": sample + f", median of 3 runs: {sec:.3f} s"}
+        if flop:
+            e = {"value": round(flop / sec / 1e9, 3), "unit": "GFLOP/s", "cores": cores, "kind": "oracle",
+                 "sample": sample + f", median of 3 runs: {sec:.4f} s"}
+        return e
+
+    c = synth.config_gemm_small()
+
+    def c1():
+        w = oracle.decode(c["w"], oracle.W_BF16, 256, 256)
+        oracle.epilogue(np.asarray(c["x"], np.float64) @ w.T, 3, c["bias"])
+    res["C1_gemm_bf16_64x256x256_gelu"] = entry(_cpu_time(c1, 3), 0, "the full call", flop=2 * 64 * 256 * 256)
+    for n_ in (1, 4):
+        cq = synth.config_q8_matvec(n_)
+
+        def c2():
+            w = oracle.decode(cq["w"], oracle.W_Q8_0, 4096, 4096)
+            np.asarray(cq["x"], np.float64) @ w.T
+        res[f"C2_q8_0_4096x4096_n{n_}"] = entry(_cpu_time(c2, 3), 17825792, "the full call")
+    c3c = synth.config_q4_matvec()
+
+    def c3():
+        w = oracle.decode(c3c["w"], oracle.W_Q4_0, 14336, 4096)
+        np.asarray(c3c["x"], np.float64) @ w.T
+    res["C3_q4_0_14336x4096_n1"] = entry(_cpu_time(c3, 3), 33030144, "the full call")
+    cm = synth.config_moe()
+    ids = cm["ids"]
+    experts = list(np.unique(ids))[:2]
+
+    def c4():
+        x64 = np.asarray(cm["x"], np.float64)
+        for e in experts:
+            w = oracle.decode(cm["w"][e], oracle.W_Q4_0, 14336, 4096)
+            t_idx, _ = np.nonzero(ids == e)
+            x64[t_idx] @ w.T
+    res["C4_moe_q4_0_16tok_top2_of_8"] = entry(_cpu_time(c4, 3), 2 * 33030144,
+                                               f"experts {experts[0]} and {experts[1]} of the 8 (their routed tokens)")
+    return res
 
 
 if __name__ == "__main__":

@@ -44,19 +44,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``gemv_wq_gemm_amd/libwq.so``; returns its path."""
-    os.makedirs(OBJDIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+# The bench's streaming-read floor: its own library, not part of the layer's ABI.
+BENCH_SOURCES = ["bench_read.hip"]
+BENCH_LIB = os.path.join(PKG, "libwq_bench.so")
+
+
+def _link(objs, lib) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``gemv_wq_gemm_amd/libwq.so`` (and the bench's
+    ``libwq_bench.so``); returns the layer library's path."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES) + len(BENCH_SOURCES))) as ex:
+        objs = list(ex.map(_compile, SOURCES + BENCH_SOURCES))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], BENCH_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {BENCH_LIB}")
     return LIB
 
 

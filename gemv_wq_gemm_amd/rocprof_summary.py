@@ -1,8 +1,8 @@
 """Short text summaries of rocprofv3 output, and the reader of the HBM byte counts they record.
 
     python -m gemv_wq_gemm_amd.rocprof_summary trace STATS_CSV OUT_MD --command CMD [--top N]
-    python -m gemv_wq_gemm_amd.rocprof_summary counters FETCH_CSV WRITE_CSV OUT_MD --command CMD \\
-        --kernel LABEL=SUBSTRING [...] --copy SUBSTRING --copy-bytes N
+    python -m gemv_wq_gemm_amd.rocprof_summary counters OUT_MD --run FETCH_CSV WRITE_CSV [--run ...] \\
+        --command CMD --kernel LABEL=[RUN:]SUBSTRING [...] --copy SUBSTRING --copy-bytes N
     python -m gemv_wq_gemm_amd.rocprof_summary pmc OUT_MD CSV [CSV ...] --command CMD --title T \\
         --kernel LABEL=SUBSTRING [...]
 
@@ -31,9 +31,11 @@ from collections import defaultdict
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 
-# The files the matvec kernels are built from (and the flags they are built with).
-KERNEL_SOURCES = ["csrc/wq_matvec_sliced.hip", "csrc/wq_matvec_mfma.hip", "csrc/wq_matvec.hip", "csrc/wq_decode.hpp",
-                  "csrc/wq_internal.hpp", "csrc/wq_lds_dma.hpp", "build.py"]
+# The files the kernels are built from (and the flags they are built with): counters taken with
+# other sources no longer describe the library.
+KERNEL_SOURCES = ["csrc/wq_matvec_sliced.hip", "csrc/wq_matvec_mfma.hip", "csrc/wq_matvec.hip", "csrc/wq_gemm.hip",
+                  "csrc/wq_decode.hpp", "csrc/wq_internal.hpp", "csrc/wq_lds_dma.hpp", "csrc/wq_moe_sched.hpp",
+                  "csrc/wq_tile_math.hpp", "build.py"]
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:
@@ -85,35 +87,47 @@ def _pick(acc: dict[str, list[float]], sub: str) -> tuple[str, list[float]]:
     return hits[0]
 
 
-def counter_summary(fetch_csv: str, write_csv: str, command: str, out: str, kernels: dict[str, str],
+def counter_summary(runs: list[tuple[str, str]], command: str, out: str, kernels: dict[str, str],
                     copy_sub: str, copy_bytes: int) -> str:
-    fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
-    write = _per_kernel(write_csv, "WRITE_SIZE")
-    _, cf = _pick(fetch, copy_sub)
-    _, cw = _pick(write, copy_sub)
-    cf_kib, cw_kib = sum(cf) / len(cf), sum(cw) / len(cw)
-    f_scale = copy_bytes / (cf_kib * 1024)
-    w_scale = copy_bytes / (cw_kib * 1024)
+    """HBM bytes per launch of the labelled kernels, from one or more profiled runs (each a FETCH_SIZE
+    CSV and a WRITE_SIZE CSV of the same command, each with its own copy calibration). A kernel is
+    named ``RUN:SUBSTRING`` (RUN the index of its run, 0 if omitted)."""
     lines = [
         "# HBM bytes per launch (FETCH_SIZE, WRITE_SIZE)",
         "",
-        f"Command (run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`",
+        f"Command (each run once with `--pmc FETCH_SIZE`, once with `--pmc WRITE_SIZE`): `{command}`",
         "",
-        f"Calibration: the copy kernel `{_short(_pick(fetch, copy_sub)[0], 70)}` reads and writes "
-        f"{copy_bytes} bytes; it counts FETCH_SIZE {cf_kib:.1f} KiB and WRITE_SIZE {cw_kib:.1f} KiB per "
-        f"dispatch, so read bytes = {f_scale:.3f} x FETCH_SIZE x 1024 and written bytes = "
-        f"{w_scale:.3f} x WRITE_SIZE x 1024.",
-        "",
-        "| label | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes |",
-        "|---|---|---:|---:|---:|---:|---:|",
     ]
+    scales = []
+    data = []
+    for i, (fetch_csv, write_csv) in enumerate(runs):
+        fetch = _per_kernel(fetch_csv, "FETCH_SIZE")
+        write = _per_kernel(write_csv, "WRITE_SIZE")
+        _, cf = _pick(fetch, copy_sub)
+        _, cw = _pick(write, copy_sub)
+        cf_kib, cw_kib = sum(cf) / len(cf), sum(cw) / len(cw)
+        f_scale = copy_bytes / (cf_kib * 1024)
+        w_scale = copy_bytes / (cw_kib * 1024)
+        scales.append((f_scale, w_scale))
+        data.append((fetch, write))
+        lines.append(f"Run {i} calibration: the copy kernel `{_short(_pick(fetch, copy_sub)[0], 70)}` reads and "
+                     f"writes {copy_bytes} bytes; it counts FETCH_SIZE {cf_kib:.1f} KiB and WRITE_SIZE {cw_kib:.1f} "
+                     f"KiB per dispatch, so read bytes = {f_scale:.3f} x FETCH_SIZE x 1024 and written bytes = "
+                     f"{w_scale:.3f} x WRITE_SIZE x 1024.")
+        lines.append("")
+    lines += ["| label | run | kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | read bytes | written bytes |",
+              "|---|---:|---|---:|---:|---:|---:|---:|"]
     tail = []
-    for label, sub in kernels.items():
+    for label, spec in kernels.items():
+        run, sub = (int(spec.split(":", 1)[0]), spec.split(":", 1)[1]) if ":" in spec and spec.split(":", 1)[0].isdigit() \
+            else (0, spec)
+        fetch, write = data[run]
+        f_scale, w_scale = scales[run]
         name, fv = _pick(fetch, sub)
         _, wv = _pick(write, sub)
         f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
         rd, wr = f_kib * 1024 * f_scale, w_kib * 1024 * w_scale
-        lines.append(f"| {label} | `{_short(name, 60)}` | {len(fv)} | {f_kib:.1f} | {w_kib:.1f} | "
+        lines.append(f"| {label} | {run} | `{_short(name, 60)}` | {len(fv)} | {f_kib:.1f} | {w_kib:.1f} | "
                      f"{rd:.0f} | {wr:.0f} |")
         tail.append(f"traffic {label} {rd + wr:.0f}")
     tail.append(f"source_digest {source_digest()}")
@@ -176,11 +190,12 @@ def main() -> None:
     t.add_argument("--command", required=True)
     t.add_argument("--top", type=int, default=16, help="kernels listed, by total time")
     c = sub.add_parser("counters")
-    c.add_argument("fetch_csv")
-    c.add_argument("write_csv")
     c.add_argument("out")
+    c.add_argument("--run", nargs=2, action="append", required=True, metavar=("FETCH_CSV", "WRITE_CSV"),
+                   help="one profiled run: its FETCH_SIZE and WRITE_SIZE CSVs (repeat for more runs)")
     c.add_argument("--command", required=True)
-    c.add_argument("--kernel", action="append", required=True, help="LABEL=SUBSTRING of the kernel name")
+    c.add_argument("--kernel", action="append", required=True,
+                   help="LABEL=[RUN:]SUBSTRING of the kernel name (RUN: index of its --run, default 0)")
     c.add_argument("--copy", required=True, help="substring of the calibration copy kernel's name")
     c.add_argument("--copy-bytes", type=int, required=True)
     q = sub.add_parser("pmc")
@@ -196,7 +211,7 @@ def main() -> None:
         print(pmc_summary(a.csvs, a.command, a.out, dict(kv.split("=", 1) for kv in a.kernel), a.title))
     else:
         kernels = dict(kv.split("=", 1) for kv in a.kernel)
-        print(counter_summary(a.fetch_csv, a.write_csv, a.command, a.out, kernels, a.copy, a.copy_bytes))
+        print(counter_summary([tuple(r) for r in a.run], a.command, a.out, kernels, a.copy, a.copy_bytes))
 
 
 if __name__ == "__main__":
