@@ -733,11 +733,23 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Test hook: with WQ_GEMM_WIDE_OFFSETS=1 in the environment (read once per process), every bf16
+// GEMM takes the route that X or W of 4 GiB or more take, so that route can be checked at
+// shapes a test can afford.
+bool force_wide_offsets() {
+  static const bool on = [] {
+    const char* v = std::getenv("WQ_GEMM_WIDE_OFFSETS");
+    return v != nullptr && v[0] == '1' && v[1] == '\0';
+  }();
+  return on;
+}
+
 template <int WT>
 hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
-  // The pipelined bf16 kernel addresses operands with 32-bit byte offsets.
+  // The pipelined bf16 kernel addresses operands with 32-bit byte offsets; larger operands take
+  // gemm_kernel, whose offsets are 64-bit.
   const bool small_enough = static_cast<long long>(p.n) * p.k * 4 < (1LL << 32) &&
-                            static_cast<long long>(p.m) * p.rowbytes < (1LL << 32);
+                            static_cast<long long>(p.m) * p.rowbytes < (1LL << 32) && !force_wide_offsets();
   if constexpr (WT == kBF16) {
     if (!small_enough) return launch_tile<WT, 128, 128, 2, 2>(p, stream);
     const long long wide_tiles = static_cast<long long>((p.n + 127) / 128) * ((p.m + 255) / 256);

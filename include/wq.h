@@ -49,7 +49,8 @@
  *     the chip and the epilogue is WQ_RESIDUAL with no activation. That call
  *     splits k across workgroups that add their partial sums into Y with f32
  *     atomics, so the order of those additions (and the last bits of Y) may
- *     differ between runs. bf16 weights never take it.
+ *     differ between runs. bf16 weights take it only when X or W reaches
+ *     4 GiB: operands that large run on the same kernel as the other types.
  */
 #ifndef WQ_H
 #define WQ_H

@@ -4,8 +4,11 @@ Every entry point may be called concurrently (include/wq.h). The gated MoE call 
 shared host state: a per-(device, stream) combine workspace that a call may have to grow while
 another thread's work on the same stream still reads the old one. Each thread here repeats a
 sequence of calls whose MoE sizes force that growth; the results must equal, bit for bit, those
-of the same calls made one at a time (the kernels sum in a fixed order, so a race shows as a
-difference), and the one-at-a-time MoE results are checked against the oracle.
+of the same calls made one at a time, and the one-at-a-time MoE results are checked against the
+oracle. Every call made here sums in a fixed order, so a race shows as a difference. (The one route
+that does not, the k split of residual layers without activation on quantized, f16 and f32 weights
+at few tiles, is not among them: the Q8_0 call has 4 rows and takes the matvec, and the bf16 GEMM
+has GELU.)
 """
 import threading
 
