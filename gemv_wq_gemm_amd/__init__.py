@@ -42,6 +42,13 @@ SIGNATURES = [
     ("wq_padded_k", _I64, [_I64]),
     ("wq_weight_bytes", _I64, [_I, _I64, _I64]),
     ("wq_gemm_path", _I, [_I64, _I64, _I64, _I]),
+    ("wq_layer_norm", _I, [_P, _P, _P, _I64, _I64, _P]),
+    ("wq_rope_table", _I, [_P, _I64, _I64]),
+    ("wq_qk_norm_rope", _I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, _P]),
+    ("wq_attention_workspace_bytes", _I64, [_I64, _I64, _I64]),
+    ("wq_attention", _I, [_P, _P, _P, _P, _I64, _I64, _I64, _I64, ctypes.c_float, _P]),
+    ("wq_encoder_workspace_bytes", _I64, [_I64, _I64, _I64, _I64]),
+    ("wq_encoder_layer", _I, [_P, _I, _P, _P, _P, _P, _I64, _I64, _I64, _I64, _I64, _I64, _I, _P]),
     ("wq_last_error", ctypes.c_char_p, []),
     ("wq_version", ctypes.c_char_p, []),
 ]
@@ -259,3 +266,126 @@ def pad_weight(w, wtype: int, *, m: int, k: int, out=None):
     st = lib().wq_pad_weight(_dev(w, "w"), wtype, _f32(out, "out", m * kp), m, k, _stream())
     _check(st)
     return out
+
+
+# ---- the encoder block -----------------------------------------------------------------------
+
+class EncoderLayerDesc(ctypes.Structure):
+    """``wq_encoder_layer_t``: device pointers of one block's weights (NULL where absent)."""
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("ln1", "qkv_w", "qkv_b", "qn", "kn", "out_w", "out_b", "ln2", "fc1_w", "fc1_b", "fc2_w", "fc2_b")]
+
+
+def layer_norm(x, wb, *, d: int, out=None):
+    """Row LayerNorm (eps 1e-5) of ``x[n][d]`` with ``wb = [w | b]`` via ``wq_layer_norm``;
+    ``out`` may be ``x`` (in place)."""
+    import torch
+    n = x.numel() // d
+    if x.numel() != n * d:
+        raise ValueError("x must hold n*d elements")
+    if out is None:
+        out = torch.empty((n, d), dtype=torch.float32, device=x.device)
+    _check(lib().wq_layer_norm(_f32(x, "x"), _f32(wb, "wb", 2 * d), _f32(out, "out", n * d), n, d, _stream()))
+    return out
+
+
+def rope_table(n: int, rot: int):
+    """The host-built f32 rotation table ``[cos n*rot/2 | sin n*rot/2]`` (``wq_rope_table``), as a
+    CPU tensor."""
+    import torch
+    cs = torch.empty(n * rot, dtype=torch.float32)
+    _check(lib().wq_rope_table(ctypes.c_void_p(cs.data_ptr()), n, rot))
+    return cs
+
+
+def qk_norm_rope(qkv, cs, *, n: int, heads: int, hd: int, rot: int, qn=None, kn=None):
+    """In place on ``qkv[n][3*heads*hd]``: per-head q/k LayerNorm (when ``qn``/``kn``) and the
+    rotation of the first ``rot`` dims by the table ``cs`` (a device tensor), via
+    ``wq_qk_norm_rope``. Returns ``qkv``."""
+    _check(lib().wq_qk_norm_rope(
+        _f32(qkv, "qkv", n * 3 * heads * hd), None if qn is None else _f32(qn, "qn", 2 * hd),
+        None if kn is None else _f32(kn, "kn", 2 * hd), None if cs is None else _f32(cs, "cs", n * rot),
+        n, heads, hd, rot, _stream()))
+    return qkv
+
+
+def attention_workspace_bytes(n: int, heads: int, hd: int) -> int:
+    r = int(lib().wq_attention_workspace_bytes(n, heads, hd))
+    if r < 0:
+        raise ValueError(f"invalid attention sizes n={n}, heads={heads}, hd={hd}")
+    return r
+
+
+def _workspace(nbytes: int, device, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace has {workspace.numel() * workspace.element_size()} bytes, needs {nbytes}")
+    return workspace
+
+
+def attention(qkv, valid, *, n: int, heads: int, hd: int, scale: float, out=None, workspace=None):
+    """Masked bidirectional attention over ``qkv[n][3*heads*hd]`` (``valid`` int32 ``[n]``) via
+    ``wq_attention``; returns ``out[n][heads*hd]``. ``workspace`` (device bytes, 256-byte aligned)
+    is allocated when not given."""
+    import torch
+    if valid.dtype != torch.int32:
+        raise ValueError("valid must be int32")
+    if out is None:
+        out = torch.empty((n, heads * hd), dtype=torch.float32, device=qkv.device)
+    ws = _workspace(attention_workspace_bytes(n, heads, hd), qkv.device, workspace)
+    _check(lib().wq_attention(_f32(qkv, "qkv", n * 3 * heads * hd), _dev(valid, "valid"),
+                              _f32(out, "out", n * heads * hd), _dev(ws, "workspace"),
+                              ws.numel() * ws.element_size(), n, heads, hd, float(scale), _stream()))
+    return out
+
+
+def encoder_workspace_bytes(n: int, d: int, heads: int, inter: int) -> int:
+    r = int(lib().wq_encoder_workspace_bytes(n, d, heads, inter))
+    if r < 0:
+        raise ValueError(f"invalid encoder sizes n={n}, d={d}, heads={heads}, inter={inter}")
+    return r
+
+
+def encoder_layer_desc(layer: dict) -> EncoderLayerDesc:
+    """The C descriptor of one block from a dict of device tensors (keys as the struct's fields;
+    ``qkv_b``, ``qn`` and ``kn`` may be missing or None). The tensors must outlive its use."""
+    def ptr(key):
+        t = layer.get(key)
+        return None if t is None else _dev(t, key).value
+    return EncoderLayerDesc(*[ptr(name) for name, _ in EncoderLayerDesc._fields_])
+
+
+def encoder_layer(h, layer, wtype: int, valid, cs, *, n: int, d: int, heads: int, rot: int, inter: int,
+                  path: int = PATH_AUTO, workspace=None):
+    """One pre-norm block in place on ``h[n][d]`` via ``wq_encoder_layer``. ``layer`` is a dict of
+    device tensors or an :class:`EncoderLayerDesc`; ``cs`` the device rotation table."""
+    desc = layer if isinstance(layer, EncoderLayerDesc) else encoder_layer_desc(layer)
+    ws = _workspace(encoder_workspace_bytes(n, d, heads, inter), h.device, workspace)
+    _check(lib().wq_encoder_layer(
+        ctypes.byref(desc), wtype, _f32(h, "h", n * d), _dev(valid, "valid"),
+        None if cs is None else _f32(cs, "cs", n * rot), _dev(ws, "workspace"), ws.numel() * ws.element_size(),
+        n, d, heads, rot, inter, path, _stream()))
+    return h
+
+
+def encoder_forward(x, model: dict, wtype: int, valid, *, heads: int, rot: int, path: int = PATH_AUTO,
+                    workspace=None):
+    """``AudioEncoder::run``: optional input projection ``model["proj"]`` (no bias), the embedding
+    LayerNorm, every block of ``model["layers"]`` (dicts of device tensors) and the final LayerNorm.
+    Returns ``[n][d]``. Every step is a library call; nothing is computed here."""
+    import torch
+    n = x.shape[0]
+    d = model["embed_norm"].numel() // 2
+    inter = model["layers"][0]["fc1_b"].numel() if model["layers"] else 32
+    if model.get("proj") is not None:
+        x = gemm(x, model["proj"], wtype, m=d, k=x.shape[1], path=path)
+    cs = rope_table(n, rot).to(x.device) if rot > 0 else None
+    h = layer_norm(x, model["embed_norm"], d=d)
+    ws = _workspace(encoder_workspace_bytes(n, d, heads, inter), x.device, workspace)
+    for layer in model["layers"]:
+        encoder_layer(h, layer, wtype, valid, cs, n=n, d=d, heads=heads, rot=rot, inter=inter, path=path,
+                      workspace=ws)
+    return layer_norm(h, model["final_norm"], d=d, out=torch.empty_like(h))
+

@@ -379,6 +379,191 @@ int wq_pad_weight(const void* w, int wtype, float* out, int64_t m, int64_t k, vo
   return WQ_OK;
 }
 
+// ---- encoder block ------------------------------------------------------------------------------
+
+int wq_layer_norm(const float* x, const float* wb, float* y, int64_t n, int64_t d, void* stream) {
+  clear_error();
+  if (n < 0 || d < 1) return fail(WQ_ERR_SHAPE, "need n >= 0 and d >= 1, got n = %lld, d = %lld", (long long)n, (long long)d);
+  if (n > kMaxRows || d > kIntMax / 2) return fail(WQ_ERR_SHAPE, "n or d too large");
+  if (n > 0 && d > kMaxOutputs / n) return fail(WQ_ERR_SHAPE, "n * d exceeds 2^40");
+  if (n == 0) return WQ_OK;
+  if (!x || !wb || !y) return fail(WQ_ERR_NULL, "x, wb and y must not be NULL");
+  if (!aligned(x, 4) || !aligned(wb, 4) || !aligned(y, 4)) return fail(WQ_ERR_ALIGN, "x, wb and y must be 4-byte aligned");
+  const int64_t bytes = n * d * 4;
+  if ((y != x && overlap(y, bytes, x, bytes)) || overlap(y, bytes, wb, 2 * d * 4))
+    return fail(WQ_ERR_ALIAS, "y overlaps wb, or overlaps x without being x");
+  hipError_t e = wq::launch_layer_norm(x, wb, y, static_cast<int>(n), static_cast<int>(d),
+                                       static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "layer norm launch");
+  return WQ_OK;
+}
+
+int wq_rope_table(float* cs, int64_t n, int64_t rot) {
+  clear_error();
+  if (n < 0 || rot < 2 || rot % 2 != 0) return fail(WQ_ERR_SHAPE, "need n >= 0 and an even rot >= 2");
+  if (n > kMaxRows || rot > kIntMax / 2 || (n > 0 && rot > kMaxOutputs / n)) return fail(WQ_ERR_SHAPE, "n * rot too large");
+  if (n == 0) return WQ_OK;
+  if (!cs) return fail(WQ_ERR_NULL, "cs must not be NULL");
+  const int64_t half = rot / 2;
+  for (int64_t i = 0; i < half; ++i) {
+    const float inv = 1.0f / std::pow(10000.0f, static_cast<float>(2 * i) / static_cast<float>(rot));
+    for (int64_t t = 0; t < n; ++t) {
+      const float ang = static_cast<float>(t) * inv;
+      cs[t * half + i] = std::cos(ang);
+      cs[n * half + t * half + i] = std::sin(ang);
+    }
+  }
+  return WQ_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+int qk_checked(float* qkv, const float* qn, const float* kn, const float* cs, int64_t n, int64_t heads, int64_t hd,
+               int64_t rot, void* stream) {
+  if (n < 0 || heads < 1 || hd < 1 || hd > 256) return fail(WQ_ERR_SHAPE, "need n >= 0, heads >= 1 and 1 <= hd <= 256");
+  if (rot < 0 || rot > hd || rot % 2 != 0) return fail(WQ_ERR_SHAPE, "rot must be even and in [0, hd], got %lld", (long long)rot);
+  if (n > (int64_t(1) << 22) || heads > (int64_t(1) << 20) || n * heads * hd * 3 > kMaxOutputs)
+    return fail(WQ_ERR_SHAPE, "n, heads or n * 3 * heads * hd too large");
+  if ((qn == nullptr) != (kn == nullptr)) return fail(WQ_ERR_NULL, "give both qn and kn, or neither");
+  if (n == 0) return WQ_OK;
+  if (!qkv || (rot > 0 && !cs)) return fail(WQ_ERR_NULL, "qkv (and cs when rot > 0) must not be NULL");
+  if (!aligned(qkv, 4) || (qn && !aligned(qn, 4)) || (kn && !aligned(kn, 4)) || (cs && !aligned(cs, 4)))
+    return fail(WQ_ERR_ALIGN, "qkv, qn, kn and cs must be 4-byte aligned");
+  const int64_t bytes = n * 3 * heads * hd * 4;
+  if (overlap(qkv, bytes, qn, 2 * hd * 4) || overlap(qkv, bytes, kn, 2 * hd * 4) || overlap(qkv, bytes, cs, n * rot * 4))
+    return fail(WQ_ERR_ALIAS, "qn, kn or cs overlaps qkv");
+  hipError_t e = wq::launch_qk_norm_rope(qkv, qn, kn, cs, static_cast<int>(n), static_cast<int>(heads),
+                                         static_cast<int>(hd), static_cast<int>(rot), static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "q/k norm launch");
+  return WQ_OK;
+}
+
+bool attention_sizes_ok(int64_t n, int64_t heads, int64_t hd) {
+  // heads is a grid dimension of the pack kernel (at most 65535); 4096 is far beyond any model.
+  return n >= 0 && n <= (int64_t(1) << 22) && heads >= 1 && heads <= 4096 && hd >= 1 && hd <= 128 &&
+         n * heads * hd * 3 <= kMaxOutputs;
+}
+
+int attention_checked(const float* qkv, const int32_t* valid, float* o, void* ws, int64_t ws_bytes, int64_t n,
+                      int64_t heads, int64_t hd, float scale, void* stream) {
+  if (!attention_sizes_ok(n, heads, hd))
+    return fail(WQ_ERR_SHAPE, "need 0 <= n <= 2^22, 1 <= heads <= 4096, 1 <= hd <= 128 (n = %lld, heads = %lld, hd = %lld)",
+                (long long)n, (long long)heads, (long long)hd);
+  if (!std::isfinite(scale)) return fail(WQ_ERR_FLAGS, "scale must be finite");
+  if (n == 0) return WQ_OK;
+  if (!qkv || !valid || !o || !ws) return fail(WQ_ERR_NULL, "qkv, valid, o and workspace must not be NULL");
+  if (!aligned(qkv, 4) || !aligned(valid, 4) || !aligned(o, 4) || !aligned(ws, 256))
+    return fail(WQ_ERR_ALIGN, "qkv, valid and o must be 4-byte aligned, the workspace 256-byte aligned");
+  const int64_t need = static_cast<int64_t>(wq::attention_workspace_bytes(n, heads, hd));
+  if (ws_bytes < need)
+    return fail(WQ_ERR_SHAPE, "the workspace holds %lld bytes, %lld needed", (long long)ws_bytes, (long long)need);
+  const int64_t obytes = n * heads * hd * 4;
+  if (overlap(o, obytes, qkv, 3 * obytes) || overlap(o, obytes, valid, n * 4) || overlap(o, obytes, ws, need) ||
+      overlap(ws, need, qkv, 3 * obytes) || overlap(ws, need, valid, n * 4))
+    return fail(WQ_ERR_ALIAS, "o or the workspace overlaps qkv, valid or each other");
+  hipError_t e = wq::launch_attention(qkv, valid, o, ws, static_cast<int>(n), static_cast<int>(heads),
+                                      static_cast<int>(hd), scale, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "attention launch");
+  return WQ_OK;
+}
+
+// Layout of wq_encoder_layer's workspace: a [n][d], qkv [n][3d], att [n][d], f [n][inter], then
+// the attention workspace; each part starts on a 256-byte boundary.
+struct EncoderWs {
+  int64_t a, qkv, att, f, attn, total;
+};
+
+EncoderWs encoder_ws(int64_t n, int64_t d, int64_t heads, int64_t inter) {
+  auto up = [](int64_t b) { return (b + 255) / 256 * 256; };
+  EncoderWs w{};
+  w.a = 0;
+  w.qkv = w.a + up(n * d * 4);
+  w.att = w.qkv + up(n * 3 * d * 4);
+  w.f = w.att + up(n * d * 4);
+  w.attn = w.f + up(n * inter * 4);
+  w.total = w.attn + static_cast<int64_t>(wq::attention_workspace_bytes(n, heads, d / heads));
+  return w;
+}
+
+bool encoder_sizes_ok(int64_t n, int64_t d, int64_t heads, int64_t inter) {
+  return n >= 0 && n <= (int64_t(1) << 22) && d >= 32 && d % 32 == 0 && d <= kIntMax / 4 && inter >= 32 &&
+         inter % 32 == 0 && inter <= kIntMax / 4 && heads >= 1 && d % heads == 0 && d / heads <= 128 &&
+         n * 3 * d <= kMaxOutputs && n * inter <= kMaxOutputs;
+}
+
+}  // namespace
+
+extern "C" {
+
+int wq_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int64_t n, int64_t heads,
+                    int64_t hd, int64_t rot, void* stream) {
+  clear_error();
+  return qk_checked(qkv, qn, kn, cs, n, heads, hd, rot, stream);
+}
+
+int64_t wq_attention_workspace_bytes(int64_t n, int64_t heads, int64_t hd) {
+  if (!attention_sizes_ok(n, heads, hd)) return -1;
+  return static_cast<int64_t>(wq::attention_workspace_bytes(n, heads, hd));
+}
+
+int wq_attention(const float* qkv, const int32_t* valid, float* o, void* workspace, int64_t workspace_bytes,
+                 int64_t n, int64_t heads, int64_t hd, float scale, void* stream) {
+  clear_error();
+  return attention_checked(qkv, valid, o, workspace, workspace_bytes, n, heads, hd, scale, stream);
+}
+
+int64_t wq_encoder_workspace_bytes(int64_t n, int64_t d, int64_t heads, int64_t inter) {
+  if (!encoder_sizes_ok(n, d, heads, inter)) return -1;
+  return encoder_ws(n, d, heads, inter).total;
+}
+
+int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int32_t* valid, const float* cs,
+                     void* workspace, int64_t workspace_bytes, int64_t n, int64_t d, int64_t heads, int64_t rot,
+                     int64_t inter, int path, void* stream) {
+  clear_error();
+  if (!encoder_sizes_ok(n, d, heads, inter))
+    return fail(WQ_ERR_SHAPE,
+                "need 0 <= n <= 2^22, d and inter positive multiples of 32, d %% heads == 0 and d / heads <= 128");
+  const int64_t hd = d / heads;
+  if (rot < 0 || rot > hd || rot % 2 != 0) return fail(WQ_ERR_SHAPE, "rot must be even and in [0, hd]");
+  if (path != WQ_PATH_AUTO && path != WQ_PATH_MFMA && path != WQ_PATH_MFMA_F32)
+    return fail(WQ_ERR_SHAPE, "path must be WQ_PATH_AUTO, WQ_PATH_MFMA or WQ_PATH_MFMA_F32");
+  if (int r = check_wtype(wtype)) return r;
+  if (!l) return fail(WQ_ERR_NULL, "layer must not be NULL");
+  if (!l->ln1 || !l->qkv_w || !l->out_w || !l->out_b || !l->ln2 || !l->fc1_w || !l->fc1_b || !l->fc2_w || !l->fc2_b)
+    return fail(WQ_ERR_NULL, "every layer weight except qkv_b, qn and kn must be given");
+  if ((l->qn == nullptr) != (l->kn == nullptr)) return fail(WQ_ERR_NULL, "give both qn and kn, or neither");
+  if (n == 0) return WQ_OK;
+  if (!h || !valid || !workspace || (rot > 0 && !cs)) return fail(WQ_ERR_NULL, "h, valid, workspace (and cs) must not be NULL");
+  if (!aligned(h, 16) || !aligned(workspace, 256))
+    return fail(WQ_ERR_ALIGN, "h must be 16-byte aligned and the workspace 256-byte aligned");
+  const EncoderWs w = encoder_ws(n, d, heads, inter);
+  if (workspace_bytes < w.total)
+    return fail(WQ_ERR_SHAPE, "the workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)w.total);
+  if (overlap(h, n * d * 4, workspace, w.total)) return fail(WQ_ERR_ALIAS, "h overlaps the workspace");
+  uint8_t* base = static_cast<uint8_t*>(workspace);
+  float* a = reinterpret_cast<float*>(base + w.a);
+  float* qkv = reinterpret_cast<float*>(base + w.qkv);
+  float* att = reinterpret_cast<float*>(base + w.att);
+  float* f = reinterpret_cast<float*>(base + w.f);
+  void* attn_ws = base + w.attn;
+  const float scale = 1.0f / std::sqrt(static_cast<float>(hd));
+  int r;
+  if ((r = wq_layer_norm(h, l->ln1, a, n, d, stream))) return r;
+  if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, path, stream)))
+    return r;
+  clear_error();
+  if ((r = qk_checked(qkv, l->qn, l->kn, cs, n, heads, hd, rot, stream))) return r;
+  if ((r = attention_checked(qkv, valid, att, attn_ws, w.total - w.attn, n, heads, hd, scale, stream))) return r;
+  if ((r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, path, stream)))
+    return r;
+  if ((r = wq_layer_norm(h, l->ln2, a, n, d, stream))) return r;
+  if ((r = gemm_checked(a, l->fc1_w, wtype, l->fc1_b, WQ_BIAS | WQ_GELU, 1.0f, f, n, inter, d, 0, path, stream))) return r;
+  return gemm_checked(f, l->fc2_w, wtype, l->fc2_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, inter, 0, path, stream);
+}
+
 const char* wq_last_error(void) { return g_err; }
 
 const char* wq_version(void) { return "wq 0.1.0 (gfx950)"; }

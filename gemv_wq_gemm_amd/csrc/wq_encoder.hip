@@ -1,0 +1,524 @@
+// The encoder block around the linear layer: row LayerNorm, per-head q/k LayerNorm with the
+// rotary embedding, and masked bidirectional attention -- the `ae_ln`, `ae_qk` and `ae_attn`
+// kernels of cortiq-engine src/gpu_wgpu/nemotron_audio.rs (`AE_WGSL`) and the order
+// `AudioEncoder::run` runs them in.
+//
+// Design for gfx950:
+//  * LayerNorm: one wave per row. The row is held in registers as float4s (d <= 4096, d a multiple
+//    of 4, 16-byte aligned rows); the mean and then the summed squared deviations come from
+//    butterfly sums across the wave (two passes over registers, as the page's two passes over
+//    memory). Other rows take a scalar kernel that reads the row three times. HBM-bound: 8·d bytes
+//    per row.
+//  * q/k norm + rotation: one wave per (frame, head, q or k) vector, in place. The normalised
+//    vector goes through wave-private LDS so each lane can read its rotation partner (dim i pairs
+//    with dim i + rot/2). HBM-bound: 16·hd bytes per vector.
+//  * Attention, in two kernels:
+//     - pack: K and V of every head to bf16 (round to nearest even), K as [head][frame][dim] and V
+//       transposed as [head][dim][frame], frames padded to a multiple of 64; and the key mask as an
+//       additive bias (0 for a valid key, -inf for a masked or padding one). These layouts let the
+//       attention kernel stream 64-key tiles into LDS with direct-to-LDS loads.
+//     - attention: flash-style, f32 online softmax, bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
+//       for both products. A workgroup of 4 waves takes 64 queries of one head, 16 per wave, and
+//       walks all key tiles. Each wave computes S^T = K.Q^T (keys in rows, its 16 queries in
+//       columns), so a lane's scores all belong to one query: the row maximum and the sum need
+//       only in-lane work plus two cross-lane steps, and the probabilities are already the B
+//       operand of O^T = V^T.P^T. Work items are numbered head-major and dealt to the 8 XCDs in
+//       contiguous ranges, so each XCD's L2 holds the K and V of few heads.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "wq_internal.hpp"
+#include "wq_lds_dma.hpp"
+
+namespace wq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLnEps = 1e-5f;
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max16(float v) {
+  // Max over the four lane groups of 16 that share a lane index mod 16.
+  v = fmaxf(v, __shfl_xor(v, 16));
+  return fmaxf(v, __shfl_xor(v, 32));
+}
+
+__device__ __forceinline__ float sum_groups16(float v) {
+  v += __shfl_xor(v, 16);
+  return v + __shfl_xor(v, 32);
+}
+
+__device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
+  return __builtin_bit_cast(uint16_t, static_cast<__bf16>(v));
+}
+
+// ---------------------------------------------------------------------------------------------
+// LayerNorm
+// ---------------------------------------------------------------------------------------------
+
+// NV float4s per lane: d <= 256·NV, d % 4 == 0, x / y rows and wb 16-byte aligned.
+template <int NV>
+__global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, const float* __restrict__ wb, float* y,
+                                                              int n, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;  // wave-uniform; no barrier follows
+  const int nv = d >> 2;
+  const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+  float4 v[NV];
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    v[i] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
+  }
+  const float fd = static_cast<float>(d);
+  const float mean = wave_sum(s) / fd;
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    if (lane + 64 * i < nv) {
+      const float a = v[i].x - mean, b = v[i].y - mean, c = v[i].z - mean, e = v[i].w - mean;
+      q += (a * a + b * b) + (c * c + e * e);
+    }
+  }
+  const float inv = rsqrtf(wave_sum(q) / fd + kLnEps);
+  const float4* w4 = reinterpret_cast<const float4*>(wb);
+  float4* yr = reinterpret_cast<float4*>(y + row * d);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = lane + 64 * i;
+    if (c < nv) {
+      const float4 w = w4[c], b = w4[nv + c];
+      yr[c] = make_float4((v[i].x - mean) * inv * w.x + b.x, (v[i].y - mean) * inv * w.y + b.y,
+                          (v[i].z - mean) * inv * w.z + b.z, (v[i].w - mean) * inv * w.w + b.w);
+    }
+  }
+}
+
+// Any d and alignment: three passes over the row in memory, one wave per row. In place is safe:
+// a lane writes y[i] only after every lane of the wave has read the row for the second time.
+__global__ __launch_bounds__(256) void layer_norm_scalar_kernel(const float* x, const float* __restrict__ wb,
+                                                                 float* y, int n, int d) {
+  const int lane = threadIdx.x & 63;
+  const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (row >= n) return;
+  const float* xr = x + row * d;
+  float s = 0.f;
+  for (int i = lane; i < d; i += 64) s += xr[i];
+  const float fd = static_cast<float>(d);
+  const float mean = wave_sum(s) / fd;
+  float q = 0.f;
+  for (int i = lane; i < d; i += 64) {
+    const float c = xr[i] - mean;
+    q += c * c;
+  }
+  const float inv = rsqrtf(wave_sum(q) / fd + kLnEps);
+  float* yr = y + row * d;
+  for (int i = lane; i < d; i += 64) yr[i] = (xr[i] - mean) * inv * wb[i] + wb[d + i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// q/k LayerNorm + rotation
+// ---------------------------------------------------------------------------------------------
+
+// E elements per lane (hd <= 64·E). Every wave reaches the barrier; waves past the last vector
+// only skip their loads and stores.
+template <int E>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(float* qkv, const float* __restrict__ qn,
+                                                            const float* __restrict__ kn,
+                                                            const float* __restrict__ cs, int n, int heads, int hd,
+                                                            int rot) {
+  __shared__ float vbuf[4][64 * E];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const long long vec = static_cast<long long>(blockIdx.x) * 4 + wave;
+  const bool live = vec < 2LL * n * heads;
+  const long long t = live ? vec / (2 * heads) : 0;
+  const int rem = static_cast<int>(vec - t * 2 * heads);
+  const int which = live ? rem / heads : 0;  // 0: q, 1: k
+  const int h = live ? rem % heads : 0;
+  const long long d = static_cast<long long>(heads) * hd;
+  float* base = qkv + t * 3 * d + which * d + static_cast<long long>(h) * hd;
+
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    v[e] = live && i < hd ? base[i] : 0.f;
+  }
+  const float* nw = which == 0 ? qn : kn;
+  if (nw != nullptr) {  // uniform: both or neither are given
+    float s = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) s += v[e];
+    const float fhd = static_cast<float>(hd);
+    const float mean = wave_sum(s) / fhd;
+    float q = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float c = lane + 64 * e < hd ? v[e] - mean : 0.f;
+      q += c * c;
+    }
+    const float inv = rsqrtf(wave_sum(q) / fhd + kLnEps);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int i = lane + 64 * e;
+      if (live && i < hd) v[e] = (v[e] - mean) * inv * nw[i] + nw[hd + i];
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) vbuf[wave][lane + 64 * e] = v[e];
+  __syncthreads();
+  const int half = rot >> 1;
+  const float* cos_t = cs + t * half;
+  const float* sin_t = cs + static_cast<long long>(n) * half + t * half;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    if (!live || i >= hd) continue;
+    float o = v[e];
+    if (i < half) {
+      o = v[e] * cos_t[i] - vbuf[wave][i + half] * sin_t[i];
+    } else if (i < rot) {
+      const int j = i - half;
+      o = v[e] * cos_t[j] + vbuf[wave][j] * sin_t[j];
+    }
+    base[i] = o;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Attention: pack
+// ---------------------------------------------------------------------------------------------
+
+constexpr int kKeyTile = 64;    // keys per tile
+constexpr int kQueryTile = 64;  // queries per workgroup (16 per wave)
+
+// Grid (npad / 64, heads). K: kb[h][t][0..HDP) bf16; V: vt[h][0..HDP)[t] bf16; dims past hd and
+// frames past n are zero. Head 0's workgroups also write the key bias.
+template <int HDP>
+__global__ __launch_bounds__(256) void attn_pack_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ valid,
+                                                         uint16_t* __restrict__ kb, uint16_t* __restrict__ vt,
+                                                         float* __restrict__ kbias, int n, int npad, int heads, int hd) {
+  __shared__ uint16_t vs[kKeyTile][HDP + 2];  // V tile, frame-major, for the transposed write
+  const int t0 = blockIdx.x * kKeyTile;
+  const int h = blockIdx.y;
+  const long long d = static_cast<long long>(heads) * hd;
+  const float* kbase = qkv + d + static_cast<long long>(h) * hd;
+  const float* vbase = qkv + 2 * d + static_cast<long long>(h) * hd;
+  uint16_t* kout = kb + (static_cast<long long>(h) * npad + t0) * HDP;
+  for (int i = threadIdx.x; i < kKeyTile * HDP; i += 256) {
+    const int r = i / HDP, c = i % HDP;
+    const int t = t0 + r;
+    const bool in = t < n && c < hd;
+    const long long off = static_cast<long long>(t) * 3 * d + c;
+    kout[i] = in ? bf16_bits_rne(kbase[off]) : uint16_t(0);
+    vs[r][c] = in ? bf16_bits_rne(vbase[off]) : uint16_t(0);
+  }
+  if (h == 0 && threadIdx.x < kKeyTile) {
+    const int t = t0 + threadIdx.x;
+    kbias[t] = t < n && valid[t] != 0 ? 0.f : -INFINITY;
+  }
+  __syncthreads();
+  // vt[h][c][t0 .. t0+63]: 8 keys (16 bytes) per store.
+  uint16_t* vout = vt + static_cast<long long>(h) * HDP * npad + t0;
+  for (int i = threadIdx.x; i < HDP * (kKeyTile / 8); i += 256) {
+    const int c = i / (kKeyTile / 8), g = i % (kKeyTile / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(vs[8 * g + 2 * j][c]) | (static_cast<uint32_t>(vs[8 * g + 2 * j + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(vout + static_cast<long long>(c) * npad + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Attention
+// ---------------------------------------------------------------------------------------------
+
+struct AttnParams {
+  const float* qkv;
+  const uint16_t* kb;
+  const uint16_t* vt;
+  const float* kbias;
+  float* o;
+  int n, npad, heads, hd;
+  int qtiles;      // query tiles per head
+  int items;       // heads * qtiles
+  int per_xcd;     // ceil(items / 8)
+  float scale_l2;  // scale * log2(e): scores enter exp2
+};
+
+// LDS tile layout (one buffer):
+//   K  [64 keys][HDP] bf16, 16-byte chunks XOR-swizzled by (key & (CPR-1)), CPR = HDP/8 chunks a row;
+//   Vt [HDP dims][64 keys] bf16, chunks swizzled by (dim & 7);
+//   bias [64] f32.
+template <int HDP>
+struct AttnLds {
+  static constexpr int kCpr = HDP / 8;                     // 16-byte chunks per K row
+  static constexpr int kKBytes = kKeyTile * HDP * 2;       // 1 KB per 512/HDP rows
+  static constexpr int kVBytes = HDP * kKeyTile * 2;
+  static constexpr int kBiasBytes = kKeyTile * 4;
+  static constexpr int kBufBytes = kKBytes + kVBytes + kBiasBytes;
+  static constexpr int kKLoads = kKBytes / 1024;  // 1 KB wave loads per tile
+  static constexpr int kVLoads = kVBytes / 1024;
+  static_assert(HDP == 32 || HDP == 64 || HDP == 128, "head dims padded to 32, 64 or 128");
+};
+
+template <int HDP>
+__global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
+  using L = AttnLds<HDP>;
+  constexpr int kSteps = HDP / 32;  // k-steps of the score product
+  constexpr int kDTiles = HDP / 16;  // 16-dim output tiles
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kBufBytes];
+
+  // Work item: head-major, dealt to XCDs in contiguous ranges (workgroup i runs on XCD i % 8).
+  const int item = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
+  if (item >= p.items) return;  // workgroup-uniform, before any barrier
+  const int h = item / p.qtiles;
+  const int q0 = (item % p.qtiles) * kQueryTile;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int j = lane & 15;  // query column of every fragment this lane holds
+  const int g = lane >> 4;  // k-octet (operands) / row quad (results)
+  const long long d = static_cast<long long>(p.heads) * p.hd;
+
+  // Q fragments (B operand of S^T): query q0 + 16·wave + j, dims 32s + 8g .. +7, rounded to bf16.
+  bf16x8 qf[kSteps];
+  {
+    const int q = q0 + 16 * wave + j;
+    const float* qr = p.qkv + static_cast<long long>(q) * 3 * d + static_cast<long long>(h) * p.hd;
+#pragma unroll
+    for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 32 * s + 8 * g + e;
+        qf[s][e] = static_cast<__bf16>(q < p.n && c < p.hd ? qr[c] : 0.f);
+      }
+    }
+  }
+
+  const uint32_t lds_base = lds_address(lds);
+  const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kb + static_cast<long long>(h) * p.npad * HDP);
+  const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.vt + static_cast<long long>(h) * HDP * p.npad);
+  const uint8_t* bg = reinterpret_cast<const uint8_t*>(p.kbias);
+  const int ntiles = p.npad / kKeyTile;
+
+  // Issues this wave's share of tile `kt`'s loads into buffer `buf`: K and V loads dealt to the
+  // waves in turn; wave 0 also loads the 256-byte bias (16 lanes).
+  auto issue = [&](int kt, int buf) {
+    const uint32_t dst = lds_base + buf * L::kBufBytes;
+    constexpr int kRowsPerLoad = 512 / HDP;  // K rows per 1 KB
+    for (int c = wave; c < L::kKLoads; c += 4) {
+      const int r = c * kRowsPerLoad + lane / L::kCpr;
+      const int cc = lane % L::kCpr;
+      const uint32_t src = static_cast<uint32_t>((kt * kKeyTile + r) * HDP * 2 + ((cc ^ (r & (L::kCpr - 1))) * 16));
+      load_lds16(kg, src, dst + c * 1024);
+    }
+    for (int c = wave; c < L::kVLoads; c += 4) {
+      const int r = c * 8 + lane / 8;  // dim
+      const int cc = lane % 8;
+      const uint32_t src =
+          static_cast<uint32_t>(static_cast<long long>(r) * p.npad * 2 + kt * kKeyTile * 2 + ((cc ^ (r & 7)) * 16));
+      load_lds16(vg, src, dst + L::kKBytes + c * 1024);
+    }
+    if (wave == 0 && lane < 16)
+      load_lds16(bg, static_cast<uint32_t>(kt * kKeyTile * 4 + lane * 16), dst + L::kKBytes + L::kVBytes);
+  };
+
+  f32x4 acc[kDTiles];
+#pragma unroll
+  for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY;  // running maximum of this lane's query (log2 domain)
+  float l_part = 0.f;       // this lane's share of the running sum of weights
+
+  issue(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  for (int kt = 0; kt < ntiles; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
+    const uint8_t* kl = lds + buf * L::kBufBytes;
+    const uint8_t* vl = kl + L::kKBytes;
+    const float* bl = reinterpret_cast<const float*>(vl + L::kVBytes);
+
+    // S^T for the tile's four 16-key groups: rows keys 16u + 4g + r, column query j.
+    f32x4 s4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      s4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int r = 16 * u + j;  // A row: key
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+        const int chunk = (4 * s + g) ^ (r & (L::kCpr - 1));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * HDP * 2 + chunk * 16);
+        s4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], s4[u], 0, 0, 0);
+      }
+    }
+    // Scale, mask, and the tile's maximum per query.
+    float mt = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 b = *reinterpret_cast<const float4*>(bl + 16 * u + 4 * g);
+      s4[u][0] = s4[u][0] * p.scale_l2 + b.x;
+      s4[u][1] = s4[u][1] * p.scale_l2 + b.y;
+      s4[u][2] = s4[u][2] * p.scale_l2 + b.z;
+      s4[u][3] = s4[u][3] * p.scale_l2 + b.w;
+      mt = fmaxf(mt, fmaxf(fmaxf(s4[u][0], s4[u][1]), fmaxf(s4[u][2], s4[u][3])));
+    }
+    mt = wave_max16(mt);
+    const float m_new = fmaxf(m_run, mt);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no valid key yet: every weight is 0
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    // Weights, rounded to bf16 as the PV product takes them; the sum adds the rounded values.
+    bf16x8 pb[2];
+    float ls = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const __bf16 w = static_cast<__bf16>(__builtin_amdgcn_exp2f(s4[u][r] - m_use));
+        pb[u >> 1][(u & 1) * 4 + r] = w;
+        ls += static_cast<float>(w);
+      }
+    }
+    l_part = l_part * alpha + ls;
+#pragma unroll
+    for (int i = 0; i < kDTiles; ++i) acc[i] *= alpha;
+    // O^T += V^T . P^T: k slot 8g + e of product mf is key 32mf + 4g + e (e < 4) or
+    // 32mf + 16 + 4g + (e - 4): the keys this lane's weights belong to.
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+      const int r = 16 * dt + j;  // A row: dim
+      const uint8_t* vrow = vl + r * (kKeyTile * 2);
+#pragma unroll
+      for (int mf = 0; mf < 2; ++mf) {
+        const int k0 = 32 * mf + 4 * g, k1 = k0 + 16;  // first keys of the two 8-byte halves
+        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((k0 >> 3) ^ (r & 7)) * 16) + (k0 & 7) * 2);
+        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((k1 >> 3) ^ (r & 7)) * 16) + (k1 & 7) * 2);
+        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mf], acc[dt], 0, 0, 0);
+      }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();  // tile kt+1 is in; every wave is done with buffer kt & 1
+  }
+
+  // Normalise and store: lane holds dims 16dt + 4g .. +3 of query q0 + 16·wave + j.
+  const float l = sum_groups16(l_part);
+  const float inv = 1.f / l;  // no valid key: 1/0, and 0 · inf = NaN, as the page's arithmetic gives
+  const int q = q0 + 16 * wave + j;
+  if (q < p.n) {
+    float* orow = p.o + static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int c = 16 * dt + 4 * g + r;
+        if (c < p.hd) orow[c] = acc[dt][r] * inv;
+      }
+    }
+  }
+}
+
+int head_pad(int hd) { return hd <= 32 ? 32 : hd <= 64 ? 64 : 128; }
+
+}  // namespace
+
+hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, int d, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  const dim3 grid((n + 3) / 4), block(256);
+  const bool vec = d % 4 == 0 && d <= 4096 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (reinterpret_cast<uintptr_t>(wb) & 15) == 0;
+  if (!vec) {
+    hipLaunchKernelGGL(layer_norm_scalar_kernel, grid, block, 0, stream, x, wb, y, n, d);
+  } else if (d <= 256) {
+    hipLaunchKernelGGL(layer_norm_vec_kernel<1>, grid, block, 0, stream, x, wb, y, n, d);
+  } else if (d <= 512) {
+    hipLaunchKernelGGL(layer_norm_vec_kernel<2>, grid, block, 0, stream, x, wb, y, n, d);
+  } else if (d <= 1024) {
+    hipLaunchKernelGGL(layer_norm_vec_kernel<4>, grid, block, 0, stream, x, wb, y, n, d);
+  } else if (d <= 2048) {
+    hipLaunchKernelGGL(layer_norm_vec_kernel<8>, grid, block, 0, stream, x, wb, y, n, d);
+  } else {
+    hipLaunchKernelGGL(layer_norm_vec_kernel<16>, grid, block, 0, stream, x, wb, y, n, d);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int n, int heads,
+                               int hd, int rot, hipStream_t stream) {
+  const long long vecs = 2LL * n * heads;
+  if (vecs == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>((vecs + 3) / 4)), block(256);
+  if (hd <= 64)
+    hipLaunchKernelGGL(qk_norm_rope_kernel<1>, grid, block, 0, stream, qkv, qn, kn, cs, n, heads, hd, rot);
+  else if (hd <= 128)
+    hipLaunchKernelGGL(qk_norm_rope_kernel<2>, grid, block, 0, stream, qkv, qn, kn, cs, n, heads, hd, rot);
+  else
+    hipLaunchKernelGGL(qk_norm_rope_kernel<4>, grid, block, 0, stream, qkv, qn, kn, cs, n, heads, hd, rot);
+  return hipGetLastError();
+}
+
+long long attention_workspace_bytes(long long n, long long heads, long long hd) {
+  const long long npad = (n + kKeyTile - 1) / kKeyTile * kKeyTile;
+  const long long hdp = head_pad(static_cast<int>(hd));
+  // kb and vt (bf16), then the key bias (f32); each part starts on a 256-byte boundary.
+  const long long kv = (heads * npad * hdp * 2 + 255) / 256 * 256;
+  return 2 * kv + (npad * 4 + 255) / 256 * 256;
+}
+
+template <int HDP>
+hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o, uint8_t* ws, int n, int heads,
+                                int hd, float scale, hipStream_t stream) {
+  const int npad = (n + kKeyTile - 1) / kKeyTile * kKeyTile;
+  const long long kv = (static_cast<long long>(heads) * npad * HDP * 2 + 255) / 256 * 256;
+  uint16_t* kb = reinterpret_cast<uint16_t*>(ws);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + kv);
+  float* kbias = reinterpret_cast<float*>(ws + 2 * kv);
+  hipLaunchKernelGGL(attn_pack_kernel<HDP>, dim3(npad / kKeyTile, heads), dim3(256), 0, stream, qkv, valid, kb, vt,
+                     kbias, n, npad, heads, hd);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  AttnParams p{};
+  p.qkv = qkv;
+  p.kb = kb;
+  p.vt = vt;
+  p.kbias = kbias;
+  p.o = o;
+  p.n = n;
+  p.npad = npad;
+  p.heads = heads;
+  p.hd = hd;
+  p.qtiles = (n + kQueryTile - 1) / kQueryTile;
+  p.items = heads * p.qtiles;
+  p.per_xcd = (p.items + 7) / 8;
+  p.scale_l2 = scale * 1.4426950408889634f;
+  hipLaunchKernelGGL(attention_kernel<HDP>, dim3(p.per_xcd * 8), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
+                            float scale, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  switch (head_pad(hd)) {
+    case 32: return launch_attention_hdp<32>(qkv, valid, o, w, n, heads, hd, scale, stream);
+    case 64: return launch_attention_hdp<64>(qkv, valid, o, w, n, heads, hd, scale, stream);
+    default: return launch_attention_hdp<128>(qkv, valid, o, w, n, heads, hd, scale, stream);
+  }
+}
+
+}  // namespace wq

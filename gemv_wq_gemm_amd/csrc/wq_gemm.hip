@@ -19,7 +19,7 @@
 //    the way to their integer quants q (Q8_0) or q-8 (Q4_0), exact in bf16; the
 //    matrix cores sum each 32-element block into a fresh accumulator and the f16
 //    scale of that (row, block) multiplies it in f32. The weights thus enter
-//    exactly; only the bf16 rounding of X (2^-9 relative) and the f32 sums
+//    exactly; only the bf16 rounding of X (at most 2^-8 relative) and the f32 sums
 //    contribute error: |y - y_ref| <= 2^-8 * sum|x*w|.
 //  * Two LDS buffers: while the matrix cores work on one k step, the next step
 //    is loaded from global memory into registers and then written to the other

@@ -88,4 +88,12 @@ struct GemmParams {
 
 hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream);
 
+// ---- encoder block (wq_encoder.hip) ---------------------------------------------------------
+hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, int d, hipStream_t stream);
+hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int n, int heads,
+                               int hd, int rot, hipStream_t stream);
+long long attention_workspace_bytes(long long n, long long heads, long long hd);
+hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
+                            float scale, hipStream_t stream);
+
 }  // namespace wq

@@ -272,6 +272,118 @@ int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k);
  * number; the reading taken is n <= 16 (WQ_MATVEC_MAX_N) on the f32 matvec. */
 int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype);
 
+/* ---- the encoder block around the layer -----------------------------------------------------
+ * The rest of the pre-norm block of cortiq-engine's audio encoder (src/gpu_wgpu/nemotron_audio.rs:
+ * the kernels `ae_ln`, `ae_qk`, `ae_attn` and the order `AudioEncoder::run` runs them in). All
+ * arithmetic is f32 except the two attention products (see wq_attention). Sizes: d = heads * hd;
+ * frames n; a q/k/v row is [q | k | v] of d floats each, head h at columns h*hd .. h*hd+hd-1 of
+ * each third. */
+
+/*
+ * wq_layer_norm: y[t] = (x[t] - mu) / sqrt(var + 1e-5) * w + b for each of n rows of d floats,
+ * with mu the row mean and var the mean squared deviation from it (division by d) -- `ae_ln`.
+ *   x   f32 [n][d], 4-byte aligned.
+ *   wb  f32 [2d]: w then b (the page's packed LayerNorm weights), 4-byte aligned.
+ *   y   f32 [n][d], 4-byte aligned; y == x (in place) is allowed, any other overlap with x or wb
+ *       is WQ_ERR_ALIAS.
+ *   n >= 0 (0: nothing to do), d >= 1, n * d <= 2^40. Rows with d % 4 == 0, d <= 4096 and x, y,
+ *   wb 16-byte aligned are held in registers; others take a slower kernel, same arithmetic.
+ */
+int wq_layer_norm(const float* x, const float* wb, float* y, int64_t n, int64_t d, void* stream);
+
+/*
+ * wq_rope_table: the rotation table `AudioEncoder::run` builds on the host, written to host
+ * memory: cs[t*(rot/2) + i] = cos(a), cs[n*(rot/2) + t*(rot/2) + i] = sin(a) with
+ * a = t * (1 / 10000^(2i/rot)), every step in f32 (the page's own arithmetic; the angle is
+ * rounded to f32 before its cosine is taken), frames t = 0 .. n-1.
+ *   cs   host float [n * rot]; rot even, 2 <= rot; n >= 0.
+ */
+int wq_rope_table(float* cs, int64_t n, int64_t rot);
+
+/*
+ * wq_qk_norm_rope: in place on qkv f32 [n][3d], for each frame t and head h of q and of k (v is
+ * not touched) -- `ae_qk`:
+ *   1. with qn / kn given: LayerNorm of the head's hd values as wq_layer_norm, weights
+ *      qn (for q) or kn (for k), each f32 [2*hd] (w then b);
+ *   2. rotation of its first rot dims: for i < rot/2, with c = cs[t*(rot/2) + i] and
+ *      s = cs[n*(rot/2) + t*(rot/2) + i],
+ *        v'[i] = v[i]*c - v[i + rot/2]*s,   v'[i + rot/2] = v[i + rot/2]*c + v[i]*s;
+ *      dims rot .. hd-1 pass through.
+ *   qkv   device f32, 4-byte aligned.
+ *   qn,kn device f32 [2*hd] each, or both NULL (no norm); one without the other: WQ_ERR_NULL.
+ *   cs    device f32 [n * rot] (the table above, or any other); may be NULL when rot == 0.
+ *   1 <= hd <= 256, heads >= 1, rot even and 0 <= rot <= hd, n >= 0.
+ * qn, kn and cs must not overlap qkv (WQ_ERR_ALIAS).
+ */
+int wq_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int64_t n,
+                    int64_t heads, int64_t hd, int64_t rot, void* stream);
+
+/* Bytes of device workspace wq_attention needs for these sizes (bf16 copies of K and of V laid
+ * out for the attention kernel, and the key mask as a bias), or -1 for invalid sizes. */
+int64_t wq_attention_workspace_bytes(int64_t n, int64_t heads, int64_t hd);
+
+/*
+ * wq_attention: bidirectional attention with masked keys -- `ae_attn`. For frame t and head h:
+ * scores s_j = scale * q[t,h] . k[j,h] over the keys j with valid[j] != 0, weights
+ * p_j = exp(s_j - max) / sum exp(s - max), output o[t, h*hd + c] = sum_j p_j v[j,h,c].
+ * Masked keys take no weight. With no valid key at all the sum of weights is 0 and every output is
+ * NaN (the page's 0 * (1/0)).
+ *   qkv        device f32 [n][3d] (the q/k/v rows after wq_qk_norm_rope), 4-byte aligned.
+ *   valid      device int32 [n], 4-byte aligned.
+ *   o          device f32 [n][d], 4-byte aligned, not overlapping qkv, valid or the workspace.
+ *   workspace  device, 256-byte aligned, at least wq_attention_workspace_bytes(n, heads, hd)
+ *              bytes (workspace_bytes says how many it has; fewer: WQ_ERR_SHAPE). Overwritten.
+ *   scale      finite; the page's is 1/sqrt(hd) in f32.
+ *   1 <= hd <= 128, 1 <= heads <= 4096, 0 <= n <= 2^22.
+ * Arithmetic: q, k and v are rounded to bf16 (nearest even) and both products run on the bf16
+ * matrix cores with f32 accumulation; the softmax runs in f32 (base-2 exponentials of scores
+ * pre-multiplied by scale*log2(e)), and the weights are rounded to bf16 for the second product,
+ * normalised by the sum of the rounded weights. The page's kernel keeps q, k and v in f32; the
+ * error bound this gives is stated with the tests.
+ */
+int wq_attention(const float* qkv, const int32_t* valid, float* o, void* workspace,
+                 int64_t workspace_bytes, int64_t n, int64_t heads, int64_t hd, float scale,
+                 void* stream);
+
+/* One pre-norm block's weights (`AeLayerDesc` on the page). Weight matrices are in the layer's
+ * storage type (wq_encoder_layer's wtype) and 16-byte aligned; vectors are f32, 4-byte aligned. */
+typedef struct wq_encoder_layer {
+  const float* ln1;   /* [2d] LayerNorm before attention: w then b */
+  const void* qkv_w;  /* [3d][d] fused q/k/v weights */
+  const float* qkv_b; /* [3d] or NULL (the page's block has no q/k/v bias) */
+  const float* qn;    /* [2*hd] q LayerNorm, or NULL (then kn is NULL too: no q/k norm) */
+  const float* kn;    /* [2*hd] k LayerNorm, or NULL */
+  const void* out_w;  /* [d][d] output projection */
+  const float* out_b; /* [d] */
+  const float* ln2;   /* [2d] LayerNorm before the MLP */
+  const void* fc1_w;  /* [inter][d] */
+  const float* fc1_b; /* [inter] */
+  const void* fc2_w;  /* [d][inter] */
+  const float* fc2_b; /* [d] */
+} wq_encoder_layer_t;
+
+/* Bytes of device workspace wq_encoder_layer needs (its activations a, qkv, att and f, and the
+ * attention workspace), or -1 for invalid sizes. */
+int64_t wq_encoder_workspace_bytes(int64_t n, int64_t d, int64_t heads, int64_t inter);
+
+/*
+ * wq_encoder_layer: one block of `AudioEncoder::run`, in place on h f32 [n][d]:
+ *   a = LayerNorm(h; ln1);  qkv = a . qkv_w^T (+ qkv_b);  wq_qk_norm_rope(qkv; qn, kn, cs);
+ *   att = wq_attention(qkv, valid, scale = 1/sqrt(hd) in f32);
+ *   h = h + att . out_w^T + out_b;  a = LayerNorm(h; ln2);
+ *   f = GELU(a . fc1_w^T + fc1_b);  h = h + f . fc2_w^T + fc2_b.
+ * The products are wq_linear calls on `path` (WQ_PATH_AUTO, WQ_PATH_MFMA or WQ_PATH_MFMA_F32).
+ *   h          device f32 [n][d], 16-byte aligned.
+ *   valid, cs  as for wq_attention / wq_qk_norm_rope (cs [n * rot]).
+ *   workspace  device, 256-byte aligned, >= wq_encoder_workspace_bytes(n, d, heads, inter).
+ *   d % 32 == 0, inter % 32 == 0, d % heads == 0 with hd = d / heads <= 128, rot as for
+ *   wq_qk_norm_rope, 0 <= n <= 2^22.
+ * Returns the first failing step's code; h is then partly updated.
+ */
+int wq_encoder_layer(const wq_encoder_layer_t* layer, int wtype, float* h, const int32_t* valid,
+                     const float* cs, void* workspace, int64_t workspace_bytes, int64_t n, int64_t d,
+                     int64_t heads, int64_t rot, int64_t inter, int path, void* stream);
+
 /* Message of the last failed call on this thread ("" when none): the text of the
  * checks above, in the manner of the messages hanzo-ml's host functions return
  * on a refused call (`bail!` with the offending sizes). */

@@ -215,3 +215,68 @@ def encoder_activations(seed: int = 0):
     n, d = ENCODER_N, ENCODER_D
     return {name: normal_f32(rng(seed, cfg, i), (n, d), 1.0)
             for i, name in enumerate(["a1", "a2", "a3", "h0"])}
+
+
+# ---- the rest of the encoder block (LayerNorm, q/k norm + rotation, attention) ----------------
+# Heads, rotated dims and padding are not fixed by the pages for this encoder: 8 heads of 128
+# (the largest head its kernels take, d = 1024), every dim of a head rotated, and the last 100 of
+# the 1500 frames marked as padding (masked keys).
+ENCODER_HEADS, ENCODER_ROT, ENCODER_VALID = 8, 128, 1400
+
+
+def layer_norm_weights(g: np.random.Generator, d: int) -> np.ndarray:
+    """f32 [2d]: weights 1 + N(0, 0.1^2), then biases N(0, 0.1^2)."""
+    return np.concatenate([1.0 + normal_f32(g, (d,), 0.1), normal_f32(g, (d,), 0.1)]).astype(np.float32)
+
+
+def unit_circle_table(g: np.random.Generator, n: int, half: int) -> np.ndarray:
+    """f32 [2 * n * half]: cosines then sines of angles drawn uniformly in [0, 2 pi), laid out as a
+    rotation table (any table serves to test the rotation's arithmetic)."""
+    theta = g.uniform(0.0, 2.0 * np.pi, (n, half))
+    return np.concatenate([np.cos(theta).reshape(-1), np.sin(theta).reshape(-1)]).astype(np.float32)
+
+
+def key_mask(n: int, n_valid: int) -> np.ndarray:
+    """int32 [n]: the first n_valid frames valid (1), the rest padding (0)."""
+    v = np.zeros(n, np.int32)
+    v[:n_valid] = 1
+    return v
+
+
+def random_key_mask(g: np.random.Generator, n: int, p_valid: float) -> np.ndarray:
+    """int32 [n]: each frame valid with probability p_valid."""
+    return (g.random(n) < p_valid).astype(np.int32)
+
+
+def encoder_block_weights(layer: int, seed: int = 0, d: int = ENCODER_D, heads: int = ENCODER_HEADS,
+                          inter: int = ENCODER_FF, qk_norm: bool = True, qkv_bias: bool = False,
+                          sigma: float = 0.02):
+    """One pre-norm block: LayerNorm weights, bf16 matrices N(0, sigma^2), biases N(0, 0.1^2);
+    q/k norm weights when qk_norm, a q/k/v bias when qkv_bias (the pages' block has none)."""
+    cfg = 6
+    hd = d // heads
+    r = lambda i: rng(seed, cfg, layer, d, inter, i)  # noqa: E731
+    return {
+        "ln1": layer_norm_weights(r(0), d),
+        "qkv_w": bf16_weight(r(1), 3 * d, d, sigma),
+        "qkv_b": normal_f32(r(2), (3 * d,), 0.1) if qkv_bias else None,
+        "qn": layer_norm_weights(r(3), hd) if qk_norm else None,
+        "kn": layer_norm_weights(r(4), hd) if qk_norm else None,
+        "out_w": bf16_weight(r(5), d, d, sigma), "out_b": normal_f32(r(6), (d,), 0.1),
+        "ln2": layer_norm_weights(r(7), d),
+        "fc1_w": bf16_weight(r(8), inter, d, sigma), "fc1_b": normal_f32(r(9), (inter,), 0.1),
+        "fc2_w": bf16_weight(r(10), d, inter, sigma), "fc2_b": normal_f32(r(11), (d,), 0.1),
+    }
+
+
+def encoder_model(n_layers: int, seed: int = 0, d: int = ENCODER_D, heads: int = ENCODER_HEADS,
+                  inter: int = ENCODER_FF, stack_in: int | None = None, qk_norm: bool = True):
+    """Embedding and final LayerNorms, an optional input projection [d][stack_in] (bf16, no bias)
+    and n_layers blocks."""
+    cfg = 7
+    return {
+        "proj": None if stack_in is None else bf16_weight(rng(seed, cfg, 0), d, stack_in, 0.05),
+        "embed_norm": layer_norm_weights(rng(seed, cfg, 1, d), d),
+        "final_norm": layer_norm_weights(rng(seed, cfg, 2, d), d),
+        "layers": [encoder_block_weights(i, seed, d, heads, inter, qk_norm) for i in range(n_layers)],
+    }

@@ -13,11 +13,11 @@ import sys
 
 import pytest
 
+import gemv_wq_gemm_amd.build as wq_build
 from tests.conftest import ROOT
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 CSRC = os.path.join(ROOT, "gemv_wq_gemm_amd", "csrc")
-KERNEL_SOURCES = ["wq_matvec.hip", "wq_matvec_sliced.hip", "wq_matvec_mfma.hip", "wq_gemm.hip"]
 SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
        "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=undefined"]
 
@@ -31,10 +31,10 @@ def _asan_runtime():
 def sanitized_lib(tmp_path_factory):
     if not os.access(HIPCC, os.X_OK) or _asan_runtime() is None:
         pytest.skip("hipcc or the clang ASan runtime is not available")
-    import gemv_wq_gemm_amd.build as b
+    b = wq_build
     out = tmp_path_factory.mktemp("asan")
     objs = []
-    for src in KERNEL_SOURCES:  # the kernels as the library builds them
+    for src in [s for s in b.SOURCES if s.endswith(".hip")]:  # the kernels as the library builds them
         obj = os.path.join(b.OBJDIR, os.path.splitext(src)[0] + ".o")
         if not os.path.exists(obj) or os.path.getmtime(obj) < os.path.getmtime(os.path.join(CSRC, src)):
             os.makedirs(b.OBJDIR, exist_ok=True)
