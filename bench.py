@@ -27,8 +27,12 @@ The same JSON line carries:
                 fraction of peak, the streaming-read floor for the same bytes (a plain read kernel,
                 libwq_bench.so) and the fraction of it reached (frac_of_sol), counted traffic and a CPU
                 baseline of its own;
-  others        the chain on the f32-accurate matrix-core path, f16 weights at 4096x4096 n = 1, and
-                the MLP-up shape with f16 / f32 / Q8_0 / Q4_0 weights.
+                The rest of the encoder block adds LayerNorm 1500x1024, the q/k norm + rotation over
+                8 heads of 128 and attention (1500 frames, 100 masked) to rooflines, each with a CPU
+                baseline;
+  others        the chain on the f32-accurate matrix-core path, f16 weights at 4096x4096 n = 1,
+                the MLP-up shape with f16 / f32 / Q8_0 / Q4_0 weights, and the whole 24-block
+                encoder forward (every kernel of the block; CPU baseline: one block).
 Weights of the matvec and MoE workloads rotate over copies of at least 600 MB, so the 256 MB
 Infinity Cache cannot serve them; the floors read the same amounts from rotating windows.
 """
@@ -59,7 +63,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--legs", default="all",
-                    help="comma list of workload groups to run (chain, c1, c2, c3, c4, moe1, moe64, others; "
+                    help="comma list of workload groups to run (chain, c1, c2, c3, c4, moe1, moe64, enc, others; "
                          "default all): profiling runs select one so its kernels' counters are its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run an elementwise copy of 256 MiB (reads and writes that many bytes), "
@@ -178,7 +182,7 @@ def main():
     import synth
     from gemv_wq_gemm_amd.rocprof_summary import read_traffic
 
-    all_legs = {"chain", "c1", "c2", "c3", "c4", "moe1", "moe64", "others"}
+    all_legs = {"chain", "c1", "c2", "c3", "c4", "moe1", "moe64", "enc", "others"}
     legs = all_legs if args.legs == "all" else set(args.legs.split(","))
     if legs - all_legs:
         print(f"unknown legs {sorted(legs - all_legs)}; choose from {sorted(all_legs)}", file=sys.stderr)
@@ -208,6 +212,10 @@ def main():
         line = {"metric": "GEMM TFLOP/s (encoder chain) on 1 MI355X", "value": None, "unit": "TFLOP/s",
                 "note": f"profiling run of legs {sorted(legs)}; the step (the chain) was not run"}
     line["rooflines"] = _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic)
+    if "enc" in legs:
+        enc_rl, enc_other = _encoder(torch, wq, synth, dev, timer, to_dev, args)
+        line["rooflines"].update(enc_rl)
+        others.update(enc_other)
     if not args.no_others and "others" in legs:
         others.update(_others(torch, wq, synth, dev, timer, to_dev, args))
     if others:
@@ -216,9 +224,11 @@ def main():
     if not args.no_cpu_baseline:
         if acts is not None:
             line["cpu_baseline"] = _cpu_chain(synth, acts)
-        for key, cpu in _cpu_configs(synth).items():
+        for key, cpu in {**_cpu_configs(synth), **(_cpu_encoder(synth) if "enc" in legs else {})}.items():
             if key in line["rooflines"]:
                 line["rooflines"][key]["cpu_baseline"] = cpu
+            elif key in others:
+                others[key]["cpu_baseline"] = cpu
 
     print(json.dumps(line), flush=True)
 
@@ -453,6 +463,85 @@ def _moe(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic, legs
     del big
 
 
+def _encoder(torch, wq, synth, dev, timer, to_dev, args):
+    """The rest of the encoder block at the workload's size (1500 frames, d = 1024, 8 heads of 128,
+    all dims rotated, the last 100 frames masked): LayerNorm, q/k norm + rotation and attention
+    each alone, and the whole 24-block forward (embedding LayerNorm, 24 blocks with bf16 weights,
+    final LayerNorm). Returns (rooflines, others)."""
+    R = args.reps
+    n, d, heads, ff = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_HEADS, synth.ENCODER_FF
+    hd, rot = d // heads, synth.ENCODER_ROT
+    g = synth.rng(60)
+    rl, oth = {}, {}
+
+    # LayerNorm [1500][1024]: reads and writes the rows once (HBM-bound).
+    xs = [to_dev(synth.normal_f32(synth.rng(61, i), (n, d), 1.0)) for i in range(4)]
+    wb = to_dev(synth.layer_norm_weights(g, d))
+    ys = [torch.empty((n, d), device=dev) for _ in range(4)]
+    st = _stats(timer.runs(lambda i: wq.layer_norm(xs[i % 4], wb, d=d, out=ys[i % 4]), 200, R))
+    nb = 2 * n * d * 4 + 2 * d * 4
+    gbs = nb / (st["median_us"] * 1e-6) / 1e9
+    rl["NEXT4_layer_norm_1500x1024"] = {**st, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                        "bound": "hbm", "bytes": nb}
+    del xs, ys
+
+    # q/k norm + rotation in place on [1500][3 x 1024]: q and k read and written once.
+    qkvs = [to_dev(synth.normal_f32(synth.rng(62, i), (n, 3 * d), 1.0)) for i in range(4)]
+    qn, kn = to_dev(synth.layer_norm_weights(g, hd)), to_dev(synth.layer_norm_weights(g, hd))
+    cs = wq.rope_table(n, rot).to(dev)
+    st = _stats(timer.runs(lambda i: wq.qk_norm_rope(qkvs[i % 4], cs, n=n, heads=heads, hd=hd, rot=rot, qn=qn, kn=kn),
+                           200, R))
+    nb = 2 * n * 2 * d * 4 + n * rot * 4
+    gbs = nb / (st["median_us"] * 1e-6) / 1e9
+    rl["NEXT4_qk_norm_rope_1500x8x128"] = {**st, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                                           "bound": "hbm", "bytes": nb}
+
+    # Attention: the call (pack + flash kernel); 4 n^2 hd FLOP per head, masked keys included.
+    valid = to_dev(synth.key_mask(n, synth.ENCODER_VALID))
+    att = torch.empty((n, d), device=dev)
+    ws = torch.empty(wq.attention_workspace_bytes(n, heads, hd), dtype=torch.uint8, device=dev)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(hd)))
+    st = _stats(timer.runs(lambda i: wq.attention(qkvs[i % 4], valid, n=n, heads=heads, hd=hd, scale=scale, out=att,
+                                                  workspace=ws), 100, R))
+    fl = 4 * n * n * hd * heads
+    tf = fl / (st["median_us"] * 1e-6) / 1e12
+    rl["NEXT4_attention_1500x8x128"] = {**st, "TFLOP/s": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
+                                        "bound": "mfma", "flop": fl,
+                                        "note": "pack (K, V to bf16) + flash kernel; kernel split in the trace"}
+    del qkvs, att, ws
+
+    if args.no_others:
+        return rl, oth
+    # The forward: 24 blocks, embedded input rows.
+    model = synth.encoder_model(synth.ENCODER_LAYERS)
+    layers = [{k: (None if v is None else to_dev(v)) for k, v in L.items()} for L in model["layers"]]
+    descs = [wq.encoder_layer_desc(L) for L in layers]
+    en, fn_ = to_dev(model["embed_norm"]), to_dev(model["final_norm"])
+    x = to_dev(synth.normal_f32(synth.rng(63), (n, d), 1.0))
+    h = torch.empty((n, d), device=dev)
+    y = torch.empty((n, d), device=dev)
+    wsl = torch.empty(wq.encoder_workspace_bytes(n, d, heads, ff), dtype=torch.uint8, device=dev)
+
+    def forward(_):
+        wq.layer_norm(x, en, d=d, out=h)
+        for D in descs:
+            wq.encoder_layer(h, D, wq.W_BF16, valid, cs, n=n, d=d, heads=heads, rot=rot, inter=ff, workspace=wsl)
+        wq.layer_norm(h, fn_, d=d, out=y)
+
+    st = _stats(timer.runs(forward, 2, R, warm=1))
+    fl_layer = 2 * n * (3 * d * d + d * d + ff * d + d * ff) + 4 * n * n * hd * heads
+    fl_fwd = synth.ENCODER_LAYERS * fl_layer
+    oth["encoder_forward_24_layers"] = {
+        **st, "ms": round(st["median_us"] / 1e3, 4),
+        "TFLOP/s": round(fl_fwd / (st["median_us"] * 1e-6) / 1e12, 1), "flop": fl_fwd,
+        "workload": "embedding LayerNorm, 24 pre-norm blocks (LayerNorm, QKV 1500x3072x1024, q/k norm + RoPE, "
+                    "attention 8x128 over 1400 valid of 1500 frames, out 1500x1024x1024 + residual, LayerNorm, "
+                    "MLP 4096 + GELU + residual; bf16 weights N(0,0.02)), final LayerNorm"}
+    del layers, descs, wsl
+    torch.cuda.empty_cache()
+    return rl, oth
+
+
 def _others(torch, wq, synth, dev, timer, to_dev, args):
     out = {}
     R = args.reps
@@ -525,6 +614,45 @@ def _cpu_chain(synth, acts):
     return {"value": round(fl / sec / 1e9, 2), "unit": "GFLOP/s", "cores": _threads(), "kind": "oracle",
             "sample": f"2 of the 24 layers (all 1500 frames, all four GEMMs): {fl / 1e9:.1f} GFLOP in {sec:.2f} s, "
                       "f64 decode + numpy product + epilogue"}
+
+
+def _cpu_encoder(synth):
+    """The oracle on the encoder-block workloads: LayerNorm, q/k norm + rotation and attention at
+    full size (median of 3 runs), and one of the forward's 24 blocks."""
+    from oracle import encoder as enc
+    n, d, heads, ff = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_HEADS, synth.ENCODER_FF
+    hd, rot = d // heads, synth.ENCODER_ROT
+    cores = _threads()
+    g = synth.rng(70)
+    x = synth.normal_f32(g, (n, d), 1.0)
+    wb = synth.layer_norm_weights(g, d)
+    qkv = synth.normal_f32(g, (n, 3 * d), 1.0)
+    qn, kn = synth.layer_norm_weights(g, hd), synth.layer_norm_weights(g, hd)
+    cos, sin = enc.rope_table(n, rot)
+    valid = synth.key_mask(n, synth.ENCODER_VALID)
+    scale = float(np.float32(1.0) / np.sqrt(np.float32(hd)))
+    res = {}
+    sec = _cpu_time(lambda: enc.layer_norm(x, wb), 3)
+    res["NEXT4_layer_norm_1500x1024"] = {"value": round((2 * n * d * 4 + 2 * d * 4) / sec / 1e9, 3), "unit": "GB/s",
+                                         "cores": cores, "kind": "oracle",
+                                         "sample": f"the full call, median of 3 runs: {sec:.4f} s"}
+    sec = _cpu_time(lambda: enc.qk_norm_rope(qkv, heads, hd, rot, cos, sin, qn, kn), 3)
+    res["NEXT4_qk_norm_rope_1500x8x128"] = {"value": round((4 * n * d * 4 + n * rot * 4) / sec / 1e9, 3),
+                                            "unit": "GB/s", "cores": cores, "kind": "oracle",
+                                            "sample": f"the full call, median of 3 runs: {sec:.4f} s"}
+    sec = _cpu_time(lambda: enc.attention(qkv, valid, heads, hd, scale), 3)
+    res["NEXT4_attention_1500x8x128"] = {"value": round(4 * n * n * hd * heads / sec / 1e9, 2), "unit": "GFLOP/s",
+                                         "cores": cores, "kind": "oracle",
+                                         "sample": f"the full call, median of 3 runs: {sec:.3f} s"}
+    L = synth.encoder_block_weights(0)
+    h = synth.normal_f32(g, (n, d), 1.0)
+    sec = _cpu_time(lambda: enc.encoder_layer(h, L, 0, valid, heads, rot, cos, sin), 1)
+    fl = 2 * n * (3 * d * d + d * d + ff * d + d * ff) + 4 * n * n * hd * heads
+    res["encoder_forward_24_layers"] = {"value": round(fl / sec / 1e9, 2), "unit": "GFLOP/s", "cores": cores,
+                                        "kind": "oracle",
+                                        "sample": f"1 of the 24 blocks, all 1500 frames: {fl / 1e9:.1f} GFLOP in "
+                                                  f"{sec:.2f} s"}
+    return res
 
 
 def _cpu_configs(synth):

@@ -18,9 +18,9 @@
 //       additive bias (0 for a valid key, -inf for a masked or padding one). These layouts let the
 //       attention kernel stream 64-key tiles into LDS with direct-to-LDS loads.
 //     - attention: flash-style, f32 online softmax, bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
-//       for both products. A workgroup of 4 waves takes 64 queries of one head, 16 per wave, and
-//       walks all key tiles. Each wave computes S^T = K.Q^T (keys in rows, its 16 queries in
-//       columns), so a lane's scores all belong to one query: the row maximum and the sum need
+//       for both products. A workgroup of 8 waves takes 64 queries of one head, 16 per wave, in two
+//       halves that walk the even and the odd key tiles. Each wave computes S^T = K.Q^T (keys in
+//       rows, queries in columns), so a lane's scores all belong to one query: the row maximum and the sum need
 //       only in-lane work plus two cross-lane steps, and the probabilities are already the B
 //       operand of O^T = V^T.P^T. Work items are numbered head-major and dealt to the 8 XCDs in
 //       contiguous ranges, so each XCD's L2 holds the K and V of few heads.
@@ -39,21 +39,39 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLnEps = 1e-5f;
 
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
 }
 
+// v[lane] combined with v[lane ^ 32] and v[lane ^ 16] (v_permlane32_swap / v_permlane16_swap with
+// both operands v leave the two halves in the two results).
+template <typename Op>
+__device__ __forceinline__ float xor32_xor16(float v, Op op) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+// Sum over the wave, in every lane: xor 32 and 16 (lane swaps), then inside each 16-lane row a
+// rotation by 8, a mirror inside 8 lanes and the two quad exchanges, which together add the 8
+// partial sums a row's lanes hold after the rotation.
+__device__ __forceinline__ float wave_sum(float v) {
+  v = xor32_xor16(v, [](float a, float b) { return a + b; });
+  v += dpp<0x128>(v);  // row_ror:8
+  v += dpp<0x141>(v);  // row_half_mirror
+  v += dpp<0x4E>(v);   // quad_perm xor 2
+  return v + dpp<0xB1>(v);  // quad_perm xor 1
+}
+
+// Max / sum over the four lane groups of 16 that share lane & 15.
 __device__ __forceinline__ float wave_max16(float v) {
-  // Max over the four lane groups of 16 that share a lane index mod 16.
-  v = fmaxf(v, __shfl_xor(v, 16));
-  return fmaxf(v, __shfl_xor(v, 32));
+  return xor32_xor16(v, [](float a, float b) { return fmaxf(a, b); });
 }
 
 __device__ __forceinline__ float sum_groups16(float v) {
-  v += __shfl_xor(v, 16);
-  return v + __shfl_xor(v, 32);
+  return xor32_xor16(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
@@ -205,25 +223,47 @@ constexpr int kKeyTile = 64;    // keys per tile
 constexpr int kQueryTile = 64;  // queries per workgroup (16 per wave)
 
 // Grid (npad / 64, heads). K: kb[h][t][0..HDP) bf16; V: vt[h][0..HDP)[t] bf16; dims past hd and
-// frames past n are zero. Head 0's workgroups also write the key bias.
+// frames past n are zero. Head 0's workgroups also write the key bias. vec4: hd % 4 == 0 and qkv
+// 16-byte aligned, so every row's head starts on a 16-byte boundary.
 template <int HDP>
 __global__ __launch_bounds__(256) void attn_pack_kernel(const float* __restrict__ qkv, const int32_t* __restrict__ valid,
                                                          uint16_t* __restrict__ kb, uint16_t* __restrict__ vt,
-                                                         float* __restrict__ kbias, int n, int npad, int heads, int hd) {
-  __shared__ uint16_t vs[kKeyTile][HDP + 2];  // V tile, frame-major, for the transposed write
+                                                         float* __restrict__ kbias, int n, int npad, int heads, int hd,
+                                                         bool vec4) {
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kKeyTile][HDP + 4];  // V tile, frame-major, for the transposed write
   const int t0 = blockIdx.x * kKeyTile;
   const int h = blockIdx.y;
   const long long d = static_cast<long long>(heads) * hd;
   const float* kbase = qkv + d + static_cast<long long>(h) * hd;
   const float* vbase = qkv + 2 * d + static_cast<long long>(h) * hd;
   uint16_t* kout = kb + (static_cast<long long>(h) * npad + t0) * HDP;
-  for (int i = threadIdx.x; i < kKeyTile * HDP; i += 256) {
-    const int r = i / HDP, c = i % HDP;
-    const int t = t0 + r;
-    const bool in = t < n && c < hd;
-    const long long off = static_cast<long long>(t) * 3 * d + c;
-    kout[i] = in ? bf16_bits_rne(kbase[off]) : uint16_t(0);
-    vs[r][c] = in ? bf16_bits_rne(vbase[off]) : uint16_t(0);
+  if (vec4) {
+    // Four dims per thread: 16-byte loads of K and V, 8-byte stores of K.
+    for (int i = threadIdx.x; i < kKeyTile * HDP / 4; i += 256) {
+      const int r = i / (HDP / 4), c = (i % (HDP / 4)) * 4;
+      const int t = t0 + r;
+      float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+      if (t < n && c < hd) {
+        const long long off = static_cast<long long>(t) * 3 * d + c;
+        kv = *reinterpret_cast<const float4*>(kbase + off);
+        vv = *reinterpret_cast<const float4*>(vbase + off);
+      }
+      *reinterpret_cast<uint2*>(kout + r * HDP + c) =
+          make_uint2(bf16_bits_rne(kv.x) | (uint32_t(bf16_bits_rne(kv.y)) << 16),
+                     bf16_bits_rne(kv.z) | (uint32_t(bf16_bits_rne(kv.w)) << 16));
+      *reinterpret_cast<uint2*>(&vs[r][c]) =
+          make_uint2(bf16_bits_rne(vv.x) | (uint32_t(bf16_bits_rne(vv.y)) << 16),
+                     bf16_bits_rne(vv.z) | (uint32_t(bf16_bits_rne(vv.w)) << 16));
+    }
+  } else {
+    for (int i = threadIdx.x; i < kKeyTile * HDP; i += 256) {
+      const int r = i / HDP, c = i % HDP;
+      const int t = t0 + r;
+      const bool in = t < n && c < hd;
+      const long long off = static_cast<long long>(t) * 3 * d + c;
+      kout[i] = in ? bf16_bits_rne(kbase[off]) : uint16_t(0);
+      vs[r][c] = in ? bf16_bits_rne(vbase[off]) : uint16_t(0);
+    }
   }
   if (h == 0 && threadIdx.x < kKeyTile) {
     const int t = t0 + threadIdx.x;
@@ -263,10 +303,11 @@ struct AttnParams {
 //   K  [64 keys][HDP] bf16, 16-byte chunks XOR-swizzled by (key & (CPR-1)), CPR = HDP/8 chunks a row;
 //   Vt [HDP dims][64 keys] bf16, chunks swizzled by (dim & 7);
 //   bias [64] f32.
+constexpr float kLazy = 8.f;  // headroom of the running maximum, in log2 units
 template <int HDP>
 struct AttnLds {
   static constexpr int kCpr = HDP / 8;                     // 16-byte chunks per K row
-  static constexpr int kKBytes = kKeyTile * HDP * 2;       // 1 KB per 512/HDP rows
+  static constexpr int kKBytes = kKeyTile * HDP * 2;
   static constexpr int kVBytes = HDP * kKeyTile * 2;
   static constexpr int kBiasBytes = kKeyTile * 4;
   static constexpr int kBufBytes = kKBytes + kVBytes + kBiasBytes;
@@ -275,12 +316,19 @@ struct AttnLds {
   static_assert(HDP == 32 || HDP == 64 || HDP == 128, "head dims padded to 32, 64 or 128");
 };
 
+// Workgroup: 8 waves, 64 queries. Waves 0-3 and 4-7 form two halves with the same four 16-query
+// groups: the first half walks the even key tiles, the second the odd ones, each half with its own
+// double-buffered LDS tiles, so two waves share every SIMD. At the end the second half hands its
+// running maximum, sum and outputs to the first through LDS, which merges them (rescaled to the
+// common maximum, in a fixed order) and stores.
 template <int HDP>
-__global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   using L = AttnLds<HDP>;
   constexpr int kSteps = HDP / 32;  // k-steps of the score product
   constexpr int kDTiles = HDP / 16;  // 16-dim output tiles
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * L::kBufBytes];
+  constexpr int kMergeFloats = 4 * kDTiles + 2;  // per lane: outputs, maximum, sum
+  static_assert(4 * 64 * kMergeFloats * 4 <= 4 * L::kBufBytes, "merge area inside the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * L::kBufBytes];  // [half][buffer]
 
   // Work item: head-major, dealt to XCDs in contiguous ranges (workgroup i runs on XCD i % 8).
   const int item = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
@@ -290,14 +338,16 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int j = lane & 15;  // query column of every fragment this lane holds
-  const int g = lane >> 4;  // k-octet (operands) / row quad (results)
+  const int hf = wave >> 2;  // half: even or odd key tiles
+  const int qw = wave & 3;   // query group
+  const int j = lane & 15;   // query column of every fragment this lane holds
+  const int g = lane >> 4;   // k-octet (operands) / row quad (results)
   const long long d = static_cast<long long>(p.heads) * p.hd;
 
-  // Q fragments (B operand of S^T): query q0 + 16·wave + j, dims 32s + 8g .. +7, rounded to bf16.
+  // Q fragments (B operand of S^T): query q0 + 16·qw + j, dims 32s + 8g .. +7, rounded to bf16.
   bf16x8 qf[kSteps];
   {
-    const int q = q0 + 16 * wave + j;
+    const int q = q0 + 16 * qw + j;
     const float* qr = p.qkv + static_cast<long long>(q) * 3 * d + static_cast<long long>(h) * p.hd;
 #pragma unroll
     for (int s = 0; s < kSteps; ++s) {
@@ -315,25 +365,25 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   const uint8_t* bg = reinterpret_cast<const uint8_t*>(p.kbias);
   const int ntiles = p.npad / kKeyTile;
 
-  // Issues this wave's share of tile `kt`'s loads into buffer `buf`: K and V loads dealt to the
-  // waves in turn; wave 0 also loads the 256-byte bias (16 lanes).
+  // Issues this wave's share of tile `kt`'s loads into its half's buffer `buf`: K and V loads dealt
+  // to the half's four waves in turn; its first wave also loads the 256-byte bias (16 lanes).
   auto issue = [&](int kt, int buf) {
-    const uint32_t dst = lds_base + buf * L::kBufBytes;
+    const uint32_t dst = lds_base + (2 * hf + buf) * L::kBufBytes;
     constexpr int kRowsPerLoad = 512 / HDP;  // K rows per 1 KB
-    for (int c = wave; c < L::kKLoads; c += 4) {
+    for (int c = qw; c < L::kKLoads; c += 4) {
       const int r = c * kRowsPerLoad + lane / L::kCpr;
       const int cc = lane % L::kCpr;
       const uint32_t src = static_cast<uint32_t>((kt * kKeyTile + r) * HDP * 2 + ((cc ^ (r & (L::kCpr - 1))) * 16));
       load_lds16(kg, src, dst + c * 1024);
     }
-    for (int c = wave; c < L::kVLoads; c += 4) {
+    for (int c = qw; c < L::kVLoads; c += 4) {
       const int r = c * 8 + lane / 8;  // dim
       const int cc = lane % 8;
       const uint32_t src =
           static_cast<uint32_t>(static_cast<long long>(r) * p.npad * 2 + kt * kKeyTile * 2 + ((cc ^ (r & 7)) * 16));
       load_lds16(vg, src, dst + L::kKBytes + c * 1024);
     }
-    if (wave == 0 && lane < 16)
+    if (qw == 0 && lane < 16)
       load_lds16(bg, static_cast<uint32_t>(kt * kKeyTile * 4 + lane * 16), dst + L::kKBytes + L::kVBytes);
   };
 
@@ -343,91 +393,131 @@ __global__ __launch_bounds__(256) void attention_kernel(AttnParams p) {
   float m_run = -INFINITY;  // running maximum of this lane's query (log2 domain)
   float l_part = 0.f;       // this lane's share of the running sum of weights
 
-  issue(0, 0);
+  const int iters = (ntiles + 1) / 2;
+  if (hf < ntiles) issue(hf, 0);
   wait_vmcnt<0>();
   __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < ntiles) issue(kt + 1, buf ^ 1);
-    const uint8_t* kl = lds + buf * L::kBufBytes;
-    const uint8_t* vl = kl + L::kKBytes;
-    const float* bl = reinterpret_cast<const float*>(vl + L::kVBytes);
+  for (int it = 0; it < iters; ++it) {
+    const int kt = 2 * it + hf;
+    const int buf = it & 1;
+    if (kt + 2 < ntiles) issue(kt + 2, buf ^ 1);
+    if (kt < ntiles) {  // wave-uniform (the odd half has one tile fewer when ntiles is odd)
+      const uint8_t* kl = lds + (2 * hf + buf) * L::kBufBytes;
+      const uint8_t* vl = kl + L::kKBytes;
+      const float* bl = reinterpret_cast<const float*>(vl + L::kVBytes);
 
-    // S^T for the tile's four 16-key groups: rows keys 16u + 4g + r, column query j.
-    f32x4 s4[4];
+      // S^T for the tile's four 16-key groups: rows keys 16u + 4g + r, column query j.
+      f32x4 s4[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      s4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int r = 16 * u + j;  // A row: key
+      for (int u = 0; u < 4; ++u) {
+        s4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int r = 16 * u + j;  // A row: key
 #pragma unroll
-      for (int s = 0; s < kSteps; ++s) {
-        const int chunk = (4 * s + g) ^ (r & (L::kCpr - 1));
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * HDP * 2 + chunk * 16);
-        s4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], s4[u], 0, 0, 0);
+        for (int s = 0; s < kSteps; ++s) {
+          const int chunk = (4 * s + g) ^ (r & (L::kCpr - 1));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * HDP * 2 + chunk * 16);
+          s4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], s4[u], 0, 0, 0);
+        }
       }
-    }
-    // Scale, mask, and the tile's maximum per query.
-    float mt = -INFINITY;
+      // Scale, mask, and the tile's maximum per query.
+      float mt = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 b = *reinterpret_cast<const float4*>(bl + 16 * u + 4 * g);
-      s4[u][0] = s4[u][0] * p.scale_l2 + b.x;
-      s4[u][1] = s4[u][1] * p.scale_l2 + b.y;
-      s4[u][2] = s4[u][2] * p.scale_l2 + b.z;
-      s4[u][3] = s4[u][3] * p.scale_l2 + b.w;
-      mt = fmaxf(mt, fmaxf(fmaxf(s4[u][0], s4[u][1]), fmaxf(s4[u][2], s4[u][3])));
-    }
-    mt = wave_max16(mt);
-    const float m_new = fmaxf(m_run, mt);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no valid key yet: every weight is 0
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    m_run = m_new;
-    // Weights, rounded to bf16 as the PV product takes them; the sum adds the rounded values.
-    bf16x8 pb[2];
-    float ls = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const __bf16 w = static_cast<__bf16>(__builtin_amdgcn_exp2f(s4[u][r] - m_use));
-        pb[u >> 1][(u & 1) * 4 + r] = w;
-        ls += static_cast<float>(w);
+      for (int u = 0; u < 4; ++u) {
+        const float4 b = *reinterpret_cast<const float4*>(bl + 16 * u + 4 * g);
+        s4[u][0] = s4[u][0] * p.scale_l2 + b.x;
+        s4[u][1] = s4[u][1] * p.scale_l2 + b.y;
+        s4[u][2] = s4[u][2] * p.scale_l2 + b.z;
+        s4[u][3] = s4[u][3] * p.scale_l2 + b.w;
+        mt = fmaxf(mt, fmaxf(fmaxf(s4[u][0], s4[u][1]), fmaxf(s4[u][2], s4[u][3])));
       }
-    }
-    l_part = l_part * alpha + ls;
+      mt = wave_max16(mt);
+      // The running maximum moves only when the tile's exceeds it by more than kLazy (log2 units):
+      // weights then stay below 2^kLazy, and numerator and denominator share whichever maximum is
+      // used, so the result is the same up to rounding while most tiles skip the rescale.
+      const float m_new = mt > m_run + kLazy ? mt : m_run;
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;  // no valid key yet: every weight is 0
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      m_run = m_new;
+      // Weights, rounded to bf16 as the PV product takes them; the sum adds the rounded values.
+      bf16x8 pb[2];
+      float ls = 0.f;
 #pragma unroll
-    for (int i = 0; i < kDTiles; ++i) acc[i] *= alpha;
-    // O^T += V^T . P^T: k slot 8g + e of product mf is key 32mf + 4g + e (e < 4) or
-    // 32mf + 16 + 4g + (e - 4): the keys this lane's weights belong to.
+      for (int u = 0; u < 4; ++u) {
 #pragma unroll
-    for (int dt = 0; dt < kDTiles; ++dt) {
-      const int r = 16 * dt + j;  // A row: dim
-      const uint8_t* vrow = vl + r * (kKeyTile * 2);
+        for (int r = 0; r < 4; ++r) {
+          const __bf16 w = static_cast<__bf16>(__builtin_amdgcn_exp2f(s4[u][r] - m_use));
+          pb[u >> 1][(u & 1) * 4 + r] = w;
+          ls += static_cast<float>(w);
+        }
+      }
+      l_part = l_part * alpha + ls;
+      if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int mf = 0; mf < 2; ++mf) {
-        const int k0 = 32 * mf + 4 * g, k1 = k0 + 16;  // first keys of the two 8-byte halves
-        const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((k0 >> 3) ^ (r & 7)) * 16) + (k0 & 7) * 2);
-        const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((k1 >> 3) ^ (r & 7)) * 16) + (k1 & 7) * 2);
-        const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mf], acc[dt], 0, 0, 0);
+        for (int i = 0; i < kDTiles; ++i) acc[i] *= alpha;
+      }
+      // O^T += V^T . P^T: k slot 8g + e of product mf is key 32mf + 4g + e (e < 4) or
+      // 32mf + 16 + 4g + (e - 4): the keys this lane's weights belong to.
+#pragma unroll
+      for (int dt = 0; dt < kDTiles; ++dt) {
+        const int r = 16 * dt + j;  // A row: dim
+        const uint8_t* vrow = vl + r * (kKeyTile * 2);
+#pragma unroll
+        for (int mf = 0; mf < 2; ++mf) {
+          const int k0 = 32 * mf + 4 * g, k1 = k0 + 16;  // first keys of the two 8-byte halves
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((k0 >> 3) ^ (r & 7)) * 16) + (k0 & 7) * 2);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((k1 >> 3) ^ (r & 7)) * 16) + (k1 & 7) * 2);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mf], acc[dt], 0, 0, 0);
+        }
       }
     }
     wait_vmcnt<0>();
-    __syncthreads();  // tile kt+1 is in; every wave is done with buffer kt & 1
+    __syncthreads();  // the next tiles are in; every wave is done with this iteration's buffers
   }
 
-  // Normalise and store: lane holds dims 16dt + 4g .. +3 of query q0 + 16·wave + j.
+  // Merge: the odd half's state goes through LDS (the tile buffers are free after the last
+  // barrier), laid out [query group][field][lane].
+  float* mg = reinterpret_cast<float*>(lds) + qw * (kMergeFloats * 64);
+  if (hf == 1) {
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mg[(4 * dt + r) * 64 + lane] = acc[dt][r];
+    mg[(4 * kDTiles) * 64 + lane] = m_run;
+    mg[(4 * kDTiles + 1) * 64 + lane] = l_part;
+  }
+  __syncthreads();
+  if (hf == 1) return;
+  {
+    const float m1 = mg[(4 * kDTiles) * 64 + lane];
+    const float m = fmaxf(m_run, m1);
+    const float m_use = m == -INFINITY ? 0.f : m;
+    const float a0 = __builtin_amdgcn_exp2f(m_run - m_use), a1 = __builtin_amdgcn_exp2f(m1 - m_use);
+    l_part = l_part * a0 + mg[(4 * kDTiles + 1) * 64 + lane] * a1;
+#pragma unroll
+    for (int dt = 0; dt < kDTiles; ++dt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * a0 + mg[(4 * dt + r) * 64 + lane] * a1;
+  }
+
+  // Normalise and store: lane holds dims 16dt + 4g .. +3 of query q0 + 16·qw + j.
   const float l = sum_groups16(l_part);
   const float inv = 1.f / l;  // no valid key: 1/0, and 0 · inf = NaN, as the page's arithmetic gives
-  const int q = q0 + 16 * wave + j;
+  const int q = q0 + 16 * qw + j;
   if (q < p.n) {
     float* orow = p.o + static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
+    const bool v4 = (p.hd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.o) & 15) == 0;
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) {
+      const int c = 16 * dt + 4 * g;
+      if (v4) {
+        if (c < p.hd)
+          *reinterpret_cast<float4*>(orow + c) =
+              make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
+      } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int c = 16 * dt + 4 * g + r;
-        if (c < p.hd) orow[c] = acc[dt][r] * inv;
+        for (int r = 0; r < 4; ++r)
+          if (c + r < p.hd) orow[c + r] = acc[dt][r] * inv;
       }
     }
   }
@@ -488,8 +578,9 @@ hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o
   uint16_t* kb = reinterpret_cast<uint16_t*>(ws);
   uint16_t* vt = reinterpret_cast<uint16_t*>(ws + kv);
   float* kbias = reinterpret_cast<float*>(ws + 2 * kv);
+  const bool vec4 = hd % 4 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 15) == 0;
   hipLaunchKernelGGL(attn_pack_kernel<HDP>, dim3(npad / kKeyTile, heads), dim3(256), 0, stream, qkv, valid, kb, vt,
-                     kbias, n, npad, heads, hd);
+                     kbias, n, npad, heads, hd, vec4);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AttnParams p{};
@@ -506,7 +597,7 @@ hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o
   p.items = heads * p.qtiles;
   p.per_xcd = (p.items + 7) / 8;
   p.scale_l2 = scale * 1.4426950408889634f;
-  hipLaunchKernelGGL(attention_kernel<HDP>, dim3(p.per_xcd * 8), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(attention_kernel<HDP>, dim3(p.per_xcd * 8), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
