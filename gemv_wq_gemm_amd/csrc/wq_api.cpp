@@ -539,6 +539,8 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   if (!h || !valid || !workspace || (rot > 0 && !cs)) return fail(WQ_ERR_NULL, "h, valid, workspace (and cs) must not be NULL");
   if (!aligned(h, 16) || !aligned(workspace, 256))
     return fail(WQ_ERR_ALIGN, "h must be 16-byte aligned and the workspace 256-byte aligned");
+  if (!aligned(valid, 4) || (cs && !aligned(cs, 4)) || (l->qn && !aligned(l->qn, 4)) || (l->kn && !aligned(l->kn, 4)))
+    return fail(WQ_ERR_ALIGN, "valid, cs, qn and kn must be 4-byte aligned");
   const EncoderWs w = encoder_ws(n, d, heads, inter);
   if (workspace_bytes < w.total)
     return fail(WQ_ERR_SHAPE, "the workspace holds %lld bytes, %lld needed", (long long)workspace_bytes, (long long)w.total);
@@ -554,9 +556,13 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   if ((r = wq_layer_norm(h, l->ln1, a, n, d, stream))) return r;
   if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, path, stream)))
     return r;
+  // The q/k norm + rotation runs fused with the attention's pack: k goes to the workspace in bf16
+  // only (the f32 rows are not needed after), q is rewritten in place as wq_qk_norm_rope would.
   clear_error();
-  if ((r = qk_checked(qkv, l->qn, l->kn, cs, n, heads, hd, rot, stream))) return r;
-  if ((r = attention_checked(qkv, valid, att, attn_ws, w.total - w.attn, n, heads, hd, scale, stream))) return r;
+  hipError_t he = wq::launch_qk_attention(qkv, l->qn, l->kn, cs, valid, att, attn_ws, static_cast<int>(n),
+                                          static_cast<int>(heads), static_cast<int>(hd), static_cast<int>(rot), scale,
+                                          static_cast<hipStream_t>(stream));
+  if (he != hipSuccess) return hip_fail(he, "q/k norm + attention launch");
   if ((r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, path, stream)))
     return r;
   if ((r = wq_layer_norm(h, l->ln2, a, n, d, stream))) return r;

@@ -149,33 +149,21 @@ __global__ __launch_bounds__(256) void layer_norm_scalar_kernel(const float* x, 
 // q/k LayerNorm + rotation
 // ---------------------------------------------------------------------------------------------
 
-// E elements per lane (hd <= 64·E). Every wave reaches the barrier; waves past the last vector
-// only skip their loads and stores.
-template <int E>
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(float* qkv, const float* __restrict__ qn,
-                                                            const float* __restrict__ kn,
-                                                            const float* __restrict__ cs, int n, int heads, int hd,
-                                                            int rot) {
-  __shared__ float vbuf[4][64 * E];
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const long long vec = static_cast<long long>(blockIdx.x) * 4 + wave;
-  const bool live = vec < 2LL * n * heads;
-  const long long t = live ? vec / (2 * heads) : 0;
-  const int rem = static_cast<int>(vec - t * 2 * heads);
-  const int which = live ? rem / heads : 0;  // 0: q, 1: k
-  const int h = live ? rem % heads : 0;
-  const long long d = static_cast<long long>(heads) * hd;
-  float* base = qkv + t * 3 * d + which * d + static_cast<long long>(h) * hd;
+// Orders one wave's LDS writes before its later reads by other lanes of the same wave.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
-  float v[E];
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    const int i = lane + 64 * e;
-    v[e] = live && i < hd ? base[i] : 0.f;
-  }
-  const float* nw = which == 0 ? qn : kn;
-  if (nw != nullptr) {  // uniform: both or neither are given
+// One q or k vector of hd values held E per lane (element lane + 64e): its LayerNorm when nw is
+// given (mean, then the summed squared deviations, then (v - mean) * inv * w + b), then the
+// rotation of its first rot dims by frame t's row of the table (cos_t, sin_t). vbuf is 64·E floats
+// of this wave's LDS, through which a lane reads its rotation partner.
+template <int E>
+__device__ __forceinline__ void qk_vector(float (&v)[E], const float* __restrict__ nw, const float* cos_t,
+                                          const float* sin_t, int hd, int rot, float* vbuf, int lane) {
+  if (nw != nullptr) {  // wave-uniform
     float s = 0.f;
 #pragma unroll
     for (int e = 0; e < E; ++e) s += v[e];
@@ -191,27 +179,58 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(float* qkv, const flo
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = lane + 64 * e;
-      if (live && i < hd) v[e] = (v[e] - mean) * inv * nw[i] + nw[hd + i];
+      if (i < hd) v[e] = (v[e] - mean) * inv * nw[i] + nw[hd + i];
     }
   }
+  if (rot == 0) return;
+  wave_lds_sync();  // the previous vector's partner reads are done
 #pragma unroll
-  for (int e = 0; e < E; ++e) vbuf[wave][lane + 64 * e] = v[e];
-  __syncthreads();
+  for (int e = 0; e < E; ++e) vbuf[lane + 64 * e] = v[e];
+  wave_lds_sync();
   const int half = rot >> 1;
-  const float* cos_t = cs + t * half;
-  const float* sin_t = cs + static_cast<long long>(n) * half + t * half;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = lane + 64 * e;
-    if (!live || i >= hd) continue;
-    float o = v[e];
     if (i < half) {
-      o = v[e] * cos_t[i] - vbuf[wave][i + half] * sin_t[i];
+      v[e] = v[e] * cos_t[i] - vbuf[i + half] * sin_t[i];
     } else if (i < rot) {
       const int j = i - half;
-      o = v[e] * cos_t[j] + vbuf[wave][j] * sin_t[j];
+      v[e] = v[e] * cos_t[j] + vbuf[j] * sin_t[j];
     }
-    base[i] = o;
+  }
+}
+
+// E elements per lane (hd <= 64·E); one wave per (frame, head, q or k) vector, in place.
+template <int E>
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(float* qkv, const float* __restrict__ qn,
+                                                            const float* __restrict__ kn,
+                                                            const float* __restrict__ cs, int n, int heads, int hd,
+                                                            int rot) {
+  __shared__ float vbuf[4][64 * E];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const long long vec = static_cast<long long>(blockIdx.x) * 4 + wave;
+  if (vec >= 2LL * n * heads) return;  // wave-uniform; only wave-level synchronisation follows
+  const long long t = vec / (2 * heads);
+  const int rem = static_cast<int>(vec - t * 2 * heads);
+  const int which = rem / heads;  // 0: q, 1: k
+  const int h = rem % heads;
+  const long long d = static_cast<long long>(heads) * hd;
+  float* base = qkv + t * 3 * d + which * d + static_cast<long long>(h) * hd;
+  const int half = rot >> 1;
+
+  float v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    v[e] = i < hd ? base[i] : 0.f;
+  }
+  qk_vector<E>(v, which == 0 ? qn : kn, cs + t * half, cs + static_cast<long long>(n) * half + t * half, hd, rot,
+               vbuf[wave], lane);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    if (i < hd) base[i] = v[e];
   }
 }
 
@@ -274,6 +293,82 @@ __global__ __launch_bounds__(256) void attn_pack_kernel(const float* __restrict_
   uint16_t* vout = vt + static_cast<long long>(h) * HDP * npad + t0;
   for (int i = threadIdx.x; i < HDP * (kKeyTile / 8); i += 256) {
     const int c = i / (kKeyTile / 8), g = i % (kKeyTile / 8);
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = static_cast<uint32_t>(vs[8 * g + 2 * j][c]) | (static_cast<uint32_t>(vs[8 * g + 2 * j + 1][c]) << 16);
+    *reinterpret_cast<uint4*>(vout + static_cast<long long>(c) * npad + 8 * g) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// The q/k norm + rotation and the pack in one pass, for a block's attention: grid (npad / 8,
+// heads), one frame per wave and four waves per workgroup, q and k of the frame side by side: q
+// normed and rotated and written back in place (f32, as qk_norm_rope_kernel writes it), k normed,
+// rotated and rounded to bf16 into kb, v rounded to bf16 and transposed into vt through LDS, as
+// attn_pack_kernel lays them out; head 0's workgroups write the key bias. k is not written back to
+// qkv. (HDP, E): (32, 1), (64, 1), (128, 2).
+constexpr int kQkFrames = 8;  // frames per workgroup
+template <int HDP, int E>
+__global__ __launch_bounds__(256) void qk_pack_kernel(float* qkv, const float* __restrict__ qn,
+                                                       const float* __restrict__ kn, const float* __restrict__ cs,
+                                                       const int32_t* __restrict__ valid, uint16_t* __restrict__ kb,
+                                                       uint16_t* __restrict__ vt, float* __restrict__ kbias, int n,
+                                                       int npad, int heads, int hd, int rot) {
+  static_assert(64 * E >= HDP, "a wave's lanes cover the padded head");
+  __shared__ float vbuf[4][2][64 * E];
+  __shared__ __attribute__((aligned(16))) uint16_t vs[kQkFrames][HDP + 8];
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kQkFrames;
+  const int h = blockIdx.y;
+  const long long d = static_cast<long long>(heads) * hd;
+  const int half = rot >> 1;
+  for (int r = wave; r < kQkFrames; r += 4) {
+    const int t = t0 + r;
+    uint16_t* krow = kb + (static_cast<long long>(h) * npad + t) * HDP;
+    if (t < n) {  // wave-uniform
+      float* qrow = qkv + static_cast<long long>(t) * 3 * d + static_cast<long long>(h) * hd;
+      const float* cos_t = cs + static_cast<long long>(t) * half;
+      const float* sin_t = cs + static_cast<long long>(n) * half + static_cast<long long>(t) * half;
+      float vq[E], vk[E], vv[E];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int c = lane + 64 * e;
+        vq[e] = c < hd ? qrow[c] : 0.f;
+        vk[e] = c < hd ? qrow[d + c] : 0.f;
+        vv[e] = c < hd ? qrow[2 * d + c] : 0.f;
+      }
+      qk_vector<E>(vq, qn, cos_t, sin_t, hd, rot, vbuf[wave][0], lane);
+      qk_vector<E>(vk, kn, cos_t, sin_t, hd, rot, vbuf[wave][1], lane);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int c = lane + 64 * e;
+        if (c < hd) qrow[c] = vq[e];
+        if (c < HDP) {
+          krow[c] = c < hd ? bf16_bits_rne(vk[e]) : uint16_t(0);
+          vs[r][c] = c < hd ? bf16_bits_rne(vv[e]) : uint16_t(0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int c = lane + 64 * e;
+        if (c < HDP) {
+          krow[c] = 0;
+          vs[r][c] = 0;
+        }
+      }
+    }
+  }
+  if (h == 0 && threadIdx.x < kQkFrames) {
+    const int t = t0 + threadIdx.x;
+    kbias[t] = t < n && valid[t] != 0 ? 0.f : -INFINITY;
+  }
+  __syncthreads();
+  // vt[h][c][t0 .. t0+7]: 8 frames (16 bytes) per store.
+  uint16_t* vout = vt + static_cast<long long>(h) * HDP * npad + t0;
+  for (int i = threadIdx.x; i < HDP * (kQkFrames / 8); i += 256) {
+    const int c = i / (kQkFrames / 8), g = i % (kQkFrames / 8);
     uint32_t w[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -570,27 +665,35 @@ long long attention_workspace_bytes(long long n, long long heads, long long hd) 
   return 2 * kv + (npad * 4 + 255) / 256 * 256;
 }
 
+// The attention workspace for these sizes: kb and vt (bf16), then the key bias, each part on a
+// 256-byte boundary.
+struct AttnWs {
+  uint16_t* kb;
+  uint16_t* vt;
+  float* kbias;
+  int npad;
+};
+
 template <int HDP>
-hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o, uint8_t* ws, int n, int heads,
-                                int hd, float scale, hipStream_t stream) {
+AttnWs attn_ws(void* ws, int n, int heads) {
   const int npad = (n + kKeyTile - 1) / kKeyTile * kKeyTile;
   const long long kv = (static_cast<long long>(heads) * npad * HDP * 2 + 255) / 256 * 256;
-  uint16_t* kb = reinterpret_cast<uint16_t*>(ws);
-  uint16_t* vt = reinterpret_cast<uint16_t*>(ws + kv);
-  float* kbias = reinterpret_cast<float*>(ws + 2 * kv);
-  const bool vec4 = hd % 4 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 15) == 0;
-  hipLaunchKernelGGL(attn_pack_kernel<HDP>, dim3(npad / kKeyTile, heads), dim3(256), 0, stream, qkv, valid, kb, vt,
-                     kbias, n, npad, heads, hd, vec4);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  return {reinterpret_cast<uint16_t*>(w), reinterpret_cast<uint16_t*>(w + kv), reinterpret_cast<float*>(w + 2 * kv),
+          npad};
+}
+
+template <int HDP>
+hipError_t run_attention(const float* qkv, const AttnWs& w, float* o, int n, int heads, int hd, float scale,
+                         hipStream_t stream) {
   AttnParams p{};
   p.qkv = qkv;
-  p.kb = kb;
-  p.vt = vt;
-  p.kbias = kbias;
+  p.kb = w.kb;
+  p.vt = w.vt;
+  p.kbias = w.kbias;
   p.o = o;
   p.n = n;
-  p.npad = npad;
+  p.npad = w.npad;
   p.heads = heads;
   p.hd = hd;
   p.qtiles = (n + kQueryTile - 1) / kQueryTile;
@@ -601,14 +704,48 @@ hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o
   return hipGetLastError();
 }
 
+template <int HDP>
+hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
+                                float scale, hipStream_t stream) {
+  const AttnWs w = attn_ws<HDP>(ws, n, heads);
+  const bool vec4 = hd % 4 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 15) == 0;
+  hipLaunchKernelGGL(attn_pack_kernel<HDP>, dim3(w.npad / kKeyTile, heads), dim3(256), 0, stream, qkv, valid, w.kb,
+                     w.vt, w.kbias, n, w.npad, heads, hd, vec4);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return run_attention<HDP>(qkv, w, o, n, heads, hd, scale, stream);
+}
+
+template <int HDP, int E>
+hipError_t launch_qk_attention_hdp(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
+                                   float* o, void* ws, int n, int heads, int hd, int rot, float scale,
+                                   hipStream_t stream) {
+  const AttnWs w = attn_ws<HDP>(ws, n, heads);
+  hipLaunchKernelGGL((qk_pack_kernel<HDP, E>), dim3(w.npad / kQkFrames, heads), dim3(256), 0, stream, qkv, qn, kn, cs,
+                     valid, w.kb, w.vt, w.kbias, n, w.npad, heads, hd, rot);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return run_attention<HDP>(qkv, w, o, n, heads, hd, scale, stream);
+}
+
 hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
                             float scale, hipStream_t stream) {
   if (n == 0) return hipSuccess;
-  uint8_t* w = static_cast<uint8_t*>(ws);
   switch (head_pad(hd)) {
-    case 32: return launch_attention_hdp<32>(qkv, valid, o, w, n, heads, hd, scale, stream);
-    case 64: return launch_attention_hdp<64>(qkv, valid, o, w, n, heads, hd, scale, stream);
-    default: return launch_attention_hdp<128>(qkv, valid, o, w, n, heads, hd, scale, stream);
+    case 32: return launch_attention_hdp<32>(qkv, valid, o, ws, n, heads, hd, scale, stream);
+    case 64: return launch_attention_hdp<64>(qkv, valid, o, ws, n, heads, hd, scale, stream);
+    default: return launch_attention_hdp<128>(qkv, valid, o, ws, n, heads, hd, scale, stream);
+  }
+}
+
+hipError_t launch_qk_attention(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
+                               float* o, void* ws, int n, int heads, int hd, int rot, float scale,
+                               hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  switch (head_pad(hd)) {
+    case 32: return launch_qk_attention_hdp<32, 1>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
+    case 64: return launch_qk_attention_hdp<64, 1>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
+    default: return launch_qk_attention_hdp<128, 2>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
   }
 }
 

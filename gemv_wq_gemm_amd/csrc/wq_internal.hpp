@@ -95,5 +95,10 @@ hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, con
 long long attention_workspace_bytes(long long n, long long heads, long long hd);
 hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
                             float scale, hipStream_t stream);
+// q/k norm + rotation fused with the attention's pack (k is not written back to qkv), then the
+// attention: the block's path. Same workspace as launch_attention.
+hipError_t launch_qk_attention(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
+                               float* o, void* ws, int n, int heads, int hd, int rot, float scale,
+                               hipStream_t stream);
 
 }  // namespace wq
