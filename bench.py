@@ -213,7 +213,7 @@ def main():
                 "note": f"profiling run of legs {sorted(legs)}; the step (the chain) was not run"}
     line["rooflines"] = _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic)
     if "enc" in legs:
-        enc_rl, enc_other = _encoder(torch, wq, synth, dev, timer, to_dev, args)
+        enc_rl, enc_other = _encoder(torch, wq, synth, dev, timer, to_dev, args, read_traffic)
         line["rooflines"].update(enc_rl)
         others.update(enc_other)
     if not args.no_others and "others" in legs:
@@ -463,7 +463,7 @@ def _moe(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic, legs
     del big
 
 
-def _encoder(torch, wq, synth, dev, timer, to_dev, args):
+def _encoder(torch, wq, synth, dev, timer, to_dev, args, read_traffic):
     """The rest of the encoder block at the workload's size (1500 frames, d = 1024, 8 heads of 128,
     all dims rotated, the last 100 frames masked): LayerNorm, q/k norm + rotation and attention
     each alone, and the whole 24-block forward (embedding LayerNorm, 24 blocks with bf16 weights,
@@ -482,7 +482,8 @@ def _encoder(torch, wq, synth, dev, timer, to_dev, args):
     nb = 2 * n * d * 4 + 2 * d * 4
     gbs = nb / (st["median_us"] * 1e-6) / 1e9
     rl["NEXT4_layer_norm_1500x1024"] = {**st, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                        "bound": "hbm", "bytes": nb}
+                                        "bound": "hbm", "bytes": nb,
+                                        "traffic": read_traffic(COUNTERS, "enc_layer_norm")}
     del xs, ys
 
     # q/k norm + rotation in place on [1500][3 x 1024]: q and k read and written once.
@@ -494,7 +495,8 @@ def _encoder(torch, wq, synth, dev, timer, to_dev, args):
     nb = 2 * n * 2 * d * 4 + n * rot * 4
     gbs = nb / (st["median_us"] * 1e-6) / 1e9
     rl["NEXT4_qk_norm_rope_1500x8x128"] = {**st, "GB/s": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                                           "bound": "hbm", "bytes": nb}
+                                           "bound": "hbm", "bytes": nb,
+                                           "traffic": read_traffic(COUNTERS, "enc_qk_norm_rope")}
 
     # Attention: the call (pack + flash kernel); 4 n^2 hd FLOP per head, masked keys included.
     valid = to_dev(synth.key_mask(n, synth.ENCODER_VALID))
@@ -507,7 +509,9 @@ def _encoder(torch, wq, synth, dev, timer, to_dev, args):
     tf = fl / (st["median_us"] * 1e-6) / 1e12
     rl["NEXT4_attention_1500x8x128"] = {**st, "TFLOP/s": round(tf, 1), "frac": round(tf / BF16_PEAK_TFLOPS, 4),
                                         "bound": "mfma", "flop": fl,
-                                        "note": "pack (K, V to bf16) + flash kernel; kernel split in the trace"}
+                                        "note": "pack (K, V to bf16) + flash kernel; kernel split in the trace",
+                                        "traffic": {"pack": read_traffic(COUNTERS, "enc_attn_pack"),
+                                                    "attention_kernel": read_traffic(COUNTERS, "enc_attention")}}
     del qkvs, att, ws
 
     if args.no_others:
