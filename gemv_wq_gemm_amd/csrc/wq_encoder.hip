@@ -392,6 +392,7 @@ struct AttnParams {
   int items;       // heads * qtiles
   int per_xcd;     // ceil(items / 8)
   float scale_l2;  // scale * log2(e): scores enter exp2
+  int v4;          // hd % 8 == 0 and qkv, o 16-byte aligned: 16-byte loads of q, stores of o
 };
 
 // LDS tile layout (one buffer):
@@ -440,16 +441,36 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   const long long d = static_cast<long long>(p.heads) * p.hd;
 
   // Q fragments (B operand of S^T): query q0 + 16·qw + j, dims 32s + 8g .. +7, rounded to bf16.
+  // Rows past n read row n-1 and dims past hd read in-row values (zeroed below), so with p.v4 the
+  // loads are unconditional 16-byte loads that the compiler issues back to back.
   bf16x8 qf[kSteps];
   {
     const int q = q0 + 16 * qw + j;
-    const float* qr = p.qkv + static_cast<long long>(q) * 3 * d + static_cast<long long>(h) * p.hd;
+    const bool qin = q < p.n;
+    const float* qr = p.qkv + static_cast<long long>(qin ? q : p.n - 1) * 3 * d + static_cast<long long>(h) * p.hd;
+    if (p.v4) {
+      float4 lo[kSteps], hi[kSteps];
 #pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
+      for (int s = 0; s < kSteps; ++s) {
+        const int c = min(32 * s + 8 * g, p.hd - 8);  // hd % 8 == 0 with v4: in the row
+        lo[s] = *reinterpret_cast<const float4*>(qr + c);
+        hi[s] = *reinterpret_cast<const float4*>(qr + c + 4);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * s + 8 * g + e;
-        qf[s][e] = static_cast<__bf16>(q < p.n && c < p.hd ? qr[c] : 0.f);
+      for (int s = 0; s < kSteps; ++s) {
+        const bool in = qin && 32 * s + 8 * g < p.hd;
+        const float v[8] = {lo[s].x, lo[s].y, lo[s].z, lo[s].w, hi[s].x, hi[s].y, hi[s].z, hi[s].w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(in ? v[e] : 0.f);
+      }
+    } else {
+#pragma unroll
+      for (int s = 0; s < kSteps; ++s) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int c = 32 * s + 8 * g + e;
+          qf[s][e] = static_cast<__bf16>(qin && c < p.hd ? qr[c] : 0.f);
+        }
       }
     }
   }
@@ -601,11 +622,10 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   const int q = q0 + 16 * qw + j;
   if (q < p.n) {
     float* orow = p.o + static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
-    const bool v4 = (p.hd & 3) == 0 && (reinterpret_cast<uintptr_t>(p.o) & 15) == 0;
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) {
       const int c = 16 * dt + 4 * g;
-      if (v4) {
+      if (p.v4) {
         if (c < p.hd)
           *reinterpret_cast<float4*>(orow + c) =
               make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
@@ -700,6 +720,7 @@ hipError_t run_attention(const float* qkv, const AttnWs& w, float* o, int n, int
   p.items = heads * p.qtiles;
   p.per_xcd = (p.items + 7) / 8;
   p.scale_l2 = scale * 1.4426950408889634f;
+  p.v4 = hd % 8 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 15) == 0 && (reinterpret_cast<uintptr_t>(o) & 15) == 0;
   hipLaunchKernelGGL(attention_kernel<HDP>, dim3(p.per_xcd * 8), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
