@@ -9,7 +9,7 @@
 //    butterfly sums across the wave (two passes over registers, as the page's two passes over
 //    memory). Other rows take a scalar kernel that reads the row three times. HBM-bound: 8·d bytes
 //    per row.
-//  * q/k norm + rotation: one wave per (frame, head, q or k) vector, in place. The normalised
+//  * q/k norm + rotation: one wave per (frame, head), its q and k vectors side by side, in place. The normalised
 //    vector goes through wave-private LDS so each lane can read its rotation partner (dim i pairs
 //    with dim i + rot/2). HBM-bound: 16·hd bytes per vector.
 //  * Attention, in two kernels:
@@ -91,12 +91,15 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, con
   if (row >= n) return;  // wave-uniform; no barrier follows
   const int nv = d >> 2;
   const float4* xr = reinterpret_cast<const float4*>(x + row * d);
+  // Loads are unconditional (lanes past the row re-read its last float4, zeroed after), so they
+  // issue back to back instead of one guarded load at a time.
   float4 v[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = xr[min(lane + 64 * i, nv - 1)];
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int c = lane + 64 * i;
-    v[i] = c < nv ? xr[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane + 64 * i >= nv) v[i] = make_float4(0.f, 0.f, 0.f, 0.f);
     s += (v[i].x + v[i].y) + (v[i].z + v[i].w);
   }
   const float fd = static_cast<float>(d);
@@ -112,11 +115,18 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, con
   const float inv = rsqrtf(wave_sum(q) / fd + kLnEps);
   const float4* w4 = reinterpret_cast<const float4*>(wb);
   float4* yr = reinterpret_cast<float4*>(y + row * d);
+  float4 wv[NV], bv[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int c = min(lane + 64 * i, nv - 1);
+    wv[i] = w4[c];
+    bv[i] = w4[nv + c];
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int c = lane + 64 * i;
     if (c < nv) {
-      const float4 w = w4[c], b = w4[nv + c];
+      const float4 w = wv[i], b = bv[i];
       yr[c] = make_float4((v[i].x - mean) * inv * w.x + b.x, (v[i].y - mean) * inv * w.y + b.y,
                           (v[i].z - mean) * inv * w.z + b.z, (v[i].w - mean) * inv * w.w + b.w);
     }
@@ -163,6 +173,24 @@ __device__ __forceinline__ void wave_lds_sync() {
 template <int E>
 __device__ __forceinline__ void qk_vector(float (&v)[E], const float* __restrict__ nw, const float* cos_t,
                                           const float* sin_t, int hd, int rot, float* vbuf, int lane) {
+  // Every load below is unconditional, from an index clamped into range (the value then unused),
+  // so the loads issue back to back.
+  const int half = rot >> 1;
+  float c_[E], s_[E], w_[E], b_[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int i = lane + 64 * e;
+    if (half > 0) {
+      const int t = i < half ? i : (i < rot ? i - half : 0);
+      c_[e] = cos_t[t];
+      s_[e] = sin_t[t];
+    }
+    if (nw != nullptr) {
+      const int ic = min(i, hd - 1);
+      w_[e] = nw[ic];
+      b_[e] = nw[hd + ic];
+    }
+  }
   if (nw != nullptr) {  // wave-uniform
     float s = 0.f;
 #pragma unroll
@@ -179,7 +207,7 @@ __device__ __forceinline__ void qk_vector(float (&v)[E], const float* __restrict
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int i = lane + 64 * e;
-      if (i < hd) v[e] = (v[e] - mean) * inv * nw[i] + nw[hd + i];
+      if (i < hd) v[e] = (v[e] - mean) * inv * w_[e] + b_[e];
     }
   }
   if (rot == 0) return;
@@ -187,50 +215,57 @@ __device__ __forceinline__ void qk_vector(float (&v)[E], const float* __restrict
 #pragma unroll
   for (int e = 0; e < E; ++e) vbuf[lane + 64 * e] = v[e];
   wave_lds_sync();
-  const int half = rot >> 1;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = lane + 64 * e;
+    const float partner = vbuf[i < half ? i + half : (i < rot ? i - half : i)];
     if (i < half) {
-      v[e] = v[e] * cos_t[i] - vbuf[i + half] * sin_t[i];
+      v[e] = v[e] * c_[e] - partner * s_[e];
     } else if (i < rot) {
-      const int j = i - half;
-      v[e] = v[e] * cos_t[j] + vbuf[j] * sin_t[j];
+      v[e] = v[e] * c_[e] + partner * s_[e];
     }
   }
 }
 
-// E elements per lane (hd <= 64·E); one wave per (frame, head, q or k) vector, in place.
+// E elements per lane (hd <= 64·E); one wave per (frame, head), q and k side by side, in place.
 template <int E>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(float* qkv, const float* __restrict__ qn,
                                                             const float* __restrict__ kn,
                                                             const float* __restrict__ cs, int n, int heads, int hd,
                                                             int rot) {
-  __shared__ float vbuf[4][64 * E];
+  __shared__ float vbuf[4][2][64 * E];
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const long long vec = static_cast<long long>(blockIdx.x) * 4 + wave;
-  if (vec >= 2LL * n * heads) return;  // wave-uniform; only wave-level synchronisation follows
-  const long long t = vec / (2 * heads);
-  const int rem = static_cast<int>(vec - t * 2 * heads);
-  const int which = rem / heads;  // 0: q, 1: k
-  const int h = rem % heads;
+  if (vec >= static_cast<long long>(n) * heads) return;  // wave-uniform; only wave-level synchronisation follows
+  const long long t = vec / heads;
+  const int h = static_cast<int>(vec - t * heads);
   const long long d = static_cast<long long>(heads) * hd;
-  float* base = qkv + t * 3 * d + which * d + static_cast<long long>(h) * hd;
+  float* qb = qkv + t * 3 * d + static_cast<long long>(h) * hd;
+  float* kb = qb + d;
   const int half = rot >> 1;
 
-  float v[E];
+  float vq[E], vk[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int i = lane + 64 * e;
-    v[e] = i < hd ? base[i] : 0.f;
+    const int c = min(lane + 64 * e, hd - 1);  // unconditional loads (zeroed past hd below)
+    vq[e] = qb[c];
+    vk[e] = kb[c];
   }
-  qk_vector<E>(v, which == 0 ? qn : kn, cs + t * half, cs + static_cast<long long>(n) * half + t * half, hd, rot,
-               vbuf[wave], lane);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (lane + 64 * e >= hd) vq[e] = vk[e] = 0.f;
+  const float* cos_t = cs + t * half;
+  const float* sin_t = cs + static_cast<long long>(n) * half + t * half;
+  qk_vector<E>(vq, qn, cos_t, sin_t, hd, rot, vbuf[wave][0], lane);
+  qk_vector<E>(vk, kn, cos_t, sin_t, hd, rot, vbuf[wave][1], lane);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int i = lane + 64 * e;
-    if (i < hd) base[i] = v[e];
+    if (i < hd) {
+      qb[i] = vq[e];
+      kb[i] = vk[e];
+    }
   }
 }
 
@@ -333,11 +368,14 @@ __global__ __launch_bounds__(256) void qk_pack_kernel(float* qkv, const float* _
       float vq[E], vk[E], vv[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) {
-        const int c = lane + 64 * e;
-        vq[e] = c < hd ? qrow[c] : 0.f;
-        vk[e] = c < hd ? qrow[d + c] : 0.f;
-        vv[e] = c < hd ? qrow[2 * d + c] : 0.f;
+        const int c = min(lane + 64 * e, hd - 1);  // unconditional loads (zeroed past hd below)
+        vq[e] = qrow[c];
+        vk[e] = qrow[d + c];
+        vv[e] = qrow[2 * d + c];
       }
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (lane + 64 * e >= hd) vq[e] = vk[e] = vv[e] = 0.f;
       qk_vector<E>(vq, qn, cos_t, sin_t, hd, rot, vbuf[wave][0], lane);
       qk_vector<E>(vk, kn, cos_t, sin_t, hd, rot, vbuf[wave][1], lane);
 #pragma unroll
@@ -665,7 +703,7 @@ hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, i
 
 hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int n, int heads,
                                int hd, int rot, hipStream_t stream) {
-  const long long vecs = 2LL * n * heads;
+  const long long vecs = static_cast<long long>(n) * heads;  // (frame, head) pairs
   if (vecs == 0) return hipSuccess;
   const dim3 grid(static_cast<unsigned>((vecs + 3) / 4)), block(256);
   if (hd <= 64)
