@@ -601,7 +601,52 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
   // The epilogue, with the flag tests taken once per workgroup and the bounds tests only on
   // tiles that reach past the edge of Y.
   const bool full = n0 + BM <= p.n && m0 + BN <= p.m;
+  // Tiles inside Y: no per-output branch. A guarded load or store per output compiles to a branch
+  // whose entry waits for every outstanding memory operation (the previous outputs' stores
+  // included), which serialises the tile's stores. Here Y is addressed through a buffer resource
+  // at the tile's corner: one 32-bit offset per fragment and lane, plus a scalar row offset per
+  // output, so the old values load back to back and the stores issue without waits between
+  // them. Taken when the tile's byte offsets fit in 31 bits.
+  const bool fast = full && p.dual == 0 &&
+                    (static_cast<long long>(BM) * p.ystride + BN) * 4 < (1LL << 31);
+  auto store_full = [&](auto act, auto res) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(p.y + static_cast<long long>(n0) * p.ystride + m0, 0,
+                                                        0x7FFFFFFF, 0x00020000);
+    const int rs = p.ystride * 4;  // bytes per row of Y
+    float old[FM][FN][16];
+    if constexpr (decltype(res)::value) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int vo = (wm * TM + i * 32 + 4 * (lane >> 5)) * rs + (wn * TN + j * 32 + frow) * 4;
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            old[i][j][v] = __builtin_bit_cast(
+                float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, (8 * (v >> 2) + (v & 3)) * rs, 0));
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int vo = (wm * TM + i * 32 + 4 * (lane >> 5)) * rs + (wn * TN + j * 32 + frow) * 4;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          float o = acc[i][j][v] + bias_v[j];
+          if constexpr (decltype(act)::value != 0) o = activation(o, decltype(act)::value);
+          o *= p.alpha;
+          if constexpr (decltype(res)::value) o += old[i][j][v];
+          // The b32 buffer builtins move 32-bit integers: the float's bits go through unchanged.
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, o), rsrc, vo, (8 * (v >> 2) + (v & 3)) * rs, 0);
+        }
+      }
+  };
   auto store = [&](auto act, auto res) {
+    if (fast) {
+      store_full(act, res);
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       const int col = m0 + wn * TN + j * 32 + frow;
