@@ -378,6 +378,63 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmParams p, int ti
 
   // ---- epilogue: lane holds column lane%32 and rows 8*(v/4) + 4*(lane/32) + v%4 of each fragment ----
   const bool first = blockIdx.z == 0;
+  // Tiles inside Y, without the k split or dual outputs: Y through a buffer resource at the
+  // tile's corner, old values loaded back to back and the stores issued without waits between
+  // them (a guarded per-output access compiles to a branch that waits for every earlier store),
+  // with the activation chosen at compile time.
+  if (!split && p.dual == 0 && n0 + BM <= p.n && m0 + BN <= p.m &&
+      (static_cast<long long>(BM) * p.ystride + BN) * 4 < (1LL << 31)) {
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(p.y + static_cast<long long>(n0) * p.ystride + m0, 0,
+                                                        0x7FFFFFFF, 0x00020000);
+    const int rs = p.ystride * 4;  // bytes per row of Y
+    float bv[C::FN];
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j) bv[j] = (p.flags & kEpiBias) ? p.bias[m0 + wn * C::TN + j * 32 + frow] : 0.f;
+    // Inlined by force: a call would take the accumulators' address and move them to scratch.
+    auto run = [&](auto act, auto res) __attribute__((always_inline)) {
+      float old[C::FM][C::FN][16];
+      if constexpr (decltype(res)::value) {
+#pragma unroll
+        for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+          for (int j = 0; j < C::FN; ++j) {
+            const int vo = (wm * C::TM + i * 32 + 4 * (lane >> 5)) * rs + (wn * C::TN + j * 32 + frow) * 4;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+              old[i][j][v] = __builtin_bit_cast(
+                  float, __builtin_amdgcn_raw_buffer_load_b32(rsrc, vo, (8 * (v >> 2) + (v & 3)) * rs, 0));
+          }
+      }
+#pragma unroll
+      for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) {
+          const int vo = (wm * C::TM + i * 32 + 4 * (lane >> 5)) * rs + (wn * C::TN + j * 32 + frow) * 4;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            float o = acc[i][j][v] + bv[j];
+            if constexpr (decltype(act)::value != 0) o = activation(o, decltype(act)::value);
+            o *= p.alpha;
+            if constexpr (decltype(res)::value) o += old[i][j][v];
+            // The b32 buffer builtins move 32-bit integers: the float's bits go through unchanged.
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, o), rsrc, vo,
+                                                  (8 * (v >> 2) + (v & 3)) * rs, 0);
+          }
+        }
+    };
+    auto with_residual = [&](auto act) __attribute__((always_inline)) {
+      if (p.flags & kEpiResidual) run(act, std::true_type{});
+      else run(act, std::false_type{});
+    };
+    switch (p.flags & kEpiAct) {
+      case kEpiGelu: with_residual(std::integral_constant<unsigned, kEpiGelu>{}); break;
+      case kEpiSilu: with_residual(std::integral_constant<unsigned, kEpiSilu>{}); break;
+      case kEpiRelu: with_residual(std::integral_constant<unsigned, kEpiRelu>{}); break;
+      case kEpiTanh: with_residual(std::integral_constant<unsigned, kEpiTanh>{}); break;
+      default: with_residual(std::integral_constant<unsigned, 0u>{}); break;
+    }
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < C::FN; ++j) {
     const int col = m0 + wn * C::TN + j * 32 + frow;
