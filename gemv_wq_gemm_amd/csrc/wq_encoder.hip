@@ -17,10 +17,10 @@
 //       transposed as [head][dim][frame], frames padded to a multiple of 64; and the key mask as an
 //       additive bias (0 for a valid key, -inf for a masked or padding one). These layouts let the
 //       attention kernel stream 64-key tiles into LDS with direct-to-LDS loads.
-//     - attention: flash-style, f32 online softmax, bf16 matrix cores (v_mfma_f32_16x16x32_bf16)
-//       for both products. A workgroup of 8 waves takes 64 queries of one head, 16 per wave, in two
-//       halves that walk the even and the odd key tiles. Each wave computes S^T = K.Q^T (keys in
-//       rows, queries in columns), so a lane's scores all belong to one query: the row maximum and the sum need
+//     - attention: flash-style, f32 online softmax, bf16 matrix cores (v_mfma_f32_32x32x16_bf16)
+//       for both products. A workgroup of 8 waves takes 64 queries of one
+//       head: four key quarters of two waves, 32 queries per wave. Each wave computes S^T = K.Q^T
+//       (keys in rows, queries in columns), so a lane's scores all belong to one query: the row maximum and the sum need
 //       only in-lane work plus two cross-lane steps, and the probabilities are already the B
 //       operand of O^T = V^T.P^T. Work items are numbered head-major and dealt to the 8 XCDs in
 //       contiguous ranges, so each XCD's L2 holds the K and V of few heads.
@@ -36,6 +36,7 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr float kLnEps = 1e-5f;
 
@@ -63,15 +64,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   v += dpp<0x141>(v);  // row_half_mirror
   v += dpp<0x4E>(v);   // quad_perm xor 2
   return v + dpp<0xB1>(v);  // quad_perm xor 1
-}
-
-// Max / sum over the four lane groups of 16 that share lane & 15.
-__device__ __forceinline__ float wave_max16(float v) {
-  return xor32_xor16(v, [](float a, float b) { return fmaxf(a, b); });
-}
-
-__device__ __forceinline__ float sum_groups16(float v) {
-  return xor32_xor16(v, [](float a, float b) { return a + b; });
 }
 
 __device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
@@ -433,36 +425,40 @@ struct AttnParams {
   int v4;          // hd % 8 == 0 and qkv, o 16-byte aligned: 16-byte loads of q, stores of o
 };
 
-// LDS tile layout (one buffer):
-//   K  [64 keys][HDP] bf16, 16-byte chunks XOR-swizzled by (key & (CPR-1)), CPR = HDP/8 chunks a row;
-//   Vt [HDP dims][64 keys] bf16, chunks swizzled by (dim & 7);
-//   bias [64] f32.
-constexpr float kLazy = 8.f;  // headroom of the running maximum, in log2 units
+// LDS tile layout (one buffer of a 32-key tile):
+//   K  [32 keys][HDP] bf16, 16-byte chunks XOR-swizzled by (key & (CPR-1)), CPR = HDP/8 chunks a row;
+//   Vt [HDP dims][32 keys] bf16 (64-byte rows), chunks swizzled by ((dim >> 2) & 3);
+//   bias [32] f32.
+constexpr int kAttnKeys = 32;  // keys per tile
+constexpr float kLazy = 8.f;   // headroom of the running maximum, in log2 units
 template <int HDP>
 struct AttnLds {
-  static constexpr int kCpr = HDP / 8;                     // 16-byte chunks per K row
-  static constexpr int kKBytes = kKeyTile * HDP * 2;
-  static constexpr int kVBytes = HDP * kKeyTile * 2;
-  static constexpr int kBiasBytes = kKeyTile * 4;
+  static constexpr int kCpr = HDP / 8;  // 16-byte chunks per K row
+  static constexpr int kKBytes = kAttnKeys * HDP * 2;
+  static constexpr int kVBytes = HDP * kAttnKeys * 2;
+  static constexpr int kBiasBytes = kAttnKeys * 4;
   static constexpr int kBufBytes = kKBytes + kVBytes + kBiasBytes;
   static constexpr int kKLoads = kKBytes / 1024;  // 1 KB wave loads per tile
   static constexpr int kVLoads = kVBytes / 1024;
   static_assert(HDP == 32 || HDP == 64 || HDP == 128, "head dims padded to 32, 64 or 128");
 };
 
-// Workgroup: 8 waves, 64 queries. Waves 0-3 and 4-7 form two halves with the same four 16-query
-// groups: the first half walks the even key tiles, the second the odd ones, each half with its own
-// double-buffered LDS tiles, so two waves share every SIMD. At the end the second half hands its
-// running maximum, sum and outputs to the first through LDS, which merges them (rescaled to the
-// common maximum, in a fixed order) and stores.
+// Workgroup: 8 waves, 64 queries of one head. The waves form four key quarters of two; quarter k
+// walks the 32-key tiles t with t % 4 == k through its own double-buffered LDS tiles, and each of
+// its two waves takes 32 queries. Both products run on v_mfma_f32_32x32x16_bf16 (on gfx950 twice
+// the rate per FLOP of the 16x16x32 form): a wave computes S^T = K.Q^T for 32 keys x its 32 queries,
+// so lane l holds 16 scores of query l % 32 (lanes l and l ^ 32 share a query), and those weights,
+// rounded to bf16, are the B operand of O^T = V^T.P^T with the k order of V^T read to match. At the
+// end quarters 1-3 hand their running maxima, sums and outputs to quarter 0 through LDS, which
+// merges them in quarter order (rescaled to the common maximum) and stores.
 template <int HDP>
 __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   using L = AttnLds<HDP>;
-  constexpr int kSteps = HDP / 32;  // k-steps of the score product
-  constexpr int kDTiles = HDP / 16;  // 16-dim output tiles
-  constexpr int kMergeFloats = 4 * kDTiles + 2;  // per lane: outputs, maximum, sum
-  static_assert(4 * 64 * kMergeFloats * 4 <= 4 * L::kBufBytes, "merge area inside the tile buffers");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[4 * L::kBufBytes];  // [half][buffer]
+  constexpr int kSteps = HDP / 16;   // k-steps of the score product
+  constexpr int kDTiles = HDP / 32;  // 32-dim output tiles
+  constexpr int kMergeFloats = 16 * kDTiles + 2;  // per lane: outputs, maximum, sum
+  static_assert(3 * 2 * 64 * kMergeFloats * 4 <= 8 * L::kBufBytes, "merge area inside the tile buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[8 * L::kBufBytes];  // [quarter][buffer]
 
   // Work item: head-major, dealt to XCDs in contiguous ranges (workgroup i runs on XCD i % 8).
   const int item = (blockIdx.x & 7) * p.per_xcd + (blockIdx.x >> 3);
@@ -472,31 +468,31 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int hf = wave >> 2;  // half: even or odd key tiles
-  const int qw = wave & 3;   // query group
-  const int j = lane & 15;   // query column of every fragment this lane holds
-  const int g = lane >> 4;   // k-octet (operands) / row quad (results)
+  const int qt = wave >> 1;   // key quarter
+  const int qw = wave & 1;    // which 32 of the 64 queries
+  const int j = lane & 31;    // query column of every fragment this lane holds
+  const int hh = lane >> 5;   // k-octet (operands) / row quad (results)
   const long long d = static_cast<long long>(p.heads) * p.hd;
 
-  // Q fragments (B operand of S^T): query q0 + 16·qw + j, dims 32s + 8g .. +7, rounded to bf16.
-  // Rows past n read row n-1 and dims past hd read in-row values (zeroed below), so with p.v4 the
-  // loads are unconditional 16-byte loads that the compiler issues back to back.
+  // Q fragments (B operand of S^T): query q0 + 32·qw + j, dims 16s + 8hh .. +7, rounded to bf16.
+  // Rows past n read row n-1 and dims past hd are zeroed, so with p.v4 the loads are unconditional
+  // 16-byte loads that issue back to back.
   bf16x8 qf[kSteps];
   {
-    const int q = q0 + 16 * qw + j;
+    const int q = q0 + 32 * qw + j;
     const bool qin = q < p.n;
     const float* qr = p.qkv + static_cast<long long>(qin ? q : p.n - 1) * 3 * d + static_cast<long long>(h) * p.hd;
     if (p.v4) {
       float4 lo[kSteps], hi[kSteps];
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        const int c = min(32 * s + 8 * g, p.hd - 8);  // hd % 8 == 0 with v4: in the row
+        const int c = min(16 * s + 8 * hh, p.hd - 8);  // hd % 8 == 0 with v4: in the row
         lo[s] = *reinterpret_cast<const float4*>(qr + c);
         hi[s] = *reinterpret_cast<const float4*>(qr + c + 4);
       }
 #pragma unroll
       for (int s = 0; s < kSteps; ++s) {
-        const bool in = qin && 32 * s + 8 * g < p.hd;
+        const bool in = qin && 16 * s + 8 * hh < p.hd;
         const float v[8] = {lo[s].x, lo[s].y, lo[s].z, lo[s].w, hi[s].x, hi[s].y, hi[s].z, hi[s].w};
 #pragma unroll
         for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<__bf16>(in ? v[e] : 0.f);
@@ -506,7 +502,7 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
       for (int s = 0; s < kSteps; ++s) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int c = 32 * s + 8 * g + e;
+          const int c = 16 * s + 8 * hh + e;
           qf[s][e] = static_cast<__bf16>(qin && c < p.hd ? qr[c] : 0.f);
         }
       }
@@ -517,74 +513,77 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   const uint8_t* kg = reinterpret_cast<const uint8_t*>(p.kb + static_cast<long long>(h) * p.npad * HDP);
   const uint8_t* vg = reinterpret_cast<const uint8_t*>(p.vt + static_cast<long long>(h) * HDP * p.npad);
   const uint8_t* bg = reinterpret_cast<const uint8_t*>(p.kbias);
-  const int ntiles = p.npad / kKeyTile;
+  const int ntiles = p.npad / kAttnKeys;
 
-  // Issues this wave's share of tile `kt`'s loads into its half's buffer `buf`: K and V loads dealt
-  // to the half's four waves in turn; its first wave also loads the 256-byte bias (16 lanes).
+  // Issues this wave's share of tile `kt`'s loads into its quarter's buffer `buf`: K and V loads
+  // dealt to the quarter's two waves in turn; its first wave also loads the 128-byte bias.
   auto issue = [&](int kt, int buf) {
-    const uint32_t dst = lds_base + (2 * hf + buf) * L::kBufBytes;
+    const uint32_t dst = lds_base + (2 * qt + buf) * L::kBufBytes;
     constexpr int kRowsPerLoad = 512 / HDP;  // K rows per 1 KB
-    for (int c = qw; c < L::kKLoads; c += 4) {
+    for (int c = qw; c < L::kKLoads; c += 2) {
       const int r = c * kRowsPerLoad + lane / L::kCpr;
       const int cc = lane % L::kCpr;
-      const uint32_t src = static_cast<uint32_t>((kt * kKeyTile + r) * HDP * 2 + ((cc ^ (r & (L::kCpr - 1))) * 16));
+      const uint32_t src =
+          static_cast<uint32_t>((kt * kAttnKeys + r) * HDP * 2 + ((cc ^ (r & (L::kCpr - 1))) * 16));
       load_lds16(kg, src, dst + c * 1024);
     }
-    for (int c = qw; c < L::kVLoads; c += 4) {
-      const int r = c * 8 + lane / 8;  // dim
-      const int cc = lane % 8;
-      const uint32_t src =
-          static_cast<uint32_t>(static_cast<long long>(r) * p.npad * 2 + kt * kKeyTile * 2 + ((cc ^ (r & 7)) * 16));
+    for (int c = qw; c < L::kVLoads; c += 2) {
+      const int r = c * 16 + lane / 4;  // dim
+      const int cc = lane % 4;
+      const uint32_t src = static_cast<uint32_t>(static_cast<long long>(r) * p.npad * 2 + kt * kAttnKeys * 2 +
+                                                 ((cc ^ ((r >> 2) & 3)) * 16));
       load_lds16(vg, src, dst + L::kKBytes + c * 1024);
     }
-    if (qw == 0 && lane < 16)
-      load_lds16(bg, static_cast<uint32_t>(kt * kKeyTile * 4 + lane * 16), dst + L::kKBytes + L::kVBytes);
+    if (qw == 0 && lane < 8)
+      load_lds16(bg, static_cast<uint32_t>(kt * kAttnKeys * 4 + lane * 16), dst + L::kKBytes + L::kVBytes);
   };
 
-  f32x4 acc[kDTiles];
+  f32x16 acc[kDTiles];
 #pragma unroll
-  for (int i = 0; i < kDTiles; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < kDTiles; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.f;
   float m_run = -INFINITY;  // running maximum of this lane's query (log2 domain)
   float l_part = 0.f;       // this lane's share of the running sum of weights
 
-  const int iters = (ntiles + 1) / 2;
-  if (hf < ntiles) issue(hf, 0);
+  const int iters = (ntiles + 3) / 4;
+  if (qt < ntiles) issue(qt, 0);
   wait_vmcnt<0>();
   __syncthreads();
   for (int it = 0; it < iters; ++it) {
-    const int kt = 2 * it + hf;
+    const int kt = 4 * it + qt;
     const int buf = it & 1;
-    if (kt + 2 < ntiles) issue(kt + 2, buf ^ 1);
-    if (kt < ntiles) {  // wave-uniform (the odd half has one tile fewer when ntiles is odd)
-      const uint8_t* kl = lds + (2 * hf + buf) * L::kBufBytes;
+    if (kt + 4 < ntiles) issue(kt + 4, buf ^ 1);
+    if (kt < ntiles) {  // wave-uniform (the last quarters may have one tile fewer)
+      const uint8_t* kl = lds + (2 * qt + buf) * L::kBufBytes;
       const uint8_t* vl = kl + L::kKBytes;
       const float* bl = reinterpret_cast<const float*>(vl + L::kVBytes);
 
-      // S^T for the tile's four 16-key groups: rows keys 16u + 4g + r, column query j.
-      f32x4 s4[4];
+      // S^T: rows keys 8(v/4) + 4hh + v%4, column query j.
+      f32x16 sc;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        s4[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int r = 16 * u + j;  // A row: key
+      for (int v = 0; v < 16; ++v) sc[v] = 0.f;
 #pragma unroll
-        for (int s = 0; s < kSteps; ++s) {
-          const int chunk = (4 * s + g) ^ (r & (L::kCpr - 1));
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + r * HDP * 2 + chunk * 16);
-          s4[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], s4[u], 0, 0, 0);
-        }
+      for (int s = 0; s < kSteps; ++s) {
+        const int chunk = (2 * s + hh) ^ (j & (L::kCpr - 1));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(kl + j * HDP * 2 + chunk * 16);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sc, 0, 0, 0);
       }
-      // Scale, mask, and the tile's maximum per query.
+      // Scale, mask, the tile's maximum per query (this lane and lane ^ 32).
       float mt = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float4 b = *reinterpret_cast<const float4*>(bl + 16 * u + 4 * g);
-        s4[u][0] = s4[u][0] * p.scale_l2 + b.x;
-        s4[u][1] = s4[u][1] * p.scale_l2 + b.y;
-        s4[u][2] = s4[u][2] * p.scale_l2 + b.z;
-        s4[u][3] = s4[u][3] * p.scale_l2 + b.w;
-        mt = fmaxf(mt, fmaxf(fmaxf(s4[u][0], s4[u][1]), fmaxf(s4[u][2], s4[u][3])));
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const float4 b = *reinterpret_cast<const float4*>(bl + 8 * g4 + 4 * hh);
+        sc[4 * g4 + 0] = sc[4 * g4 + 0] * p.scale_l2 + b.x;
+        sc[4 * g4 + 1] = sc[4 * g4 + 1] * p.scale_l2 + b.y;
+        sc[4 * g4 + 2] = sc[4 * g4 + 2] * p.scale_l2 + b.z;
+        sc[4 * g4 + 3] = sc[4 * g4 + 3] * p.scale_l2 + b.w;
+        mt = fmaxf(mt, fmaxf(fmaxf(sc[4 * g4], sc[4 * g4 + 1]), fmaxf(sc[4 * g4 + 2], sc[4 * g4 + 3])));
       }
-      mt = wave_max16(mt);
+      {
+        auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mt), __float_as_uint(mt), false, false);
+        mt = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
       // The running maximum moves only when the tile's exceeds it by more than kLazy (log2 units):
       // weights then stay below 2^kLazy, and numerator and denominator share whichever maximum is
       // used, so the result is the same up to rounding while most tiles skip the rescale.
@@ -596,32 +595,29 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
       bf16x8 pb[2];
       float ls = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const __bf16 w = static_cast<__bf16>(__builtin_amdgcn_exp2f(s4[u][r] - m_use));
-          pb[u >> 1][(u & 1) * 4 + r] = w;
-          ls += static_cast<float>(w);
-        }
+      for (int v = 0; v < 16; ++v) {
+        const __bf16 w = static_cast<__bf16>(__builtin_amdgcn_exp2f(sc[v] - m_use));
+        pb[v >> 3][v & 7] = w;
+        ls += static_cast<float>(w);
       }
       l_part = l_part * alpha + ls;
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int i = 0; i < kDTiles; ++i) acc[i] *= alpha;
       }
-      // O^T += V^T . P^T: k slot 8g + e of product mf is key 32mf + 4g + e (e < 4) or
-      // 32mf + 16 + 4g + (e - 4): the keys this lane's weights belong to.
+      // O^T += V^T . P^T: k slot 8hh + e of product mf is key 16mf + 4hh + e (e < 4) or
+      // 16mf + 8 + 4hh + (e - 4), the keys this lane's weights belong to.
 #pragma unroll
       for (int dt = 0; dt < kDTiles; ++dt) {
-        const int r = 16 * dt + j;  // A row: dim
-        const uint8_t* vrow = vl + r * (kKeyTile * 2);
+        const int r = 32 * dt + j;  // A row: dim
+        const uint8_t* vrow = vl + r * (kAttnKeys * 2);
+        const int sw = (r >> 2) & 3;
 #pragma unroll
         for (int mf = 0; mf < 2; ++mf) {
-          const int k0 = 32 * mf + 4 * g, k1 = k0 + 16;  // first keys of the two 8-byte halves
-          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((k0 >> 3) ^ (r & 7)) * 16) + (k0 & 7) * 2);
-          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((k1 >> 3) ^ (r & 7)) * 16) + (k1 & 7) * 2);
+          const uint2 lo = *reinterpret_cast<const uint2*>(vrow + (((2 * mf) ^ sw) * 16) + hh * 8);
+          const uint2 hi = *reinterpret_cast<const uint2*>(vrow + (((2 * mf + 1) ^ sw) * 16) + hh * 8);
           const bf16x8 a = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[mf], acc[dt], 0, 0, 0);
+          acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[mf], acc[dt], 0, 0, 0);
         }
       }
     }
@@ -629,48 +625,62 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
     __syncthreads();  // the next tiles are in; every wave is done with this iteration's buffers
   }
 
-  // Merge: the odd half's state goes through LDS (the tile buffers are free after the last
-  // barrier), laid out [query group][field][lane].
-  float* mg = reinterpret_cast<float*>(lds) + qw * (kMergeFloats * 64);
-  if (hf == 1) {
+  // Merge: quarters 1-3 write their state to LDS (the tile buffers are free after the last
+  // barrier), laid out [quarter - 1][query half][field][lane]; quarter 0 folds them in in order.
+  auto slot = [&](int quarter) {
+    return reinterpret_cast<float*>(lds) + ((quarter - 1) * 2 + qw) * (kMergeFloats * 64);
+  };
+  if (qt > 0) {
+    float* f = slot(qt);
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mg[(4 * dt + r) * 64 + lane] = acc[dt][r];
-    mg[(4 * kDTiles) * 64 + lane] = m_run;
-    mg[(4 * kDTiles + 1) * 64 + lane] = l_part;
+      for (int v = 0; v < 16; ++v) f[(16 * dt + v) * 64 + lane] = acc[dt][v];
+    f[(16 * kDTiles) * 64 + lane] = m_run;
+    f[(16 * kDTiles + 1) * 64 + lane] = l_part;
   }
   __syncthreads();
-  if (hf == 1) return;
-  {
-    const float m1 = mg[(4 * kDTiles) * 64 + lane];
+  if (qt > 0) return;
+#pragma unroll 1
+  for (int other = 1; other < 4; ++other) {
+    const float* f = slot(other);
+    const float m1 = f[(16 * kDTiles) * 64 + lane];
     const float m = fmaxf(m_run, m1);
     const float m_use = m == -INFINITY ? 0.f : m;
     const float a0 = __builtin_amdgcn_exp2f(m_run - m_use), a1 = __builtin_amdgcn_exp2f(m1 - m_use);
-    l_part = l_part * a0 + mg[(4 * kDTiles + 1) * 64 + lane] * a1;
+    m_run = m;
+    l_part = l_part * a0 + f[(16 * kDTiles + 1) * 64 + lane] * a1;
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) acc[dt][r] = acc[dt][r] * a0 + mg[(4 * dt + r) * 64 + lane] * a1;
+      for (int v = 0; v < 16; ++v) acc[dt][v] = acc[dt][v] * a0 + f[(16 * dt + v) * 64 + lane] * a1;
   }
 
-  // Normalise and store: lane holds dims 16dt + 4g .. +3 of query q0 + 16·qw + j.
-  const float l = sum_groups16(l_part);
+  // Normalise and store: lane holds dims 32dt + 8(v/4) + 4hh + v%4 of query q0 + 32·qw + j.
+  float l;
+  {
+    auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+    l = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
   const float inv = 1.f / l;  // no valid key: 1/0, and 0 · inf = NaN, as the page's arithmetic gives
-  const int q = q0 + 16 * qw + j;
+  const int q = q0 + 32 * qw + j;
   if (q < p.n) {
     float* orow = p.o + static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) {
-      const int c = 16 * dt + 4 * g;
-      if (p.v4) {
-        if (c < p.hd)
-          *reinterpret_cast<float4*>(orow + c) =
-              make_float4(acc[dt][0] * inv, acc[dt][1] * inv, acc[dt][2] * inv, acc[dt][3] * inv);
-      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (c + r < p.hd) orow[c + r] = acc[dt][r] * inv;
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int c = 32 * dt + 8 * g4 + 4 * hh;
+        const f32x16& v = acc[dt];
+        if (p.v4) {
+          if (c < p.hd)
+            *reinterpret_cast<float4*>(orow + c) =
+                make_float4(v[4 * g4] * inv, v[4 * g4 + 1] * inv, v[4 * g4 + 2] * inv, v[4 * g4 + 3] * inv);
+        } else {
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (c + r < p.hd) orow[c + r] = v[4 * g4 + r] * inv;
+        }
       }
     }
   }
