@@ -284,9 +284,12 @@ def attn_sigma(qkv, var_in, valid, heads: int, hd: int, scale: float):
         term_v = p2 @ sv
         term_k = scale * scale * dev2(p2 * ((q * q) @ sk.T))
         term_p = (R_BF16 ** 2 / 3.0) * dev2(p2)
-        # shared dq: M[t, c, c'] = sum_j p_tj v_jc k_jc' - o_tc (p_t . k)_c'
-        m = np.einsum("tj,jc,je->tce", p, v, k) - o[:, :, None] * (p @ k)[:, None, :]
+        # shared dq: M[t, c, c'] = sum_j p_tj v_jc k_jc' - o_tc (p_t . k)_c', as one matrix product
+        # over the keys' outer products v_j k_j^T (row j of `outer`)
+        outer = (v[:, :, None] * k[:, None, :]).reshape(v.shape[0], hd * hd)
+        m = (p @ outer).reshape(-1, hd, hd) - o[:, :, None] * (p @ k)[:, None, :]
         term_q = scale * scale * np.einsum("tce,te->tc", m * m, sq)
+        del outer, m
         var[:, h * hd:(h + 1) * hd] += np.maximum(term_v + term_k + term_q + term_p, 0.0)
     return val, var
 

@@ -266,3 +266,19 @@ def test_encoder_forward_small():
         h, var = _layer_reference(h, L, valid, heads, rot, False, var)
     _, var = eb.ln_sigma(h, model["final_norm"], var)
     assert_within(got, want, eb.sigma_tol(want, var), "encoder forward")
+
+
+def test_encoder_layer_workload_size():
+    """One block at the workload's size (1500 frames, d = 1024, 8 heads of 128, MLP 4096, the last
+    100 frames masked), on the bf16 matrix-core path the forward uses: every output against the
+    oracle's block within the probabilistic bound."""
+    n, d, heads, inter, rot = synth.ENCODER_N, synth.ENCODER_D, synth.ENCODER_HEADS, synth.ENCODER_FF, synth.ENCODER_ROT
+    L = synth.encoder_block_weights(0)
+    h = synth.normal_f32(synth.rng(409), (n, d), 1.0)
+    valid = synth.key_mask(n, synth.ENCODER_VALID)
+    t = dev(h)
+    wq.encoder_layer(t, _layer_dev(L), wq.W_BF16, dev(valid), wq.rope_table(n, rot).cuda(), n=n, d=d, heads=heads,
+                     rot=rot, inter=inter, path=wq.PATH_MFMA)
+    got = t.cpu().numpy()
+    want, var = eb.layer_sigma(h, L, valid, heads, rot, True)
+    assert_within(got, want, eb.sigma_tol(want, var), "encoder layer 1500x1024")
