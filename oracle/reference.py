@@ -21,7 +21,11 @@ What it computes, written out from the pages it follows:
   ``d`` and int8 ``q`` (wavo ``Gpu::upload_linear`` and the test helper
   ``weights``); Q4_0 is ``d * (q - 8)`` with 4-bit ``q`` (format named by
   hanzo-ml ``wgpu_backend.rs`` ``matvec_q4_0_gpu``; nibble order: low nibbles
-  are elements 0-15, high nibbles 16-31).
+  are elements 0-15, high nibbles 16-31). Q4_K (hanzo-ml ``matvec_q4k_gpu``:
+  144-byte super-blocks of 256 weights, k a multiple of 256) is
+  ``d * sc_j * q - dmin * m_j`` per 32-element sub-block ``j``; the pages name
+  the type but do not print its bytes, so its layout is GGML's published
+  k-quant super-block (``decode_q4_k``).
 * The MoE matvec of hanzo-ml ``moe_matvec_gpu``: for routed slot ``s`` and
   output row ``r``, ``y[s, r] = sum_k W[ids[s], r, k] * x[s, k]`` over one
   weight bank ``[E, m, k]``; with gate weights the slots of a token are summed,
@@ -37,11 +41,14 @@ from __future__ import annotations
 import numpy as np
 from scipy.special import erf
 
-W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16 = 0, 1, 2, 3, 4
+W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16, W_Q4_K = 0, 1, 2, 3, 4, 5
 FLAG_BIAS, FLAG_GELU, FLAG_RESIDUAL = 1, 2, 4
 FLAG_SILU, FLAG_RELU, FLAG_TANH = 8, 16, 32
 QBLOCK = 32
 QBYTES = {W_Q8_0: 34, W_Q4_0: 18}
+# Q4_K super-block: 256 weights in 144 bytes (hanzo-ml ``matvec_q4k_gpu`` states both sizes).
+QK_K = 256
+Q4K_BYTES = 144
 
 
 # ---------------------------------------------------------------------------
@@ -110,6 +117,8 @@ PLAIN_BYTES = {W_BF16: 2, W_F32: 4, W_F16: 2}
 def weight_nbytes(wtype: int, m: int, k: int) -> int:
     if wtype in PLAIN_BYTES:
         return PLAIN_BYTES[wtype] * m * k
+    if wtype == W_Q4_K:
+        return Q4K_BYTES * m * (k // QK_K)
     return QBYTES[wtype] * m * (k // QBLOCK)
 
 
@@ -144,12 +153,60 @@ def decode_q4_0(raw: np.ndarray, m: int, k: int) -> np.ndarray:
     return (d[:, :, None] * (q - 8.0)).reshape(m, k)
 
 
+def q4_k_scale_min(scales) -> tuple:
+    """``(sc, mn)``, each ``int64[..., 8]``: the 6-bit scale and 6-bit min of the eight sub-blocks
+    of a Q4_K super-block, from its 12 packed bytes ``scales[..., 0:12]``.
+
+    GGML's k-quant packing: for sub-blocks j = 0..3 the scale is the low 6 bits of byte j and the
+    min the low 6 bits of byte j + 4. For j = 4..7 byte j + 4 carries the low 4 bits of the scale
+    (its low nibble) and of the min (its high nibble), and the top 2 bits of the scale and of the
+    min sit in the top 2 bits of bytes j - 4 and j.
+    """
+    b = np.asarray(scales).astype(np.int64)
+    sc = np.empty(b.shape[:-1] + (8,), np.int64)
+    mn = np.empty_like(sc)
+    for j in range(4):
+        sc[..., j] = b[..., j] & 63
+        mn[..., j] = b[..., j + 4] & 63
+    for j in range(4, 8):
+        sc[..., j] = (b[..., j + 4] & 15) | ((b[..., j - 4] >> 6) << 4)
+        mn[..., j] = (b[..., j + 4] >> 4) | ((b[..., j] >> 6) << 4)
+    return sc, mn
+
+
+def decode_q4_k(raw: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Q4_K rows -> ``f64[m][k]``: ``k/256`` super-blocks of 144 bytes per row.
+
+    Super-block bytes (GGML's published k-quant layout; the pages give only the sizes):
+    0-1 little-endian f16 ``d``, 2-3 little-endian f16 ``dmin``, 4-15 the packed 6-bit scales
+    and mins of the eight 32-element sub-blocks (``q4_k_scale_min``), 16-143 the 4-bit quants.
+    Sub-blocks 2c and 2c+1 (c = 0..3) share quant bytes 32c .. 32c+31: element l of sub-block
+    2c is the low nibble of byte 32c + l, element l of sub-block 2c+1 its high nibble.
+    Weight = ``d * sc_j * q - dmin * m_j`` for element of sub-block j, with unsigned ``q``.
+    """
+    if k % QK_K:
+        raise ValueError(f"k = {k} is not a multiple of {QK_K}")
+    a = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)
+    need = weight_nbytes(W_Q4_K, m, k)
+    if a.size < need:
+        raise ValueError(f"weight has {a.size} bytes, needs {need}")
+    sb = a[:need].reshape(m, k // QK_K, Q4K_BYTES).astype(np.int64)
+    d = f16_bits_to_f64(sb[:, :, 0] | (sb[:, :, 1] << 8))
+    dmin = f16_bits_to_f64(sb[:, :, 2] | (sb[:, :, 3] << 8))
+    sc, mn = q4_k_scale_min(sb[:, :, 4:16])
+    qs = sb[:, :, 16:].reshape(m, k // QK_K, 4, 32)          # [row][super][c][byte]
+    q = np.stack([qs & 0xF, qs >> 4], axis=3)                # [row][super][c][nibble][l]
+    q = q.reshape(m, k // QK_K, 8, 32).astype(np.float64)    # sub-block j = 2c + nibble
+    w = d[:, :, None, None] * sc[:, :, :, None] * q - dmin[:, :, None, None] * mn[:, :, :, None]
+    return w.reshape(m, k)
+
+
 def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray:
     """Exact f64 values of an ``m x k`` weight (optionally only the listed rows).
 
     bf16 and f16 rows are 16-bit patterns, f32 rows 32-bit patterns, all
     little-endian (wavo ``Gpu::upload_linear`` copies F32 / F16 tensor bytes as
-    stored); Q8_0 / Q4_0 rows are 34- / 18-byte blocks.
+    stored); Q8_0 / Q4_0 rows are 34- / 18-byte blocks, Q4_K rows 144-byte super-blocks.
     """
     if wtype in PLAIN_BYTES:
         dt = np.uint32 if wtype == W_F32 else np.uint16
@@ -159,15 +216,14 @@ def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray
             a = a[np.asarray(rows)]
         fn = {W_BF16: bf16_bits_to_f64, W_F32: f32_bits_to_f64, W_F16: f16_bits_to_f64}[wtype]
         return fn(a)
-    per_row = QBYTES.get(wtype)
-    if per_row is None:
+    if wtype not in QBYTES and wtype != W_Q4_K:
         raise ValueError(f"unknown weight type {wtype}")
-    a = np.ascontiguousarray(raw).view(np.uint8).reshape(m, -1)
+    a = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)[: weight_nbytes(wtype, m, k)].reshape(m, -1)
     mm = m
     if rows is not None:
         a = a[np.asarray(rows)]
         mm = a.shape[0]
-    dec = decode_q8_0 if wtype == W_Q8_0 else decode_q4_0
+    dec = {W_Q8_0: decode_q8_0, W_Q4_0: decode_q4_0, W_Q4_K: decode_q4_k}[wtype]
     return dec(a, mm, k)
 
 

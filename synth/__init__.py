@@ -21,6 +21,11 @@ follows, and restated here only to lay the bytes out):
   f16 scale followed by 16 bytes whose low nibbles are elements 0-15 and high
   nibbles elements 16-31 (hanzo-ml ``wgpu_backend.rs`` names the format in
   ``matvec_q4_0_gpu``; the nibble order is the plain GGML reading).
+* Q4_K weights: ``m`` rows of ``k/256`` super-blocks of 144 bytes (hanzo-ml
+  ``matvec_q4k_gpu`` names the type and both sizes); the bytes hold two f16
+  factors, packed 6-bit sub-block fields and 4-bit quants in GGML's published
+  k-quant layout. Only the two f16 factors are drawn as numbers; the rest are
+  uniform random bytes.
 
 Every tensor gets its own generator ``numpy.random.default_rng([seed, cfg,
 tensor])`` so that its values do not depend on the shapes of other tensors.
@@ -29,9 +34,11 @@ from __future__ import annotations
 
 import numpy as np
 
-W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16 = 0, 1, 2, 3, 4
+W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16, W_Q4_K = 0, 1, 2, 3, 4, 5
 BLOCK = 32
 BLOCK_BYTES = {W_Q8_0: 34, W_Q4_0: 18}
+SUPER = 256        # Q4_K super-block: 256 weights
+SUPER_BYTES = 144  # in 144 bytes
 
 
 def rng(*key: int) -> np.random.Generator:
@@ -94,6 +101,29 @@ def q4_0_weight(g: np.random.Generator, m: int, k: int, dsigma: float = 0.01) ->
     return out.reshape(m, nb * 18)
 
 
+def q4_k_weight(g: np.random.Generator, m: int, k: int, dsigma: float = 0.01) -> np.ndarray:
+    """``uint8[m][k/256*144]``: Q4_K super-blocks with random fields.
+
+    Bytes 0-1 and 2-3 of each 144-byte super-block are the f16 bits of |N(0, (dsigma/16)^2)| and
+    |N(0, (dsigma/2)^2)| (the super-block's scale and min factors); the other 140 bytes (the packed
+    6-bit sub-block scales and mins, and the 4-bit quants) are uniform random bytes, so every
+    6-bit field and every nibble is uniform. With these factors the weights of a sub-block
+    straddle zero, as trained weights do.
+    """
+    assert k % SUPER == 0
+    ns = k // SUPER
+    d = _scales_f16_bits(g, (m, ns), dsigma / 16)
+    dmin = _scales_f16_bits(g, (m, ns), dsigma / 2)
+    rest = g.integers(0, 256, size=(m, ns, SUPER_BYTES - 4), dtype=np.uint8)
+    out = np.empty((m, ns, SUPER_BYTES), dtype=np.uint8)
+    out[:, :, 0] = (d & 0xFF).astype(np.uint8)
+    out[:, :, 1] = (d >> 8).astype(np.uint8)
+    out[:, :, 2] = (dmin & 0xFF).astype(np.uint8)
+    out[:, :, 3] = (dmin >> 8).astype(np.uint8)
+    out[:, :, 4:] = rest
+    return out.reshape(m, ns * SUPER_BYTES)
+
+
 def weight(g: np.random.Generator, wtype: int, m: int, k: int, sigma: float = 0.02,
            dsigma: float = 0.01) -> np.ndarray:
     """A weight of the given storage type, as the raw array the layer reads."""
@@ -107,6 +137,8 @@ def weight(g: np.random.Generator, wtype: int, m: int, k: int, sigma: float = 0.
         return normal_f32(g, (m, k), sigma)
     if wtype == W_F16:
         return f16_weight(g, m, k, sigma)
+    if wtype == W_Q4_K:
+        return q4_k_weight(g, m, k, dsigma)
     raise ValueError(f"unknown weight type {wtype}")
 
 
@@ -121,6 +153,8 @@ def weight_nbytes(wtype: int, m: int, k: int) -> int:
         return 2 * m * k
     if wtype == W_F32:
         return 4 * m * k
+    if wtype == W_Q4_K:
+        return SUPER_BYTES * m * (k // SUPER)
     return BLOCK_BYTES[wtype] * m * (k // BLOCK)
 
 
