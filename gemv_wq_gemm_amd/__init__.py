@@ -15,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16 = 0, 1, 2, 3, 4
+W_BF16, W_Q8_0, W_Q4_0, W_F32, W_F16, W_Q4_K = 0, 1, 2, 3, 4, 5
 BIAS, GELU, RESIDUAL, SILU, RELU, TANH = 1, 2, 4, 8, 16, 32
 ACTIVATIONS = {None: 0, "gelu": GELU, "silu": SILU, "relu": RELU, "tanh": TANH}
 PATH_AUTO, PATH_MATVEC, PATH_MFMA, PATH_MFMA_F32 = 0, 1, 2, 3

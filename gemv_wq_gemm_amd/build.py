@@ -19,7 +19,8 @@ LIB = os.path.join(PKG, "libwq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["wq_api.cpp", "wq_matvec.hip", "wq_matvec_sliced.hip", "wq_matvec_mfma.hip", "wq_gemm.hip", "wq_encoder.hip"]
+SOURCES = ["wq_api.cpp", "wq_matvec.hip", "wq_matvec_sliced.hip", "wq_matvec_mfma.hip", "wq_matvec_q4k.hip", "wq_gemm.hip",
+           "wq_encoder.hip"]
 
 COMMON = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

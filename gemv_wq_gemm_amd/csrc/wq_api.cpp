@@ -55,14 +55,18 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 }
 
 int check_wtype(int wtype) {
-  if (wtype != WQ_W_BF16 && wtype != WQ_W_Q8_0 && wtype != WQ_W_Q4_0 && wtype != WQ_W_F32 && wtype != WQ_W_F16)
-    return fail(WQ_ERR_WTYPE, "unknown weight type %d (0 = bf16, 1 = Q8_0, 2 = Q4_0, 3 = f32, 4 = f16)", wtype);
+  if (wtype != WQ_W_BF16 && wtype != WQ_W_Q8_0 && wtype != WQ_W_Q4_0 && wtype != WQ_W_F32 && wtype != WQ_W_F16 &&
+      wtype != WQ_W_Q4_K)
+    return fail(WQ_ERR_WTYPE, "unknown weight type %d (0 = bf16, 1 = Q8_0, 2 = Q4_0, 3 = f32, 4 = f16, 5 = Q4_K)",
+                wtype);
   return WQ_OK;
 }
 
-int check_k(int64_t k) {
+int check_k(int64_t k, int wtype) {
   if (k <= 0 || k % 32 != 0) return fail(WQ_ERR_SHAPE, "k must be a positive multiple of 32, got %lld", (long long)k);
   if (k > kIntMax / 4) return fail(WQ_ERR_SHAPE, "k = %lld is too large", (long long)k);
+  if (wtype == WQ_W_Q4_K && k % 256 != 0)
+    return fail(WQ_ERR_SHAPE, "Q4_K weights need k % 256 == 0 (256-weight super-blocks), got %lld", (long long)k);
   return WQ_OK;
 }
 
@@ -143,11 +147,14 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
   if (path != WQ_PATH_AUTO && path != WQ_PATH_MATVEC && path != WQ_PATH_MFMA && path != WQ_PATH_MFMA_F32)
     return fail(WQ_ERR_SHAPE, "unknown path %d", path);
   if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size n = %lld, m = %lld", (long long)n, (long long)m);
-  if (int r = check_k(k)) return r;
+  if (int r = check_k(k, wtype)) return r;
   if (n > kMaxRows || m > kMaxRows) return fail(WQ_ERR_SHAPE, "n or m exceeds 2^31 - 513");
   if (dual < 0 || dual > m) return fail(WQ_ERR_SHAPE, "dual must be in [0, m], got %lld", (long long)dual);
   if (m + dual > kMaxRows) return fail(WQ_ERR_SHAPE, "m + dual exceeds 2^31 - 513");
   if (n > 0 && (m + dual) > kMaxOutputs / n) return fail(WQ_ERR_SHAPE, "n * (m + dual) exceeds 2^40");
+  if (wtype == WQ_W_Q4_K && (path == WQ_PATH_MFMA || path == WQ_PATH_MFMA_F32 || n > WQ_MATVEC_MAX_N))
+    return fail(WQ_ERR_WTYPE, "Q4_K weights take the matvec path only (n <= %d), got n = %lld, path %d", WQ_MATVEC_MAX_N,
+                (long long)n, path);
   if (path == WQ_PATH_AUTO) path = n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
   if (path == WQ_PATH_MATVEC && n > WQ_MATVEC_MAX_N)
     return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
@@ -212,6 +219,7 @@ extern "C" {
 int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k) {
   if (m < 0 || k < 0 || k % 32 != 0) return -1;
   switch (wtype) {
+    case WQ_W_Q4_K: return k % 256 != 0 ? -1 : 144 * m * (k / 256);
     case WQ_W_BF16: return 2 * m * k;
     case WQ_W_Q8_0: return 34 * m * (k / 32);
     case WQ_W_Q4_0: return 18 * m * (k / 32);
@@ -225,7 +233,9 @@ int wq_gemm_path(int64_t n, int64_t m, int64_t k, int wtype) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   if (n < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size");
-  if (int r = check_k(k)) return r;
+  if (int r = check_k(k, wtype)) return r;
+  if (wtype == WQ_W_Q4_K && n > WQ_MATVEC_MAX_N)
+    return fail(WQ_ERR_WTYPE, "Q4_K weights take the matvec path only (n <= %d)", WQ_MATVEC_MAX_N);
   return n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA;
 }
 
@@ -263,7 +273,7 @@ int moe_checked(const float* x, const void* w_experts, int wtype, const int32_t*
   if (n_tok < 0 || m < 0) return fail(WQ_ERR_SHAPE, "negative size");
   if (n_experts < 1 || n_experts > 65534) return fail(WQ_ERR_SHAPE, "n_experts must be in [1, 65534]");
   if (top_k < 1 || top_k > n_experts) return fail(WQ_ERR_SHAPE, "top_k must be in [1, n_experts]");
-  if (int r = check_k(k)) return r;
+  if (int r = check_k(k, wtype)) return r;
   if (m > kMaxRows) return fail(WQ_ERR_SHAPE, "m exceeds 2^31 - 513");
   if (n_tok * top_k > 4096) return fail(WQ_ERR_SHAPE, "n_tok * top_k must be <= 4096");
   if (n_tok * top_k * m > kMaxOutputs) return fail(WQ_ERR_SHAPE, "n_tok * top_k * m exceeds 2^40");
@@ -345,7 +355,7 @@ int wq_dequantize(const void* w, int wtype, float* out, int64_t m, int64_t k, vo
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   if (m < 0) return fail(WQ_ERR_SHAPE, "negative m");
-  if (int r = check_k(k)) return r;
+  if (int r = check_k(k, wtype)) return r;
   if (m > kMaxRows || m * (k / 32) > kIntMax * 128LL) return fail(WQ_ERR_SHAPE, "m * k too large");
   if (m == 0) return WQ_OK;
   if (!w || !out) return fail(WQ_ERR_NULL, "w and out must not be NULL");

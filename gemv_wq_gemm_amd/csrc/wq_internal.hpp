@@ -7,12 +7,16 @@
 
 namespace wq {
 
-enum WType : int { kBF16 = 0, kQ8_0 = 1, kQ4_0 = 2, kF32 = 3, kF16 = 4 };
+enum WType : int { kBF16 = 0, kQ8_0 = 1, kQ4_0 = 2, kF32 = 3, kF16 = 4, kQ4_K = 5 };
 
 // Bytes of one 32-element block in each storage type (bf16, f16: 32 x 2 bytes; f32: 32 x 4).
+// Q4_K is stored in 256-element super-blocks (kQ4KBytes each): 18 bytes per 32 elements on
+// average, but its 32-element sub-blocks are not self-contained, so only the Q4_K kernels read it.
 __host__ __device__ constexpr int block_bytes(int wt) {
   return wt == kBF16 || wt == kF16 ? 64 : wt == kF32 ? 128 : wt == kQ8_0 ? 34 : 18;
 }
+constexpr int kQ4KElems = 256;  // weights per Q4_K super-block
+constexpr int kQ4KBytes = 144;  // bytes per Q4_K super-block
 
 // Types stored value by value (no per-block scale): bf16, f16, f32.
 __host__ __device__ constexpr bool plain_type(int wt) { return wt == kBF16 || wt == kF16 || wt == kF32; }
@@ -58,6 +62,11 @@ hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tokens
 // in 2048..4096), which launch_matvec prefers when it applies.
 bool matvec_mfma_supports(int wtype, int k);
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream);
+
+// Q4_K weights (k a multiple of 256): the sliced kernel where it applies (no dual outputs), else
+// the Q4_K general kernel (wq_matvec_q4k.hip). launch_matvec sends Q4_K here.
+hipError_t launch_matvec_q4k(const MatvecParams& p, int max_tokens_per_expert, hipStream_t stream);
+hipError_t launch_dequantize_q4k(const uint8_t* w, float* out, int m, int k, hipStream_t stream);
 
 // y[t][j] = sum_s gate[t*top_k + s] * slots[(t*top_k + s)][j], summed in s order.
 hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, int n_tok,

@@ -397,6 +397,7 @@ hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStrea
   // Dual outputs (wavo `Linear.dual`) are stored by this file's general kernel only: the sliced
   // and matrix-core kernels keep one output per row, since even a skipped second store in their
   // flush measured 12% slower on Q4_0 14336 x 4096 at n = 1.
+  if (wtype == kQ4_K) return launch_matvec_q4k(p, max_tok, stream);
   const bool dual = p.dual > 0;
   if (!dual && matvec_mfma_supports(wtype, p.k) && ((p.ids != nullptr && max_tok > 1) || max_tok > 8))
     return launch_matvec_mfma(wtype, p, stream);
@@ -423,6 +424,7 @@ hipError_t launch_moe_combine(const float* slots, const float* gates, float* y, 
 }
 
 hipError_t launch_dequantize(int wtype, const uint8_t* w, float* out, int m, int k, hipStream_t stream) {
+  if (wtype == kQ4_K) return launch_dequantize_q4k(w, out, m, k, stream);
   const long long blocks_total = static_cast<long long>(m) * (k / 32);
   const unsigned grid = static_cast<unsigned>((blocks_total + 255) / 256);
   const long long rowbytes = static_cast<long long>(k / 32) * block_bytes(wtype);

@@ -38,10 +38,17 @@
 //    and stores. An epilogue that reads memory (bias, residual) would make
 //    the compiler wait for every ring load in flight, so such launches give each
 //    workgroup at most one flush of rows.
+//  * Q4_K (k a multiple of 256): the unit is the 144-byte super-block of 256 weights, so 256/E
+//    lanes share one. A lane's E elements E q .. E q + E-1 lie in one 32-element sub-block j, whose
+//    quants are one nibble (low for even j, high for odd j) of E consecutive bytes. The lane sums
+//    x q over them (q unsigned, exact in f32) and finishes with d sc_j * that - dmin m_j * sum(x),
+//    the sum of its activations being formed once per token group.
 //  * MoE: the grid is dealt over the experts the ids touch (wq_moe_sched.hpp; for banks of more
 //    than 256 experts blockIdx.y is the expert), and a ballot over the ids finds the expert's slots.
 //  * Rounding: an E-term chain, one scale, a 6-level tree and at most 16 slice
-//    additions per output -- far inside 1e-5 * sum |x w|.
+//    additions per output -- far inside 1e-5 * sum |x w|. For Q4_K the lane's closing
+//    d sc_j s - dmin m_j sum(x) rounds relative to d sc_j sum|x q| + dmin m_j sum|x|, which exceeds
+//    sum |x w| by the cancellation inside a sub-block whose weights straddle zero.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -58,10 +65,11 @@ namespace {
 template <int WT, int SLICE>
 struct Slice {
   static_assert(SLICE == 1024 || SLICE == 512, "k elements per wave: 1024 or 512");
-  static constexpr int BB = block_bytes(WT);
-  static constexpr int E = SLICE / 64;                  // elements per lane and row
-  static constexpr int kLanesPerBlock = 32 / E;         // 2 or 4
-  static constexpr int kSegBytes = SLICE / 32 * BB;     // one wave's slice of a row
+  static constexpr int kBlockElems = WT == kQ4_K ? kQ4KElems : 32;  // Q4_K: the super-block
+  static constexpr int BB = WT == kQ4_K ? kQ4KBytes : block_bytes(WT);
+  static constexpr int E = SLICE / 64;                         // elements per lane and row
+  static constexpr int kLanesPerBlock = kBlockElems / E;       // 2 or 4 (Q4_K: 16 or 32)
+  static constexpr int kSegBytes = SLICE / kBlockElems * BB;   // one wave's slice of a row
 };
 
 template <int CTRL>
@@ -201,13 +209,69 @@ __device__ __forceinline__ float decode_lane(const uint8_t* lds, int boff, int q
   }
 }
 
+// Where a lane's Q4_K quants and sub-block fields sit in its super-block (lane-constant).
+struct Q4KLane {
+  int qs_off;  // byte offset of its E quant bytes from the super-block start
+  int nib;     // 0: low nibbles (even sub-block), 4: high nibbles (odd sub-block)
+  int lo_off;  // bit offset of the field's low 6 bits (j < 4) or top 2 bits (j >= 4) in bytes 4-7 / 8-11
+  int lo_w;    // 6 or 2
+  int hi_shl;  // 0 or 4: where those bits go
+  int nb_off;  // bit offset of the field's low nibble in bytes 12-15 (j >= 4)
+  int nb_w;    // 0 (j < 4) or 4
+};
+
+// Super-block layout (GGML k-quant, the type hanzo-ml src/wgpu_backend.rs `matvec_q4k_gpu` takes):
+// bytes 0-1 f16 d, 2-3 f16 dmin, 4-15 the 6-bit scales sc_j and mins m_j of the eight sub-blocks
+// (j < 4: low 6 bits of bytes 4+j and 8+j; j >= 4: low / high nibble of byte 8+j, top 2 bits
+// from the top of bytes j and 4+j), 16-143 the quants (sub-blocks 2c, 2c+1 in the low / high
+// nibbles of bytes 16+32c ..).
+template <int E>
+__device__ __forceinline__ Q4KLane q4k_lane(int q) {
+  const int j = E * q / 32;      // the lane's sub-block
+  const int o = E * q % 32;      // its first element within the sub-block
+  const int jj = j & 3, hi = j >> 2;
+  return Q4KLane{16 + 32 * (j >> 1) + o, 4 * (j & 1), 8 * jj + 6 * hi, hi ? 2 : 6, 4 * hi, 8 * jj, 4 * hi};
+}
+
+// The lane's E quants of the super-block at byte `boff` of `lds`, as floats in wv; returns
+// (d sc_j, dmin m_j), both exact in f32.
+template <int E>
+__device__ __forceinline__ float2 decode_q4k(const uint8_t* lds, int boff, const Q4KLane& c, float (&wv)[E]) {
+  const uint4 h = *reinterpret_cast<const uint4*>(lds + boff);  // d | dmin, scale bytes 0-3, 4-7, 8-11
+  const uint32_t sc = (__builtin_amdgcn_ubfe(h.y, c.lo_off, c.lo_w) << c.hi_shl) |
+                      __builtin_amdgcn_ubfe(h.w, c.nb_off, c.nb_w);
+  const uint32_t mn = (__builtin_amdgcn_ubfe(h.z, c.lo_off, c.lo_w) << c.hi_shl) |
+                      __builtin_amdgcn_ubfe(h.w, c.nb_off + 4, c.nb_w);
+  uint32_t dw[E / 4];
+  if constexpr (E == 16) {
+    const uint4 v = *reinterpret_cast<const uint4*>(lds + boff + c.qs_off);
+    dw[0] = v.x;
+    dw[1] = v.y;
+    dw[2] = v.z;
+    dw[3] = v.w;
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(lds + boff + c.qs_off);
+    dw[0] = v.x;
+    dw[1] = v.y;
+  }
+#pragma unroll
+  for (int i = 0; i < E / 4; ++i) {
+    const uint32_t v = (dw[i] >> c.nib) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) wv[4 * i + b] = static_cast<float>((v >> (8 * b)) & 0xFFu);
+  }
+  return make_float2(f16_to_f32(h.x & 0xFFFFu) * static_cast<float>(sc),
+                     f16_to_f32(h.x >> 16) * static_cast<float>(mn));
+}
+
 // First element, within the lane's k-slice, of the j-th run of 4 activations the lane
 // multiplies (E/4 runs, in the order of decode_lane's weights).
 template <int WT, int E>
 __device__ __forceinline__ int x_run(int lane, int j) {
-  const int bl = lane / (32 / E), q = lane % (32 / E);
+  constexpr int kElems = WT == kQ4_K ? kQ4KElems : 32;
+  const int bl = lane / (kElems / E), q = lane % (kElems / E);
   if constexpr (WT == kQ4_0) return bl * 32 + (E / 2) * q + (j < E / 8 ? 4 * j : 16 + 4 * (j - E / 8));
-  return bl * 32 + E * q + 4 * j;
+  return bl * kElems + E * q + 4 * j;
 }
 
 template <int WT, int NTC, int R, int NSTAGE, int MAXW, int SLICE>
@@ -286,6 +350,7 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
 
   const int q = lane % S::kLanesPerBlock;
   const int blk_off = wave * S::kSegBytes + (lane / S::kLanesPerBlock) * S::BB;  // this lane's block in a row
+  const Q4KLane qk = q4k_lane<E>(q);  // used by Q4_K only
 
   for (int win = 0; win < p.n_slots; win += 64) {
     uint64_t mask;
@@ -328,6 +393,15 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
           for (int j = 0; j < E; ++j) xr[t][j] = 0.f;
         }
       }
+      float xsum[NTC];  // Q4_K: the sum of the lane's activations, the factor of its sub-block min
+#pragma unroll
+      for (int t = 0; t < NTC; ++t) {
+        xsum[t] = 0.f;
+        if constexpr (WT == kQ4_K) {
+#pragma unroll
+          for (int j = 0; j < E; ++j) xsum[t] += xr[t][j];
+        }
+      }
 
       // Prologue: the first NSTAGE-1 tiles in flight.
 #pragma unroll
@@ -348,13 +422,24 @@ __global__ __launch_bounds__(64 * MAXW) void matvec_sliced_kernel(MatvecParams p
 #pragma unroll
           for (int r = 0; r < R; ++r) {
             float wv[E];
-            const float d = decode_lane<WT, E>(ring_lds, seg + r * rowbytes, q, wv);
+            if constexpr (WT == kQ4_K) {
+              const float2 f = decode_q4k<E>(ring_lds, seg + r * rowbytes, qk, wv);
 #pragma unroll
-            for (int t = 0; t < NTC; ++t) {
-              float s = 0.f;
+              for (int t = 0; t < NTC; ++t) {
+                float s = 0.f;
 #pragma unroll
-              for (int j = 0; j < E; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
-              acc[t][r] = d * s;
+                for (int j = 0; j < E; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
+                acc[t][r] = __builtin_fmaf(f.x, s, -(f.y * xsum[t]));
+              }
+            } else {
+              const float d = decode_lane<WT, E>(ring_lds, seg + r * rowbytes, q, wv);
+#pragma unroll
+              for (int t = 0; t < NTC; ++t) {
+                float s = 0.f;
+#pragma unroll
+                for (int j = 0; j < E; ++j) s = __builtin_fmaf(xr[t][j], wv[j], s);
+                acc[t][r] = d * s;
+              }
             }
           }
 #pragma unroll
@@ -464,7 +549,7 @@ constexpr Shape sliced_shape(int wt, int ntc, bool k8) {
                                                                                              : Shape{4, 3, 512};
     return ntc == 8 ? Shape{4, 2, 512} : Shape{4, 2, 1024};
   }
-  if (wt == kQ4_0) {
+  if (wt == kQ4_0 || wt == kQ4_K) {
     if (!k8) return ntc == 4 ? Shape{4, 3, 1024} : Shape{4, 2, 1024};
     return ntc == 1 ? Shape{8, 2, 1024} : Shape{4, 2, 1024};
   }
@@ -505,6 +590,7 @@ hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tok, h
     case kQ4_0: return launch_wt<kQ4_0>(p, max_tok, n_exp_rows, stream);
     case kF32: return launch_wt<kF32>(p, max_tok, n_exp_rows, stream);
     case kF16: return launch_wt<kF16>(p, max_tok, n_exp_rows, stream);
+    case kQ4_K: return launch_wt<kQ4_K>(p, max_tok, n_exp_rows, stream);
     default: return hipErrorInvalidValue;
   }
 }

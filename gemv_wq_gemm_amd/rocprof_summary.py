@@ -35,7 +35,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 # other sources no longer describe the library.
 KERNEL_SOURCES = ["csrc/wq_matvec_sliced.hip", "csrc/wq_matvec_mfma.hip", "csrc/wq_matvec.hip", "csrc/wq_gemm.hip",
                   "csrc/wq_decode.hpp", "csrc/wq_internal.hpp", "csrc/wq_lds_dma.hpp", "csrc/wq_moe_sched.hpp",
-                  "csrc/wq_tile_math.hpp", "csrc/wq_encoder.hip", "build.py"]
+                  "csrc/wq_tile_math.hpp", "csrc/wq_encoder.hip", "csrc/wq_matvec_q4k.hip", "build.py"]
 
 
 def source_digest(files=KERNEL_SOURCES) -> str:

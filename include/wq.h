@@ -76,6 +76,17 @@ extern "C" {
  *            type 0, copied as stored by `Gpu::upload_linear`).
  * WQ_W_F16:  uint16[m][k], IEEE binary16, little-endian (wavo `Linear` GEMM
  *            type 1).
+ * WQ_W_Q4_K: m rows of k/256 super-blocks of 144 bytes, k a multiple of 256
+ *            (hanzo-ml `matvec_q4k_gpu` names the type and both sizes; the
+ *            byte layout is GGML's published k-quant super-block): bytes 0-1
+ *            f16 d, 2-3 f16 dmin, 4-15 the 6-bit scale sc_j and 6-bit min m_j
+ *            of each 32-element sub-block j (j < 4: low 6 bits of bytes 4+j
+ *            and 8+j; j >= 4: low and high nibble of byte 8+j, their top two
+ *            bits in the top bits of bytes j and 4+j), 16-143 the 4-bit quants
+ *            (sub-blocks 2c and 2c+1 in the low and high nibbles of bytes
+ *            16+32c .. 16+32c+31); value = d*sc_j*q - dmin*m_j. Q4_K takes the
+ *            matvec path only (n <= WQ_MATVEC_MAX_N, and wq_moe_matvec); the
+ *            matrix-core paths refuse it with WQ_ERR_WTYPE.
  * Every type enters every path exactly: the f32 paths decode each weight to
  * its f32 value; the matrix cores take bf16 as stored, the integer quants with
  * the block scale applied in f32, and f16 / f32 weights as two / three bf16
@@ -85,6 +96,7 @@ extern "C" {
 #define WQ_W_Q4_0 2
 #define WQ_W_F32 3
 #define WQ_W_F16 4
+#define WQ_W_Q4_K 5
 
 /* ---- epilogue flags ---------------------------------------------------------
  * Applied to each output in this order: + bias[j] (WQ_BIAS); then at most one
@@ -148,7 +160,8 @@ extern "C" {
  *   bias  f32 [m] when flags & WQ_BIAS, else NULL; 4-byte aligned.
  *   y     f32 [n][m], 4-byte aligned (wavo's `Pass::gemv` writes its output from an offset into
  *         a larger buffer); read first when flags & WQ_RESIDUAL.
- *   n, m  >= 0 (n == 0 or m == 0: nothing to do, WQ_OK); k > 0, k % 32 == 0.
+ *   n, m  >= 0 (n == 0 or m == 0: nothing to do, WQ_OK); k > 0, k % 32 == 0 (Q4_K: k % 256 == 0,
+ *         and n <= WQ_MATVEC_MAX_N, else WQ_ERR_SHAPE / WQ_ERR_WTYPE).
  * Returns WQ_OK or a WQ_ERR_* code.
  */
 int wq_gemm(const float* x, const void* w, int wtype, const float* bias, unsigned flags,
@@ -233,7 +246,8 @@ int wq_moe_matvec_noalloc(const float* x, const void* w_experts, int wtype, cons
 /*
  * wq_dequantize: out[m][k] = the exact f32 value of every weight (bf16: the
  * upper-half bit pattern; Q8_0: d*q; Q4_0: d*(q-8); f32 as stored; f16
- * widened; all exact in f32) -- the per-type unpacking of the formats above
+ * widened; all exact in f32; Q4_K: d*sc_j*q - dmin*m_j rounded once to f32, since the
+ * difference of the two exact products need not fit in f32) -- the per-type unpacking of the formats above
  * (cortiq-engine `ae_gemm`'s weight pairs, wavo `Gpu::upload_linear`, hanzo-ml
  * `upload_qweight`), written out in full so it can be compared bit for bit.
  *   w    weight in `wtype` storage, 16-byte aligned; out f32 [m][k], 16-byte aligned
@@ -260,13 +274,13 @@ int wq_pad_weight(const void* w, int wtype, float* out, int64_t m, int64_t k, vo
 int64_t wq_padded_k(int64_t k);
 
 /* Bytes of one m x k weight: bf16 2*m*k; Q8_0 34*m*(k/32); Q4_0 18*m*(k/32); f32 4*m*k; f16 2*m*k;
- * -1 for an unknown type, negative sizes or k % 32 != 0. The block sizes are those of the formats
+ * Q4_K 144*m*(k/256); -1 for an unknown type, negative sizes, k % 32 != 0 or (Q4_K) k % 256 != 0. The block sizes are those of the formats
  * above (wavo `Gpu::upload_linear` sizes a Q8_0 row as k/32 blocks of 34 bytes; hanzo-ml
  * `matvec_q4_0_gpu` / `matvec_q8_0_gpu` refuse a buffer shorter than the blocks of nout rows). */
 int64_t wq_weight_bytes(int wtype, int64_t m, int64_t k);
 
 /* The path wq_gemm takes for these sizes: WQ_PATH_MATVEC or WQ_PATH_MFMA
- * (negative WQ_ERR_* for invalid sizes or type). The pages put the split between
+ * (negative WQ_ERR_* for invalid sizes or type, and for Q4_K with n > WQ_MATVEC_MAX_N). The pages put the split between
  * a matrix path for many rows of X (cortiq-engine `ae_gemm`, wavo `Pass::gemm`) and
  * a vector path for a few (wavo `Pass::gemv`, hanzo-ml `matvec_*_gpu`) without a
  * number; the reading taken is n <= 16 (WQ_MATVEC_MAX_N) on the f32 matvec. */

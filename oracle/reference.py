@@ -174,16 +174,10 @@ def q4_k_scale_min(scales) -> tuple:
     return sc, mn
 
 
-def decode_q4_k(raw: np.ndarray, m: int, k: int) -> np.ndarray:
-    """Q4_K rows -> ``f64[m][k]``: ``k/256`` super-blocks of 144 bytes per row.
-
-    Super-block bytes (GGML's published k-quant layout; the pages give only the sizes):
-    0-1 little-endian f16 ``d``, 2-3 little-endian f16 ``dmin``, 4-15 the packed 6-bit scales
-    and mins of the eight 32-element sub-blocks (``q4_k_scale_min``), 16-143 the 4-bit quants.
-    Sub-blocks 2c and 2c+1 (c = 0..3) share quant bytes 32c .. 32c+31: element l of sub-block
-    2c is the low nibble of byte 32c + l, element l of sub-block 2c+1 its high nibble.
-    Weight = ``d * sc_j * q - dmin * m_j`` for element of sub-block j, with unsigned ``q``.
-    """
+def decode_q4_k_parts(raw: np.ndarray, m: int, k: int):
+    """``(P, N)``, both ``f64[m][k]``: the two products a Q4_K weight is the difference of,
+    ``P = d * sc_j * q`` and ``N = dmin * m_j`` (so ``W = P - N``, ``decode_q4_k``). A layer that
+    computes with the two parts rounds relative to ``|P| + |N|`` rather than ``|W|``."""
     if k % QK_K:
         raise ValueError(f"k = {k} is not a multiple of {QK_K}")
     a = np.ascontiguousarray(raw).view(np.uint8).reshape(-1)
@@ -197,8 +191,33 @@ def decode_q4_k(raw: np.ndarray, m: int, k: int) -> np.ndarray:
     qs = sb[:, :, 16:].reshape(m, k // QK_K, 4, 32)          # [row][super][c][byte]
     q = np.stack([qs & 0xF, qs >> 4], axis=3)                # [row][super][c][nibble][l]
     q = q.reshape(m, k // QK_K, 8, 32).astype(np.float64)    # sub-block j = 2c + nibble
-    w = d[:, :, None, None] * sc[:, :, :, None] * q - dmin[:, :, None, None] * mn[:, :, :, None]
-    return w.reshape(m, k)
+    pos = d[:, :, None, None] * sc[:, :, :, None] * q
+    neg = np.broadcast_to(dmin[:, :, None, None] * mn[:, :, :, None], pos.shape)
+    return pos.reshape(m, k), np.ascontiguousarray(neg).reshape(m, k)
+
+
+def decode_q4_k(raw: np.ndarray, m: int, k: int) -> np.ndarray:
+    """Q4_K rows -> ``f64[m][k]``: ``k/256`` super-blocks of 144 bytes per row.
+
+    Super-block bytes (GGML's published k-quant layout; the pages give only the sizes):
+    0-1 little-endian f16 ``d``, 2-3 little-endian f16 ``dmin``, 4-15 the packed 6-bit scales
+    and mins of the eight 32-element sub-blocks (``q4_k_scale_min``), 16-143 the 4-bit quants.
+    Sub-blocks 2c and 2c+1 (c = 0..3) share quant bytes 32c .. 32c+31: element l of sub-block
+    2c is the low nibble of byte 32c + l, element l of sub-block 2c+1 its high nibble.
+    Weight = ``d * sc_j * q - dmin * m_j`` for element of sub-block j, with unsigned ``q``.
+    """
+    pos, neg = decode_q4_k_parts(raw, m, k)
+    return pos - neg
+
+
+def q4_k_part_scale(x, raw, m: int, k: int, rows=None) -> np.ndarray:
+    """``S2[t, j] = sum_k |x[t, k]| * (|P[j, k]| + |N[j, k]|)`` for a Q4_K weight (``P``, ``N`` of
+    ``decode_q4_k_parts``): the scale of the roundings of a product computed from the two parts."""
+    a = np.ascontiguousarray(raw).view(np.uint8).reshape(m, -1)
+    if rows is not None:
+        a = a[np.asarray(rows)]
+    pos, neg = decode_q4_k_parts(a, a.shape[0], k)
+    return np.abs(np.asarray(x, dtype=np.float64).reshape(-1, k)) @ (np.abs(pos) + np.abs(neg)).T
 
 
 def decode(raw: np.ndarray, wtype: int, m: int, k: int, rows=None) -> np.ndarray:

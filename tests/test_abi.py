@@ -49,6 +49,7 @@ def test_header_constants_match_binding():
     assert int(consts["WQ_W_Q8_0"]) == wq.W_Q8_0
     assert int(consts["WQ_W_Q4_0"]) == wq.W_Q4_0
     assert int(consts["WQ_W_F32"]) == wq.W_F32 and int(consts["WQ_W_F16"]) == wq.W_F16
+    assert int(consts["WQ_W_Q4_K"]) == wq.W_Q4_K
     assert int(consts["WQ_BIAS"]) == wq.BIAS and int(consts["WQ_GELU"]) == wq.GELU
     assert int(consts["WQ_RESIDUAL"]) == wq.RESIDUAL
     assert [int(consts[f"WQ_{a}"]) for a in ("SILU", "RELU", "TANH")] == [wq.SILU, wq.RELU, wq.TANH]
@@ -76,6 +77,11 @@ def test_version():
     (4, 5, 32, 320),
     (3, 5, 48, -1),
     (5, 5, 32, -1),
+    (5, 5, 768, 5 * 3 * 144),
+    (5, 14336, 4096, 33030144),
+    (5, 1, 512, 288),
+    (5, 2, 1024 + 32, -1),
+    (6, 5, 256, -1),
     (0, -1, 32, -1),
 ])
 def test_weight_bytes(wtype, m, k, want):
@@ -89,6 +95,11 @@ def test_path_selection():
     assert wq.gemm_path(1500, 1024, 4096, 0) == wq.PATH_MFMA
     with pytest.raises(wq.WqError):
         wq.gemm_path(4, 8, 40, 0)
+    assert wq.gemm_path(16, 8, 256, wq.W_Q4_K) == wq.PATH_MATVEC
+    with pytest.raises(wq.WqError, match="matvec path"):
+        wq.gemm_path(17, 8, 256, wq.W_Q4_K)
+    with pytest.raises(wq.WqError, match="256"):
+        wq.gemm_path(4, 8, 32, wq.W_Q4_K)
 
 
 def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
@@ -98,8 +109,12 @@ def _gemm(x=X, w=W, wtype=0, bias=None, flags=0, y=Y, n=4, m=8, k=32, path=0):
 
 
 @pytest.mark.parametrize("kwargs,code,msg", [
-    (dict(wtype=5), -3, "weight type"),
+    (dict(wtype=6), -3, "weight type"),
     (dict(wtype=-1), -3, "weight type"),
+    (dict(wtype=5), -2, "256"),
+    (dict(wtype=5, k=256, n=17), -3, "matvec path"),
+    (dict(wtype=5, k=256, path=2), -3, "matvec path"),
+    (dict(wtype=5, k=256, path=3), -3, "matvec path"),
     (dict(flags=64), -4, "flag"),
     (dict(flags=2 | 8), -4, "at most one activation"),
     (dict(flags=16 | 32 | 4), -4, "at most one activation"),
@@ -142,7 +157,8 @@ def test_linear_refuses_non_finite_alpha(alpha):
 
 def test_linear_checks_like_gemm_ex():
     lib = wq.lib()
-    assert lib.wq_linear(X, W, 5, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -3
+    assert lib.wq_linear(X, W, 6, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -3
+    assert lib.wq_linear(X, W, 5, None, 0, ctypes.c_float(1.0), Y, 4, 8, 32, 0, None) == -2
     assert lib.wq_linear(X, W, 0, None, 2 | 16, ctypes.c_float(0.5), Y, 4, 8, 32, 2, None) == -4
     assert lib.wq_linear(X, W, 0, None, 0, ctypes.c_float(0.5), Y, 4, 8, 40, 0, None) == -2
     assert lib.wq_linear(None, None, 0, None, 0, ctypes.c_float(2.0), None, 0, 8, 32, 0, None) == 0
@@ -185,7 +201,8 @@ def _moe(x=X, w=W, wtype=2, ids=B, gates=None, y=Y, n_tok=4, top_k=2, n_exp=8, m
 
 
 @pytest.mark.parametrize("kwargs,code", [
-    (dict(wtype=5), -3),
+    (dict(wtype=6), -3),
+    (dict(wtype=5), -2),
     (dict(top_k=0), -2),
     (dict(top_k=9), -2),
     (dict(n_exp=0), -2),
@@ -205,7 +222,8 @@ def test_moe_argument_errors(kwargs, code):
 
 def test_moe_noalloc_checks_like_moe():
     lib = wq.lib()
-    for kwargs, code in [(dict(wtype=5), -3), (dict(top_k=0), -2), (dict(ids=None), -1), (dict(y=B), -6)]:
+    for kwargs, code in [(dict(wtype=6), -3), (dict(wtype=5), -2), (dict(top_k=0), -2), (dict(ids=None), -1),
+                         (dict(y=B), -6)]:
         a = dict(x=X, w=W, wtype=2, ids=B, gates=None, y=Y, n_tok=4, top_k=2, n_exp=8, m=16, k=32)
         a.update(kwargs)
         st = lib.wq_moe_matvec_noalloc(a["x"], a["w"], a["wtype"], a["ids"], a["gates"], a["y"], a["n_tok"],
@@ -219,6 +237,7 @@ def test_moe_noalloc_checks_like_moe():
 
 @pytest.mark.parametrize("args,code", [
     ((W, 9, Y, 4, 32), -3),
+    ((W, 5, Y, 4, 32), -2),
     ((W, 1, Y, 4, 31), -2),
     ((None, 1, Y, 4, 32), -1),
     ((W + 2, 1, Y, 4, 32), -5),

@@ -193,3 +193,38 @@ def test_q4_k_rows_subset_and_sizes():
     assert np.array_equal(oracle.decode(raw, oracle.W_Q4_K, 5, 512, rows=[4, 1]), full[[4, 1]])
     with pytest.raises(ValueError):
         oracle.decode_q4_k(raw, 5, 480)
+
+
+def test_q4_k_parts_are_the_two_products():
+    g = np.random.default_rng(23)
+    for _ in range(10):
+        d_bits, dmin_bits = (int(b) for b in g.integers(0, 0x7C00, 2))
+        sc, mn, q = g.integers(0, 64, 8), g.integers(0, 64, 8), g.integers(0, 16, 256)
+        blk = _pack(d_bits, dmin_bits, sc, mn, q)
+        pos, neg = oracle.decode_q4_k_parts(blk, 1, 256)
+        d, dmin = _f16(d_bits), _f16(dmin_bits)
+        assert np.array_equal(pos[0], [d * int(sc[e // 32]) * int(q[e]) for e in range(256)])
+        assert np.array_equal(neg[0], [dmin * int(mn[e // 32]) for e in range(256)])
+        assert np.array_equal(oracle.decode_q4_k(blk, 1, 256), pos - neg)
+
+
+def test_q4_k_part_scale_brute_force():
+    g = synth.rng(95)
+    x = synth.normal_f32(g, (2, 512), 1.0)
+    raw = synth.q4_k_weight(g, 3, 512)
+    got = oracle.q4_k_part_scale(x, raw, 3, 512)
+    for j in range(3):
+        b = [int(v) for v in raw[j]]
+        for t in range(2):
+            tot = []
+            for s in range(2):
+                o = 144 * s
+                d, dmin = _f16(b[o] | b[o + 1] << 8), _f16(b[o + 2] | b[o + 3] << 8)
+                sc, mn = oracle.q4_k_scale_min(np.array(b[o + 4:o + 16]))
+                for e in range(256):
+                    jj, l = divmod(e, 32)
+                    qb = b[o + 16 + 32 * (jj // 2) + l]
+                    q = (qb >> 4) if jj % 2 else (qb & 15)
+                    tot.append(abs(float(x[t, 256 * s + e])) * (abs(d * int(sc[jj]) * q) + abs(dmin * int(mn[jj]))))
+            assert got[t, j] == pytest.approx(math.fsum(tot), rel=1e-12)
+    assert (got >= oracle.linear(x, raw, oracle.W_Q4_K, 3, 512)[1] - 1e-12).all()
