@@ -27,6 +27,8 @@ The same JSON line carries:
                 fraction of peak, the streaming-read floor for the same bytes (a plain read kernel,
                 libwq_bench.so) and the fraction of it reached (frac_of_sol), counted traffic and a CPU
                 baseline of its own;
+                Q4_K weights (hanzo-ml matvec_q4k_gpu) add the matvec 14336x4096 at n = 1 and the
+                MoE of 16 tokens top-2 of 8 experts of that shape, gated, both on Q4_K super-blocks;
                 The rest of the encoder block adds LayerNorm 1500x1024, the q/k norm + rotation over
                 8 heads of 128 and attention (1500 frames, 100 masked) to rooflines, each with a CPU
                 baseline;
@@ -63,7 +65,7 @@ def _parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--legs", default="all",
-                    help="comma list of workload groups to run (chain, c1, c2, c3, c4, moe1, moe64, enc, others; "
+                    help="comma list of workload groups to run (chain, c1, c2, c3, c4, moe1, moe64, q4k, enc, others; "
                          "default all): profiling runs select one so its kernels' counters are its own")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run an elementwise copy of 256 MiB (reads and writes that many bytes), "
@@ -182,7 +184,7 @@ def main():
     import synth
     from gemv_wq_gemm_amd.rocprof_summary import read_traffic
 
-    all_legs = {"chain", "c1", "c2", "c3", "c4", "moe1", "moe64", "enc", "others"}
+    all_legs = {"chain", "c1", "c2", "c3", "c4", "moe1", "moe64", "q4k", "enc", "others"}
     legs = all_legs if args.legs == "all" else set(args.legs.split(","))
     if legs - all_legs:
         print(f"unknown legs {sorted(legs - all_legs)}; choose from {sorted(all_legs)}", file=sys.stderr)
@@ -358,7 +360,7 @@ def _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic):
     out = {}
     legs = args.legs_set
     R = args.reps
-    floor = Floor(torch, timer, dev) if legs & {"c2", "c3", "c4", "moe1", "moe64"} else None
+    floor = Floor(torch, timer, dev) if legs & {"c2", "c3", "c4", "moe1", "moe64", "q4k"} else None
 
     # C1: bf16 GEMM 64x256x256 + bias + GELU (launch-bound by size)
     if "c1" in legs:
@@ -369,8 +371,39 @@ def _rooflines(torch, wq, synth, dev, timer, to_dev, args, read_traffic):
         _c3(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic)
     if legs & {"c4", "moe1", "moe64"}:
         _moe(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic, legs)
+    if "q4k" in legs:
+        _q4k(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic)
     torch.cuda.empty_cache()
     return out
+
+
+def _q4k(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic):
+    """Q4_K (hanzo-ml matvec_q4k_gpu / moe_matvec_gpu) on the Q4_0 workloads' shapes: 14336 x 4096 at
+    one token, and 16 tokens top-2 of 8 experts, gated."""
+    m, k = 14336, 4096
+    wb = wq.weight_bytes(wq.W_Q4_K, m, k)
+    nc = max(2, -(-ROTATE_BYTES // wb))
+    W = _rotated(torch, to_dev(synth.q4_k_weight(synth.rng(0, 6, 1), m, k).reshape(-1)), m, nc)
+    x = to_dev(synth.normal_f32(synth.rng(0, 6, 2), (1, k), 1.0))
+    y = torch.empty((1, m), device=dev)
+    gs = [wq.bind_gemm(x, W[i], wq.W_Q4_K, m=m, k=k, out=y) for i in range(nc)]
+    st = _stats(timer.runs(lambda i: gs[i % nc](), 100, R))
+    out["NEXT2_q4_k_14336x4096_n1"] = _hbm_entry(st, wb, floor.us(wb, R), read_traffic(COUNTERS, "q4_k_n1"),
+                                                 extra={"copies": nc})
+    del W
+    banks = [to_dev(np.stack([synth.q4_k_weight(synth.rng(0, 6, 3, b, e), m, k) for e in range(8)]).reshape(-1))
+             for b in range(3)]
+    x16 = to_dev(synth.normal_f32(synth.rng(0, 6, 4), (16, k), 1.0))
+    ids, gates = synth.moe_routing(synth.rng(0, 6, 5), 16, 8, 2)
+    ids_d, gates_d = to_dev(ids), to_dev(gates)
+    y16 = torch.empty((16, m), device=dev)
+    touched = len(np.unique(ids))
+    st = _stats(timer.runs(lambda i: wq.moe_matvec(x16, banks[i % 3], wq.W_Q4_K, ids_d, gates_d, n_experts=8, m=m,
+                                                   k=k, out=y16), 30, R))
+    key = "NEXT2_moe_q4_k_16tok_top2_of_8"
+    out[key] = _hbm_entry(st, touched * wb, floor.us(touched * wb, R), read_traffic(COUNTERS, key),
+                          extra={"experts_touched": touched, "n_experts": 8, "tokens": 16, "top_k": 2})
+    del banks
 
 
 def _c1(torch, wq, synth, dev, timer, to_dev, R, out, read_traffic):
@@ -704,6 +737,13 @@ def _cpu_configs(synth):
             x64[t_idx] @ w.T
     res["C4_moe_q4_0_16tok_top2_of_8"] = entry(_cpu_time(c4, 3), 2 * 33030144,
                                                f"experts {experts[0]} and {experts[1]} of the 8 (their routed tokens)")
+    wk = synth.q4_k_weight(synth.rng(0, 6, 1), 14336, 4096)
+    xk = synth.normal_f32(synth.rng(0, 6, 2), (1, 4096), 1.0)
+
+    def q4k():
+        w = oracle.decode(wk, oracle.W_Q4_K, 14336, 4096)
+        np.asarray(xk, np.float64) @ w.T
+    res["NEXT2_q4_k_14336x4096_n1"] = entry(_cpu_time(q4k, 3), 33030144, "the full call")
     return res
 
 

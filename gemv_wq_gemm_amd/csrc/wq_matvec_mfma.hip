@@ -1,5 +1,5 @@
-// The MoE matvec on matrix cores, with f32 accuracy (Q8_0 and Q4_0 weights); also the plain layer
-// at 9 to 16 tokens.
+// The MoE matvec on matrix cores, with f32 accuracy (Q8_0, Q4_0 and Q4_K weights); also the plain
+// layer at 9 to 16 tokens.
 //
 // Contract: per routed slot s and output row j, y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k]
 // (hanzo-ml src/wgpu_backend.rs `moe_matvec_gpu`), the same as the f32 matvec kernels. Without
@@ -17,6 +17,10 @@
 //    exactly (outside the bottom of the exponent range).
 //  * The integer quants q (Q8_0) and q - 8 (Q4_0, taken as (q - 8) / 16 against activations
 //    times 16) are exact in bf16, and products of two bf16 values are exact in f32.
+//  * Q4_K (hanzo-ml `matvec_q4k_gpu`; GGML's k-quant super-block of 256 weights in 144 bytes): the
+//    unsigned quants q (0..15) enter as they are, and each 32-element sub-block j adds
+//    d sc_j * (its MFMA sum of x q) - dmin m_j * (the sum of its activations), the activation sums
+//    being formed once per group of slots. A wave's slice (8 sub-blocks) is one super-block.
 //  * One 32-element block is one MFMA's k: three chained MFMAs (one per activation part, sharing
 //    the decoded weights) sum the block's products into a fresh 16x16 f32 tile, which the block's
 //    scale then multiplies and adds to the running sum in f32. So only f32 additions round: the
@@ -137,6 +141,38 @@ __device__ __forceinline__ void split3(const float (&x)[8], bf16x8& p1, bf16x8& 
   }
 }
 
+// The 8 quants of k-octet o of Q4_K sub-block j, as MFMA B operand (q exact in bf16): nibble
+// SH / 4 (low for even j, high for odd j) of bytes 8o .. 8o+7 of the 32 bytes that sub-blocks j and
+// j^1 share, given as the two dwords d0, d1.
+template <int SH>
+__device__ __forceinline__ bf16x8 q4k_octet(uint32_t d0, uint32_t d1) {
+  const uint32_t l0 = (d0 >> SH) & 0x0F0F0F0Fu, l1 = (d1 >> SH) & 0x0F0F0F0Fu;
+  auto b = [](uint32_t w, int i) { return static_cast<float>((w >> (8 * i)) & 0xFFu); };
+  uint4 u;
+  u.x = bf16_pair(b(l0, 0), b(l0, 1));
+  u.y = bf16_pair(b(l0, 2), b(l0, 3));
+  u.z = bf16_pair(b(l1, 0), b(l1, 1));
+  u.w = bf16_pair(b(l1, 2), b(l1, 3));
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// (d sc_j, dmin m_j) of sub-block j of a Q4_K super-block from its 16 header bytes: bytes 0-1 f16 d,
+// 2-3 f16 dmin, then the 6-bit fields (j < 4: low 6 bits of scale bytes j and j+4; j >= 4: low and
+// high nibble of scale byte j+4 with the top 2 bits of scale bytes j-4 and j). Both exact in f32.
+template <int J>
+__device__ __forceinline__ float2 q4k_factor(const uint4& h, float d, float dmin) {
+  constexpr uint32_t sh = 8u * (J & 3);
+  uint32_t sc, mn;
+  if constexpr (J < 4) {
+    sc = (h.y >> sh) & 63u;
+    mn = (h.z >> sh) & 63u;
+  } else {
+    sc = ((h.w >> sh) & 15u) | (((h.y >> (sh + 6)) & 3u) << 4);
+    mn = ((h.w >> (sh + 4)) & 15u) | (((h.z >> (sh + 6)) & 3u) << 4);
+  }
+  return make_float2(d * static_cast<float>(sc), dmin * static_cast<float>(mn));
+}
+
 // Calls f(integral_constant<int, I>) for I = 0 .. N-1, in order.
 template <int I, int N, typename F>
 __device__ __forceinline__ void static_for(F&& f) {
@@ -164,6 +200,8 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
   __shared__ __attribute__((aligned(16))) uint8_t ring[NSTAGE * kSlotBytes];
   __shared__ float part[PB][kMaxWaves * kPartWave];
   __shared__ int slot_lds[kSlots];
+  // Q4_K: the sum of each slot's activations over each 32-element sub-block, [sub-block][slot].
+  __shared__ __attribute__((aligned(16))) float xsum_lds[WT == kQ4_K ? kMaxK / 32 * kSlots : 4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -227,7 +265,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
   const int j = lane & 15;  // weight row in the tile (B, D column); slot as A
   const int o = lane >> 4;  // k-octet of each block; D rows 4o .. 4o+3
   const int s_off = j * stride + wave * kSliceBlocks * BB;         // the lane's row slice
-  const int q_off = s_off + (WT == kQ8_0 ? 8 * o : 4 * o);  // and its quant bytes
+  const int q_off = s_off + (WT == kQ8_0 ? 8 * o : WT == kQ4_K ? 16 + 8 * o : 4 * o);  // and its quant bytes
 
   // Finishes tile `tile` from the wave partials in part[buf]: the k-slices of all waves, added in
   // wave order.
@@ -277,6 +315,29 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
       for (int t = 0; t < kSlots; ++t)
         if (t == j) my_slot = slot_of[t];
       if (threadIdx.x < kSlots) slot_lds[threadIdx.x] = my_slot;  // read after the next barrier
+      if constexpr (WT == kQ4_K) {
+        // Sub-block sums of the pass's activations, each a 32-term sum in element order; read
+        // after the next barrier.
+        __syncthreads();  // slot_lds is complete
+        const int nsub = p.k / 32;
+        for (int i = threadIdx.x; i < nsub * kSlots; i += blockDim.x) {
+          const int sb = i / kSlots, t = i - sb * kSlots;
+          const int st = slot_lds[t];
+          float sum = 0.f;
+          if (st >= 0) {
+            const float4* xp = reinterpret_cast<const float4*>(p.x + static_cast<long long>(st / p.top_k) * p.k + 32 * sb);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+              const float4 v = xp[c];
+              sum += v.x;
+              sum += v.y;
+              sum += v.z;
+              sum += v.w;
+            }
+          }
+          xsum_lds[i] = sum;
+        }
+      }
 
       // Prologue: the first NSTAGE-1 tiles in flight, then the activation operands.
 #pragma unroll
@@ -290,10 +351,12 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         for (int bb = 0; bb < kSliceBlocks; ++bb) {
           float xv[8];
           if (xs) {
-            // The k order of decode_octet: Q8_0 elements 8o .. 8o+7, Q4_0 4o .. 4o+3 and 16+4o .. 16+4o+3.
+            // The k order of decode_octet: Q8_0 and Q4_K elements 8o .. 8o+7, Q4_0 4o .. 4o+3 and
+            // 16+4o .. 16+4o+3.
+            constexpr bool kOctet = WT == kQ8_0 || WT == kQ4_K;
             const float* xb = xs + wave * (32 * kSliceBlocks) + bb * 32;
-            const float4 v0 = *reinterpret_cast<const float4*>(xb + (WT == kQ8_0 ? 8 * o : 4 * o));
-            const float4 v1 = *reinterpret_cast<const float4*>(xb + (WT == kQ8_0 ? 8 * o + 4 : 16 + 4 * o));
+            const float4 v0 = *reinterpret_cast<const float4*>(xb + (kOctet ? 8 * o : 4 * o));
+            const float4 v1 = *reinterpret_cast<const float4*>(xb + (kOctet ? 8 * o + 4 : 16 + 4 * o));
             xv[0] = v0.x; xv[1] = v0.y; xv[2] = v0.z; xv[3] = v0.w;
             xv[4] = v1.x; xv[5] = v1.y; xv[6] = v1.z; xv[7] = v1.w;
           } else {
@@ -324,6 +387,28 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
 
         const int slot_base = (tile % NSTAGE) * kSlotBytes;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (WT == kQ4_K) {
+          static_assert(kSliceBlocks == 8, "a Q4_K slice is one super-block");
+          const uint4 h = *reinterpret_cast<const uint4*>(ring + slot_base + s_off);
+          const float d = f16_to_f32(h.x & 0xFFFFu), dmin = f16_to_f32(h.x >> 16);
+          const float* xsw = xsum_lds + wave * kSliceBlocks * kSlots + 4 * o;
+          static_for<0, kSliceBlocks>([&](auto jj) {
+            constexpr int J = decltype(jj)::value;
+            const uint2 qd = *reinterpret_cast<const uint2*>(ring + slot_base + q_off + 32 * (J >> 1));
+            const bf16x8 wb = q4k_octet<4 * (J & 1)>(qd.x, qd.y);
+            const float2 f = q4k_factor<J>(h, d, dmin);
+            const float4 xsum = *reinterpret_cast<const float4*>(xsw + J * kSlots);
+            f32x4 blk = {0.f, 0.f, 0.f, 0.f};
+            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][J], wb, blk, 0, 0, 0);
+            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][J], wb, blk, 0, 0, 0);
+            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2][J], wb, blk, 0, 0, 0);
+            acc[0] = __builtin_fmaf(f.x, blk[0], __builtin_fmaf(-f.y, xsum.x, acc[0]));
+            acc[1] = __builtin_fmaf(f.x, blk[1], __builtin_fmaf(-f.y, xsum.y, acc[1]));
+            acc[2] = __builtin_fmaf(f.x, blk[2], __builtin_fmaf(-f.y, xsum.z, acc[2]));
+            acc[3] = __builtin_fmaf(f.x, blk[3], __builtin_fmaf(-f.y, xsum.w, acc[3]));
+            if constexpr (J % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
+          });
+        } else {
         static_for<0, kSliceBlocks>([&](auto bb) {
           constexpr int B = decltype(bb)::value;
           float scale;
@@ -337,6 +422,7 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
           // Keep the scheduler within a few blocks: hoisting many decodes runs out of registers.
           if constexpr (B % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
         });
+        }
         // One buffer: every thread has finished adding up the previous tile's partials.
         if constexpr (PB == 1) __syncthreads();
         float* pw = part[tile % PB] + wave * kPartWave;
@@ -397,6 +483,7 @@ hipError_t launch_mfma(const MatvecParams& p, hipStream_t stream) {
 }  // namespace
 
 bool matvec_mfma_supports(int wtype, int k) {
+  if (wtype == kQ4_K) return k % kQ4KElems == 0 && k >= 2048 && k <= kMaxK;
   return (wtype == kQ8_0 || wtype == kQ4_0) && k % 512 == 0 && k >= 2048 && k <= kMaxK;
 }
 
@@ -405,6 +492,7 @@ hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stre
   // Both run a 2-slot ring (one tile in flight behind the one in use). For Q4_0 a third slot
   // measured 3-4% slower on the MoE workload (16 tokens, top-2 of 8 experts of 14336 x 4096).
   if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2, 8, 1>(p, stream);
+  if (wtype == kQ4_K) return launch_mfma<kQ4_K, 2, 8, 2>(p, stream);
   return launch_mfma<kQ4_0, 2, 8, 2>(p, stream);
 }
 

@@ -12,9 +12,11 @@
 // plain layer (with wavo's dual outputs), y[s][j] = sum_k W[ids[s]][j][k] x[s / top_k][k] for the
 // MoE slots, all in f32.
 //
-// launch_matvec_q4k sends k a multiple of 1024 up to 8192 (no dual outputs) to the sliced kernel
-// (wq_matvec_sliced.hip), which streams tiles of rows through an LDS ring. The general kernel here
-// takes every other k (a multiple of 256) and the dual outputs:
+// launch_matvec_q4k sends MoE calls with two or more slots per expert and 9 to 16 tokens (k a
+// multiple of 256 in 2048..4096) to the matrix-core kernel (wq_matvec_mfma.hip), k a multiple of
+// 1024 up to 8192 to the sliced kernel (wq_matvec_sliced.hip), which streams tiles of rows through
+// an LDS ring (neither stores dual outputs). The general kernel here takes every other k (a
+// multiple of 256) and the dual outputs:
 //  * A wave owns RW consecutive rows; lane l walks the sub-blocks l, l+64, ... of the rows. Per
 //    sub-block it loads the 16 header bytes and the 32 quant bytes of its super-block with 16-byte
 //    loads (the 8 lanes of one super-block read neighbouring bytes, so the wave's loads of a row
@@ -241,6 +243,11 @@ __global__ __launch_bounds__(256) void dequantize_q4k_kernel(const uint8_t* w, f
 
 hipError_t launch_matvec_q4k(const MatvecParams& p, int max_tok, hipStream_t stream) {
   if (p.k % kQ4KElems != 0) return hipErrorInvalidValue;
+  // As for the other quantized types: the matrix cores for MoE with two or more slots per expert
+  // and for 9 to 16 tokens (every weight decoded once for up to 16 slots), the sliced f32 kernel
+  // for 1 to 8 tokens.
+  if (p.dual == 0 && matvec_mfma_supports(kQ4_K, p.k) && ((p.ids != nullptr && max_tok > 1) || max_tok > 8))
+    return launch_matvec_mfma(kQ4_K, p, stream);
   if (p.dual == 0 && matvec_sliced_supports(p.k)) return launch_matvec_sliced(kQ4_K, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;
   if (max_tok <= 1) return launch_general_rw<1>(p, n_exp_rows, stream);
