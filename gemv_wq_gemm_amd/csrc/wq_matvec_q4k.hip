@@ -58,15 +58,20 @@ __device__ __forceinline__ float2 q4k_factors(const uint4& h, int j) {
 }
 
 // The 32 quants of sub-block j from its super-block's 32 quant bytes (low nibbles for even j,
-// high for odd j), as floats.
+// high for odd j), as floats. A byte 0000qqqq read as FP8 E4M3 is q * 2^-9 exactly (q = 0..15),
+// so one conversion with scale 2^9 gives two quants.
 __device__ __forceinline__ void q4k_quants(const uint4& a, const uint4& b, int j, float (&q)[32]) {
   const uint32_t dw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
   const int sh = 4 * (j & 1);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint32_t v = (dw[i] >> sh) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) q[4 * i + c] = static_cast<float>((v >> (8 * c)) & 0xFFu);
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.f, true);
+    q[4 * i] = lo[0];
+    q[4 * i + 1] = lo[1];
+    q[4 * i + 2] = hi[0];
+    q[4 * i + 3] = hi[1];
   }
 }
 

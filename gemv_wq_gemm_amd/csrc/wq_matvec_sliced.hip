@@ -254,11 +254,17 @@ __device__ __forceinline__ float2 decode_q4k(const uint8_t* lds, int boff, const
     dw[0] = v.x;
     dw[1] = v.y;
   }
+  // A byte 0000qqqq read as FP8 E4M3 is q * 2^-9 exactly (q = 0..15), so one conversion with
+  // scale 2^9 gives two quants as f32.
 #pragma unroll
   for (int i = 0; i < E / 4; ++i) {
     const uint32_t v = (dw[i] >> c.nib) & 0x0F0F0F0Fu;
-#pragma unroll
-    for (int b = 0; b < 4; ++b) wv[4 * i + b] = static_cast<float>((v >> (8 * b)) & 0xFFu);
+    const auto lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.f, false);
+    const auto hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.f, true);
+    wv[4 * i] = lo[0];
+    wv[4 * i + 1] = lo[1];
+    wv[4 * i + 2] = hi[0];
+    wv[4 * i + 3] = hi[1];
   }
   return make_float2(f16_to_f32(h.x & 0xFFFFu) * static_cast<float>(sc),
                      f16_to_f32(h.x >> 16) * static_cast<float>(mn));
