@@ -133,8 +133,11 @@ int scratch_address(float** out) {
   return WQ_OK;
 }
 
+// io (inside the library only): bit 0, x holds bf16 bit patterns; bit 1, y receives them. Both
+// take bf16 weights on the bf16 matrix-core path (which rounds X to bf16 anyway), and a bf16 y
+// takes no residual and no dual outputs.
 int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
-                 float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream) {
+                 float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream, int io = 0) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   constexpr unsigned kActs = WQ_GELU | WQ_SILU | WQ_RELU | WQ_TANH;
@@ -160,13 +163,16 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     return fail(WQ_ERR_SHAPE, "the matvec path takes n <= %d, got %lld", WQ_MATVEC_MAX_N, (long long)n);
   if ((path == WQ_PATH_MFMA || path == WQ_PATH_MFMA_F32) && n > 65535LL * 128)
     return fail(WQ_ERR_SHAPE, "n = %lld exceeds the GEMM grid (65535 x 128 rows)", (long long)n);
+  if (io != 0 && (wtype != WQ_W_BF16 || path != WQ_PATH_MFMA || dual != 0 || ((io & 2) && (flags & WQ_RESIDUAL))))
+    return fail(WQ_ERR_SHAPE, "bf16 activations take bf16 weights on the bf16 matrix-core path");
   if (n == 0 || m == 0) return WQ_OK;
   if (!x || !w || !y) return fail(WQ_ERR_NULL, "x, w and y must not be NULL");
   if (!aligned(x, 16) || !aligned(w, 16)) return fail(WQ_ERR_ALIGN, "x and w must be 16-byte aligned");
   if (!aligned(y, 4) || (bias && !aligned(bias, 4))) return fail(WQ_ERR_ALIGN, "y and bias must be 4-byte aligned");
   const int64_t wbytes = wq_weight_bytes(wtype, m, k);
-  const int64_t ybytes = n * (m + dual) * 4;
-  if (overlap(y, ybytes, x, n * k * 4) || overlap(y, ybytes, w, wbytes) || overlap(y, ybytes, bias, (m + dual) * 4))
+  const int64_t ybytes = n * (m + dual) * ((io & 2) ? 2 : 4);
+  if (overlap(y, ybytes, x, n * k * ((io & 1) ? 2 : 4)) || overlap(y, ybytes, w, wbytes) ||
+      overlap(y, ybytes, bias, (m + dual) * 4))
     return fail(WQ_ERR_ALIAS, "y overlaps x, w or bias");
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -206,6 +212,8 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
     p.ystride = static_cast<int>(m + dual);
     p.dual = static_cast<int>(dual);
     p.x_parts = path == WQ_PATH_MFMA_F32 ? 3 : 1;
+    p.x_bf16 = io & 1;
+    p.y_bf16 = (io >> 1) & 1;
     e = wq::launch_gemm(wtype, p, s);
   }
   if (e != hipSuccess) return hip_fail(e, "kernel launch");
@@ -562,22 +570,43 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   float* f = reinterpret_cast<float*>(base + w.f);
   void* attn_ws = base + w.attn;
   const float scale = 1.0f / std::sqrt(static_cast<float>(hd));
+  // With bf16 weights on the bf16 matrix cores each product rounds its input to bf16 as it reads
+  // it, so the LayerNorms, the attention and the MLP's first product hand their outputs over in
+  // bf16, rounded the same way: half the bytes, and the block's output is bit-identical. The
+  // f32-accurate path, the matvec path (n <= 16) and the other weight types keep f32 hand-offs.
+  const int gpath = path == WQ_PATH_AUTO ? (n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA) : path;
+  const bool b16 = wtype == WQ_W_BF16 && gpath == WQ_PATH_MFMA && d % 64 == 0 && inter % 64 == 0 &&
+                   n * inter * 2 < (int64_t(1) << 32) && 3 * d * d * 2 < (int64_t(1) << 32) &&
+                   inter * d * 2 < (int64_t(1) << 32);
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   int r;
-  if ((r = wq_layer_norm(h, l->ln1, a, n, d, stream))) return r;
-  if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, path, stream)))
+  auto norm = [&](const float* wb) -> int {
+    if (!b16) return wq_layer_norm(h, wb, a, n, d, stream);
+    clear_error();
+    hipError_t e = wq::launch_layer_norm_bf16(h, wb, reinterpret_cast<uint16_t*>(a), static_cast<int>(n),
+                                               static_cast<int>(d), hs);
+    return e == hipSuccess ? WQ_OK : hip_fail(e, "LayerNorm launch");
+  };
+  if ((r = norm(l->ln1))) return r;
+  if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, gpath, stream,
+                        b16 ? 1 : 0)))
     return r;
   // The q/k norm + rotation runs fused with the attention's pack: k goes to the workspace in bf16
   // only (the f32 rows are not needed after), q is rewritten in place as wq_qk_norm_rope would.
   clear_error();
   hipError_t he = wq::launch_qk_attention(qkv, l->qn, l->kn, cs, valid, att, attn_ws, static_cast<int>(n),
                                           static_cast<int>(heads), static_cast<int>(hd), static_cast<int>(rot), scale,
-                                          static_cast<hipStream_t>(stream));
+                                          hs, b16 ? 1 : 0);
   if (he != hipSuccess) return hip_fail(he, "q/k norm + attention launch");
-  if ((r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, path, stream)))
+  if ((r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, gpath, stream,
+                        b16 ? 1 : 0)))
     return r;
-  if ((r = wq_layer_norm(h, l->ln2, a, n, d, stream))) return r;
-  if ((r = gemm_checked(a, l->fc1_w, wtype, l->fc1_b, WQ_BIAS | WQ_GELU, 1.0f, f, n, inter, d, 0, path, stream))) return r;
-  return gemm_checked(f, l->fc2_w, wtype, l->fc2_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, inter, 0, path, stream);
+  if ((r = norm(l->ln2))) return r;
+  if ((r = gemm_checked(a, l->fc1_w, wtype, l->fc1_b, WQ_BIAS | WQ_GELU, 1.0f, f, n, inter, d, 0, gpath, stream,
+                        b16 ? 3 : 0)))
+    return r;
+  return gemm_checked(f, l->fc2_w, wtype, l->fc2_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, inter, 0, gpath, stream,
+                      b16 ? 1 : 0);
 }
 
 const char* wq_last_error(void) { return g_err; }

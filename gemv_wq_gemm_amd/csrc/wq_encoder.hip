@@ -74,9 +74,21 @@ __device__ __forceinline__ uint16_t bf16_bits_rne(float v) {
 // LayerNorm
 // ---------------------------------------------------------------------------------------------
 
-// NV float4s per lane: d <= 256·NV, d % 4 == 0, x / y rows and wb 16-byte aligned.
-template <int NV>
-__global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, const float* __restrict__ wb, float* y,
+// Four outputs rounded to bf16 (nearest even, as the products round their f32 inputs), packed.
+__device__ __forceinline__ uint2 bf16x4_bits(float a, float b, float c, float d) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 lo, hi;
+  lo[0] = static_cast<__bf16>(a);
+  lo[1] = static_cast<__bf16>(b);
+  hi[0] = static_cast<__bf16>(c);
+  hi[1] = static_cast<__bf16>(d);
+  return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
+}
+
+// NV float4s per lane: d <= 256·NV, d % 4 == 0, x / y rows and wb 16-byte aligned. OB: y receives
+// bf16 bit patterns (8-byte aligned rows) for a product that rounds its input to bf16 anyway.
+template <int NV, bool OB = false>
+__global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, const float* __restrict__ wb, void* y,
                                                               int n, int d) {
   const int lane = threadIdx.x & 63;
   const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
@@ -106,7 +118,8 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, con
   }
   const float inv = rsqrtf(wave_sum(q) / fd + kLnEps);
   const float4* w4 = reinterpret_cast<const float4*>(wb);
-  float4* yr = reinterpret_cast<float4*>(y + row * d);
+  float4* yr = reinterpret_cast<float4*>(static_cast<float*>(y) + row * d);
+  uint2* yb = reinterpret_cast<uint2*>(static_cast<uint16_t*>(y) + row * d);
   float4 wv[NV], bv[NV];
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
@@ -119,16 +132,20 @@ __global__ __launch_bounds__(256) void layer_norm_vec_kernel(const float* x, con
     const int c = lane + 64 * i;
     if (c < nv) {
       const float4 w = wv[i], b = bv[i];
-      yr[c] = make_float4((v[i].x - mean) * inv * w.x + b.x, (v[i].y - mean) * inv * w.y + b.y,
-                          (v[i].z - mean) * inv * w.z + b.z, (v[i].w - mean) * inv * w.w + b.w);
+      const float4 o = make_float4((v[i].x - mean) * inv * w.x + b.x, (v[i].y - mean) * inv * w.y + b.y,
+                                   (v[i].z - mean) * inv * w.z + b.z, (v[i].w - mean) * inv * w.w + b.w);
+      if constexpr (OB) yb[c] = bf16x4_bits(o.x, o.y, o.z, o.w);
+      else yr[c] = o;
     }
   }
 }
 
 // Any d and alignment: three passes over the row in memory, one wave per row. In place is safe:
 // a lane writes y[i] only after every lane of the wave has read the row for the second time.
+// OB: y receives bf16 bit patterns.
+template <bool OB = false>
 __global__ __launch_bounds__(256) void layer_norm_scalar_kernel(const float* x, const float* __restrict__ wb,
-                                                                 float* y, int n, int d) {
+                                                                 void* y, int n, int d) {
   const int lane = threadIdx.x & 63;
   const long long row = static_cast<long long>(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (row >= n) return;
@@ -143,8 +160,11 @@ __global__ __launch_bounds__(256) void layer_norm_scalar_kernel(const float* x, 
     q += c * c;
   }
   const float inv = rsqrtf(wave_sum(q) / fd + kLnEps);
-  float* yr = y + row * d;
-  for (int i = lane; i < d; i += 64) yr[i] = (xr[i] - mean) * inv * wb[i] + wb[d + i];
+  for (int i = lane; i < d; i += 64) {
+    const float o = (xr[i] - mean) * inv * wb[i] + wb[d + i];
+    if constexpr (OB) static_cast<__bf16*>(y)[row * d + i] = static_cast<__bf16>(o);
+    else static_cast<float*>(y)[row * d + i] = o;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -423,6 +443,7 @@ struct AttnParams {
   int per_xcd;     // ceil(items / 8)
   float scale_l2;  // scale * log2(e): scores enter exp2
   int v4;          // hd % 8 == 0 and qkv, o 16-byte aligned: 16-byte loads of q, stores of o
+  int o_bf16;      // o receives bf16 bit patterns (for a product that rounds its input to bf16)
 };
 
 // LDS tile layout (one buffer of a 32-key tile):
@@ -665,14 +686,26 @@ __global__ __launch_bounds__(512) void attention_kernel(AttnParams p) {
   const float inv = 1.f / l;  // no valid key: 1/0, and 0 · inf = NaN, as the page's arithmetic gives
   const int q = q0 + 32 * qw + j;
   if (q < p.n) {
-    float* orow = p.o + static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
+    const long long obase = static_cast<long long>(q) * d + static_cast<long long>(h) * p.hd;
+    float* orow = p.o + obase;
+    __bf16* orow_b = reinterpret_cast<__bf16*>(p.o) + obase;
 #pragma unroll
     for (int dt = 0; dt < kDTiles; ++dt) {
 #pragma unroll
       for (int g4 = 0; g4 < 4; ++g4) {
         const int c = 32 * dt + 8 * g4 + 4 * hh;
         const f32x16& v = acc[dt];
-        if (p.v4) {
+        if (p.o_bf16) {
+          if (p.v4) {
+            if (c < p.hd)
+              *reinterpret_cast<uint2*>(orow_b + c) =
+                  bf16x4_bits(v[4 * g4] * inv, v[4 * g4 + 1] * inv, v[4 * g4 + 2] * inv, v[4 * g4 + 3] * inv);
+          } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              if (c + r < p.hd) orow_b[c + r] = static_cast<__bf16>(v[4 * g4 + r] * inv);
+          }
+        } else if (p.v4) {
           if (c < p.hd)
             *reinterpret_cast<float4*>(orow + c) =
                 make_float4(v[4 * g4] * inv, v[4 * g4 + 1] * inv, v[4 * g4 + 2] * inv, v[4 * g4 + 3] * inv);
@@ -690,25 +723,34 @@ int head_pad(int hd) { return hd <= 32 ? 32 : hd <= 64 ? 64 : 128; }
 
 }  // namespace
 
-hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, int d, hipStream_t stream) {
+template <bool OB>
+hipError_t launch_layer_norm_t(const float* x, const float* wb, void* y, int n, int d, hipStream_t stream) {
   if (n == 0) return hipSuccess;
   const dim3 grid((n + 3) / 4), block(256);
   const bool vec = d % 4 == 0 && d <= 4096 && (reinterpret_cast<uintptr_t>(x) & 15) == 0 &&
-                   (reinterpret_cast<uintptr_t>(y) & 15) == 0 && (reinterpret_cast<uintptr_t>(wb) & 15) == 0;
+                   (reinterpret_cast<uintptr_t>(y) & (OB ? 7 : 15)) == 0 && (reinterpret_cast<uintptr_t>(wb) & 15) == 0;
   if (!vec) {
-    hipLaunchKernelGGL(layer_norm_scalar_kernel, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL(layer_norm_scalar_kernel<OB>, grid, block, 0, stream, x, wb, y, n, d);
   } else if (d <= 256) {
-    hipLaunchKernelGGL(layer_norm_vec_kernel<1>, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL((layer_norm_vec_kernel<1, OB>), grid, block, 0, stream, x, wb, y, n, d);
   } else if (d <= 512) {
-    hipLaunchKernelGGL(layer_norm_vec_kernel<2>, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL((layer_norm_vec_kernel<2, OB>), grid, block, 0, stream, x, wb, y, n, d);
   } else if (d <= 1024) {
-    hipLaunchKernelGGL(layer_norm_vec_kernel<4>, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL((layer_norm_vec_kernel<4, OB>), grid, block, 0, stream, x, wb, y, n, d);
   } else if (d <= 2048) {
-    hipLaunchKernelGGL(layer_norm_vec_kernel<8>, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL((layer_norm_vec_kernel<8, OB>), grid, block, 0, stream, x, wb, y, n, d);
   } else {
-    hipLaunchKernelGGL(layer_norm_vec_kernel<16>, grid, block, 0, stream, x, wb, y, n, d);
+    hipLaunchKernelGGL((layer_norm_vec_kernel<16, OB>), grid, block, 0, stream, x, wb, y, n, d);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, int d, hipStream_t stream) {
+  return launch_layer_norm_t<false>(x, wb, y, n, d, stream);
+}
+
+hipError_t launch_layer_norm_bf16(const float* x, const float* wb, uint16_t* y, int n, int d, hipStream_t stream) {
+  return launch_layer_norm_t<true>(x, wb, y, n, d, stream);
 }
 
 hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int n, int heads,
@@ -753,7 +795,7 @@ AttnWs attn_ws(void* ws, int n, int heads) {
 
 template <int HDP>
 hipError_t run_attention(const float* qkv, const AttnWs& w, float* o, int n, int heads, int hd, float scale,
-                         hipStream_t stream) {
+                         hipStream_t stream, int o_bf16 = 0) {
   AttnParams p{};
   p.qkv = qkv;
   p.kb = w.kb;
@@ -769,6 +811,7 @@ hipError_t run_attention(const float* qkv, const AttnWs& w, float* o, int n, int
   p.per_xcd = (p.items + 7) / 8;
   p.scale_l2 = scale * 1.4426950408889634f;
   p.v4 = hd % 8 == 0 && (reinterpret_cast<uintptr_t>(qkv) & 15) == 0 && (reinterpret_cast<uintptr_t>(o) & 15) == 0;
+  p.o_bf16 = o_bf16;
   hipLaunchKernelGGL(attention_kernel<HDP>, dim3(p.per_xcd * 8), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
@@ -788,13 +831,13 @@ hipError_t launch_attention_hdp(const float* qkv, const int32_t* valid, float* o
 template <int HDP, int E>
 hipError_t launch_qk_attention_hdp(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
                                    float* o, void* ws, int n, int heads, int hd, int rot, float scale,
-                                   hipStream_t stream) {
+                                   hipStream_t stream, int o_bf16) {
   const AttnWs w = attn_ws<HDP>(ws, n, heads);
   hipLaunchKernelGGL((qk_pack_kernel<HDP, E>), dim3(w.npad / kQkFrames, heads), dim3(256), 0, stream, qkv, qn, kn, cs,
                      valid, w.kb, w.vt, w.kbias, n, w.npad, heads, hd, rot);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  return run_attention<HDP>(qkv, w, o, n, heads, hd, scale, stream);
+  return run_attention<HDP>(qkv, w, o, n, heads, hd, scale, stream, o_bf16);
 }
 
 hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
@@ -808,13 +851,15 @@ hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, vo
 }
 
 hipError_t launch_qk_attention(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
-                               float* o, void* ws, int n, int heads, int hd, int rot, float scale,
-                               hipStream_t stream) {
+                               void* o, void* ws, int n, int heads, int hd, int rot, float scale,
+                               hipStream_t stream, int o_bf16) {
   if (n == 0) return hipSuccess;
+  float* of = static_cast<float*>(o);
   switch (head_pad(hd)) {
-    case 32: return launch_qk_attention_hdp<32, 1>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
-    case 64: return launch_qk_attention_hdp<64, 1>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
-    default: return launch_qk_attention_hdp<128, 2>(qkv, qn, kn, cs, valid, o, ws, n, heads, hd, rot, scale, stream);
+    case 32: return launch_qk_attention_hdp<32, 1>(qkv, qn, kn, cs, valid, of, ws, n, heads, hd, rot, scale, stream, o_bf16);
+    case 64: return launch_qk_attention_hdp<64, 1>(qkv, qn, kn, cs, valid, of, ws, n, heads, hd, rot, scale, stream, o_bf16);
+    default:
+      return launch_qk_attention_hdp<128, 2>(qkv, qn, kn, cs, valid, of, ws, n, heads, hd, rot, scale, stream, o_bf16);
   }
 }
 

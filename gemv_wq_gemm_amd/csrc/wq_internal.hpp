@@ -93,21 +93,28 @@ struct GemmParams {
   int ystride;        // floats from one row of y to the next: m + dual
   int dual;           // outputs 0..dual-1 stored again at columns m + j, with bias[m + j]
   int x_parts;        // 3: X enters as three exact bf16 parts (three MFMAs per product); 1: as bf16(X)
+  int x_bf16;         // 1: x holds bf16 bit patterns [n][k] (already rounded; bf16 weights, x_parts 1)
+  int y_bf16;         // 1: y receives bf16 bit patterns [n][ystride], each output rounded to nearest
+                      // even (bf16 weights, no residual, no dual outputs)
 };
 
 hipError_t launch_gemm(int wtype, const GemmParams& p, hipStream_t stream);
 
 // ---- encoder block (wq_encoder.hip) ---------------------------------------------------------
 hipError_t launch_layer_norm(const float* x, const float* wb, float* y, int n, int d, hipStream_t stream);
+// The same with y as bf16 bit patterns (8-byte aligned for the vector kernel), each output rounded to
+// nearest even: the encoder block's input to a product that rounds it so anyway.
+hipError_t launch_layer_norm_bf16(const float* x, const float* wb, uint16_t* y, int n, int d, hipStream_t stream);
 hipError_t launch_qk_norm_rope(float* qkv, const float* qn, const float* kn, const float* cs, int n, int heads,
                                int hd, int rot, hipStream_t stream);
 long long attention_workspace_bytes(long long n, long long heads, long long hd);
 hipError_t launch_attention(const float* qkv, const int32_t* valid, float* o, void* ws, int n, int heads, int hd,
                             float scale, hipStream_t stream);
 // q/k norm + rotation fused with the attention's pack (k is not written back to qkv), then the
-// attention: the block's path. Same workspace as launch_attention.
+// attention: the block's path. Same workspace as launch_attention. o_bf16: o receives bf16 bit
+// patterns (rounded to nearest even) instead of f32.
 hipError_t launch_qk_attention(float* qkv, const float* qn, const float* kn, const float* cs, const int32_t* valid,
-                               float* o, void* ws, int n, int heads, int hd, int rot, float scale,
-                               hipStream_t stream);
+                               void* o, void* ws, int n, int heads, int hd, int rot, float scale,
+                               hipStream_t stream, int o_bf16);
 
 }  // namespace wq

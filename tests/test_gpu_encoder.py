@@ -207,6 +207,8 @@ LAYER_CASES = [  # n, d, heads, inter, rot, qk_norm, qkv_bias, path
     (33, 96, 3, 160, 32, True, False, wq.PATH_MFMA_F32),
     (130, 256, 4, 512, 64, True, True, wq.PATH_AUTO),
     (12, 128, 1, 128, 128, True, False, wq.PATH_AUTO),   # n <= 16: the products take the f32 matvec
+    (50, 96, 3, 160, 32, True, True, wq.PATH_MFMA),       # d % 64 != 0: f32 hand-offs on the bf16 path
+    (200, 192, 3, 640, 64, False, True, wq.PATH_MFMA),    # bf16 hand-offs, 64 x 64 product tiles
 ]
 
 
@@ -282,3 +284,21 @@ def test_encoder_layer_workload_size():
     got = t.cpu().numpy()
     want, var = eb.layer_sigma(h, L, valid, heads, rot, True)
     assert_within(got, want, eb.sigma_tol(want, var), "encoder layer 1500x1024")
+
+    # The block hands its activations over in bf16 between its kernels; its steps called one by one
+    # (f32 hand-offs, other product tiles) give the same bits.
+    import torch
+    Ld = _layer_dev(L)
+    cs = wq.rope_table(n, rot).cuda()
+    hs = dev(h)
+    a = wq.layer_norm(hs, Ld["ln1"], d=d)
+    qkv = wq.gemm(a, Ld["qkv_w"], wq.W_BF16, m=3 * d, k=d, bias=Ld["qkv_b"], path=wq.PATH_MFMA)
+    wq.qk_norm_rope(qkv, cs, n=n, heads=heads, hd=d // heads, rot=rot, qn=Ld["qn"], kn=Ld["kn"])
+    att = wq.attention(qkv, dev(valid), n=n, heads=heads, hd=d // heads,
+                       scale=float(np.float32(1.0) / np.sqrt(np.float32(d // heads))))
+    wq.gemm(att, Ld["out_w"], wq.W_BF16, m=d, k=d, bias=Ld["out_b"], residual=True, out=hs, path=wq.PATH_MFMA)
+    a = wq.layer_norm(hs, Ld["ln2"], d=d)
+    f = wq.gemm(a, Ld["fc1_w"], wq.W_BF16, m=inter, k=d, bias=Ld["fc1_b"], gelu=True, path=wq.PATH_MFMA)
+    wq.gemm(f, Ld["fc2_w"], wq.W_BF16, m=d, k=inter, bias=Ld["fc2_b"], residual=True, out=hs, path=wq.PATH_MFMA)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(got, hs.cpu().numpy())
