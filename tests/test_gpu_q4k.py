@@ -253,3 +253,66 @@ def test_q4k_moe_16_tokens_top2_of_8_full():
         tol = B_F32 * s2 + 8 * 2.0 ** -24 * np.abs(y_ref)
         worst = max(worst, assert_within(got[:, rows], y_ref, tol, f"rows {r0}.."))
     print(f"Q4_K MoE 16 tok top-2 of 8: err/tol {worst:.3f}")
+
+
+# ---------------------------------------------------------------- seeded random sweep
+
+Q4K_K = [256, 512, 768, 1024, 1280, 2048, 2304, 2560, 3072, 4096, 5120, 8192, 9216]
+ACTS = [None, "gelu", "silu", "relu", "tanh"]
+ACT_FLAG = {None: 0, "gelu": 2, "silu": 8, "relu": 16, "tanh": 32}
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_q4k_random_layer(i):
+    g = np.random.default_rng(5000 + i)
+    k = int(g.choice(Q4K_K))
+    n = int(g.integers(1, 17))
+    m = int(g.integers(1, 300))
+    act = ACTS[int(g.integers(0, 5))]
+    bias_on, res_on = bool(g.integers(0, 2)), bool(g.integers(0, 2))
+    alpha = float(g.choice([1.0, 0.5, -1.25]))
+    dual = int(g.integers(0, m + 1)) if g.integers(0, 4) == 0 else 0
+    gs = synth.rng(5100, i)
+    x = synth.normal_f32(gs, (n, k), 1.0)
+    w = _weight(5200 + i, m, k)
+    bias = synth.normal_f32(gs, (m + dual,), 0.1) if bias_on else None
+    y_old = synth.normal_f32(gs, (n, m + dual), 1.0) if res_on else None
+    buf, out = guarded_out(n, m + dual, y_old)
+    wq.gemm(dev(x), dev(w), wq.W_Q4_K, m=m, k=k, bias=None if bias is None else dev(bias), act=act,
+            residual=res_on, out=out, alpha=alpha, dual=dual)
+    got = read_guarded(buf, n, m + dual)
+    flags = (wq.BIAS if bias_on else 0) | ACT_FLAG[act] | (wq.RESIDUAL if res_on else 0)
+    y_ref, _ = oracle.linear_dual(x, w, wq.W_Q4_K, m, k, dual, bias, flags, y_old, alpha=alpha)
+    v = None
+    if ACT_FLAG[act]:
+        v, _ = oracle.linear_dual(x, w, wq.W_Q4_K, m, k, dual, bias, flags & wq.BIAS)
+    S2 = oracle.q4_k_part_scale(x, w, m, k)
+    S2 = np.concatenate([S2, S2[:, :dual]], axis=1)
+    tol = tolerance(S2, y_ref, B_F32, flags, v, bias, y_old, alpha)
+    assert_within(got, y_ref, tol, f"case {i}: n={n} m={m} k={k} act={act} bias={bias_on} res={res_on} "
+                                   f"alpha={alpha} dual={dual}")
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_q4k_random_moe(i):
+    g = np.random.default_rng(6000 + i)
+    k = int(g.choice([256, 1024, 2048, 2304, 3072, 4096, 5120]))
+    n_exp = int(g.integers(1, 9))
+    top_k = int(g.integers(1, min(n_exp, 4) + 1))
+    n_tok = int(g.integers(1, 40))
+    m = int(g.integers(1, 200))
+    gated = bool(g.integers(0, 2))
+    gs = synth.rng(6100, i)
+    x = synth.normal_f32(gs, (n_tok, k), 1.0)
+    bank = np.stack([_weight(6200 + 16 * i + e, m, k) for e in range(n_exp)])
+    ids, gates = synth.moe_routing(gs, n_tok, n_exp, top_k)
+    rows = n_tok if gated else n_tok * top_k
+    buf, out = guarded_out(rows, m)
+    wq.moe_matvec(dev(x), dev(bank), wq.W_Q4_K, dev(ids), dev(gates) if gated else None, n_experts=n_exp, m=m, k=k,
+                  out=out)
+    got = read_guarded(buf, rows, m)
+    y_ref, _ = oracle.moe(x, bank, wq.W_Q4_K, ids, n_exp, m, k, gates if gated else None)
+    s2 = _moe_part_scale(x, bank, ids, m, k)
+    S2 = (np.abs(gates)[:, :, None] * s2).sum(axis=1) if gated else s2.reshape(n_tok * top_k, m)
+    assert_within(got, y_ref, B_F32 * S2 + 8 * 2.0 ** -24 * np.abs(y_ref),
+                  f"moe case {i}: n_tok={n_tok} n_exp={n_exp} top_k={top_k} m={m} k={k} gated={gated}")
