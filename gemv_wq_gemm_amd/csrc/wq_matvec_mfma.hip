@@ -395,25 +395,30 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
         const int slot_base = (tile % NSTAGE) * kSlotBytes;
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (WT == kQ4_K) {
-          static_assert(kSliceBlocks == 8, "a Q4_K slice is one super-block");
-          const uint4 h = *reinterpret_cast<const uint4*>(ring + slot_base + s_off);
-          const float d = f16_to_f32(h.x & 0xFFFFu), dmin = f16_to_f32(h.x >> 16);
+          static_assert(kSliceBlocks % 8 == 0, "a Q4_K slice is whole super-blocks");
           const float* xsw = xsum_lds + wave * kSliceBlocks * kSlots + 4 * o;
-          static_for<0, kSliceBlocks>([&](auto jj) {
-            constexpr int J = decltype(jj)::value;
-            const uint2 qd = *reinterpret_cast<const uint2*>(ring + slot_base + q_off + 32 * (J >> 1));
-            const bf16x8 wb = q4k_octet<4 * (J & 1)>(qd.x, qd.y);
-            const float2 f = q4k_factor<J>(h, d, dmin);
-            const float4 xsum = *reinterpret_cast<const float4*>(xsw + J * kSlots);
-            f32x4 blk = {0.f, 0.f, 0.f, 0.f};
-            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][J], wb, blk, 0, 0, 0);
-            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][J], wb, blk, 0, 0, 0);
-            blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2][J], wb, blk, 0, 0, 0);
-            acc[0] = __builtin_fmaf(f.x, blk[0], __builtin_fmaf(-f.y, xsum.x, acc[0]));
-            acc[1] = __builtin_fmaf(f.x, blk[1], __builtin_fmaf(-f.y, xsum.y, acc[1]));
-            acc[2] = __builtin_fmaf(f.x, blk[2], __builtin_fmaf(-f.y, xsum.z, acc[2]));
-            acc[3] = __builtin_fmaf(f.x, blk[3], __builtin_fmaf(-f.y, xsum.w, acc[3]));
-            if constexpr (J % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
+          static_for<0, kSliceBlocks / 8>([&](auto ss) {
+            constexpr int SS = decltype(ss)::value;  // super-block of the slice
+            const uint4 h = *reinterpret_cast<const uint4*>(ring + slot_base + s_off + SS * kQ4KBytes);
+            const float d = f16_to_f32(h.x & 0xFFFFu), dmin = f16_to_f32(h.x >> 16);
+            static_for<0, 8>([&](auto jj) {
+              constexpr int J = decltype(jj)::value;  // sub-block of the super-block
+              constexpr int B = 8 * SS + J;           // block of the slice
+              const uint2 qd =
+                  *reinterpret_cast<const uint2*>(ring + slot_base + q_off + SS * kQ4KBytes + 32 * (J >> 1));
+              const bf16x8 wb = q4k_octet<4 * (J & 1)>(qd.x, qd.y);
+              const float2 f = q4k_factor<J>(h, d, dmin);
+              const float4 xsum = *reinterpret_cast<const float4*>(xsw + B * kSlots);
+              f32x4 blk = {0.f, 0.f, 0.f, 0.f};
+              blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[0][B], wb, blk, 0, 0, 0);
+              blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[1][B], wb, blk, 0, 0, 0);
+              blk = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xa[2][B], wb, blk, 0, 0, 0);
+              acc[0] = __builtin_fmaf(f.x, blk[0], __builtin_fmaf(-f.y, xsum.x, acc[0]));
+              acc[1] = __builtin_fmaf(f.x, blk[1], __builtin_fmaf(-f.y, xsum.y, acc[1]));
+              acc[2] = __builtin_fmaf(f.x, blk[2], __builtin_fmaf(-f.y, xsum.z, acc[2]));
+              acc[3] = __builtin_fmaf(f.x, blk[3], __builtin_fmaf(-f.y, xsum.w, acc[3]));
+              if constexpr (J % kSchedBlocks == kSchedBlocks - 1) __builtin_amdgcn_sched_barrier(0);
+            });
           });
         } else {
         static_for<0, kSliceBlocks>([&](auto bb) {
@@ -499,7 +504,14 @@ hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stre
   // Both run a 2-slot ring (one tile in flight behind the one in use). For Q4_0 a third slot
   // measured 3-4% slower on the MoE workload (16 tokens, top-2 of 8 experts of 14336 x 4096).
   if (wtype == kQ8_0) return launch_mfma<kQ8_0, 2, 8, 1>(p, stream);
-  if (wtype == kQ4_K) return launch_mfma<kQ4_K, 2, 8, 2>(p, stream);
+  if (wtype == kQ4_K) {
+    // Q4_K holds a sub-block sum and scale per block beside the activation parts: with 256-element
+    // slices (16 waves, 128 VGPRs) it spills 56 bytes per lane; 512-element slices (8 waves, no
+    // spill) measured 4% faster on 16 tokens top-2 of 8 experts of 14336 x 4096 (92-93 against
+    // 96-97 us). k an odd multiple of 256 keeps the 256-element slices.
+    if (p.k % 512 == 0) return launch_mfma<kQ4_K, 2, 16, 2>(p, stream);
+    return launch_mfma<kQ4_K, 2, 8, 2>(p, stream);
+  }
   return launch_mfma<kQ4_0, 2, 8, 2>(p, stream);
 }
 
