@@ -744,6 +744,19 @@ def _cpu_configs(synth):
         w = oracle.decode(wk, oracle.W_Q4_K, 14336, 4096)
         np.asarray(xk, np.float64) @ w.T
     res["NEXT2_q4_k_14336x4096_n1"] = entry(_cpu_time(q4k, 3), 33030144, "the full call")
+    ids_k, _ = synth.moe_routing(synth.rng(0, 6, 5), 16, 8, 2)
+    xk16 = synth.normal_f32(synth.rng(0, 6, 4), (16, 4096), 1.0)
+    ek = list(np.unique(ids_k))[:2]
+    wks = {e: synth.q4_k_weight(synth.rng(0, 6, 3, 0, e), 14336, 4096) for e in ek}
+
+    def q4k_moe():
+        x64 = np.asarray(xk16, np.float64)
+        for e in ek:
+            w = oracle.decode(wks[e], oracle.W_Q4_K, 14336, 4096)
+            t_idx, _ = np.nonzero(ids_k == e)
+            x64[t_idx] @ w.T
+    res["NEXT2_moe_q4_k_16tok_top2_of_8"] = entry(_cpu_time(q4k_moe, 3), 2 * 33030144,
+                                                  f"experts {ek[0]} and {ek[1]} of the 8 (their routed tokens)")
     return res
 
 
