@@ -209,6 +209,8 @@ LAYER_CASES = [  # n, d, heads, inter, rot, qk_norm, qkv_bias, path
     (12, 128, 1, 128, 128, True, False, wq.PATH_AUTO),   # n <= 16: the products take the f32 matvec
     (50, 96, 3, 160, 32, True, True, wq.PATH_MFMA),       # d % 64 != 0: f32 hand-offs on the bf16 path
     (200, 192, 3, 640, 64, False, True, wq.PATH_MFMA),    # bf16 hand-offs, 64 x 64 product tiles
+    (10, 128, 2, 256, 32, True, False, wq.PATH_MFMA),     # bf16 hand-offs with fewer frames than a tile
+    (40, 192, 16, 256, 4, True, True, wq.PATH_MFMA),      # heads of 12 dims: element-wise bf16 stores
 ]
 
 
