@@ -20,7 +20,7 @@
 //  * Q4_K (hanzo-ml `matvec_q4k_gpu`; GGML's k-quant super-block of 256 weights in 144 bytes): the
 //    unsigned quants q (0..15) enter as they are, and each 32-element sub-block j adds
 //    d sc_j * (its MFMA sum of x q) - dmin m_j * (the sum of its activations), the activation sums
-//    being formed once per group of slots. A wave's slice (8 sub-blocks) is one super-block.
+//    being formed once per group of slots. A wave's slice is one or two whole super-blocks.
 //  * One 32-element block is one MFMA's k: three chained MFMAs (one per activation part, sharing
 //    the decoded weights) sum the block's products into a fresh 16x16 f32 tile, which the block's
 //    scale then multiplies and adds to the running sum in f32. So only f32 additions round: the
@@ -284,7 +284,8 @@ __global__ __launch_bounds__(64 * (kMaxK / (32 * SB))) void matvec_mfma_kernel(M
       const int slot = slot_lds[t];
       if (row < p.m && slot >= 0) {
         float v = 0.f;
-        // Not unrolled: this runs inside the tile loop, where registers are scarce.
+        // Not unrolled: this runs inside the tile loop, where registers are scarce (issuing the
+        // partials' reads four at a time measured no faster on the MoE workloads).
 #pragma unroll 1
         for (int w = 0; w < nw; ++w) v += part[buf][w * kPartWave + i];
         float* yp = p.y + static_cast<long long>(slot) * p.m + row;
