@@ -9,6 +9,7 @@
 // flag 1 exactly when a bias is given). Every check runs before any HIP call.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -575,8 +576,10 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   // bf16, rounded the same way: half the bytes, and the block's output is bit-identical. The
   // f32-accurate path, the matvec path (n <= 16) and the other weight types keep f32 hand-offs.
   const int gpath = path == WQ_PATH_AUTO ? (n <= WQ_MATVEC_MAX_N ? WQ_PATH_MATVEC : WQ_PATH_MFMA) : path;
+  // The bf16 products address their operands with 32-bit byte offsets (checked again by their
+  // launcher): every bf16 activation (n x d, n x inter) and weight under 4 GiB.
   const bool b16 = wtype == WQ_W_BF16 && gpath == WQ_PATH_MFMA && d % 64 == 0 && inter % 64 == 0 &&
-                   n * inter * 2 < (int64_t(1) << 32) && 3 * d * d * 2 < (int64_t(1) << 32) &&
+                   n * std::max(d, inter) * 2 < (int64_t(1) << 32) && 3 * d * d * 2 < (int64_t(1) << 32) &&
                    inter * d * 2 < (int64_t(1) << 32);
   hipStream_t hs = static_cast<hipStream_t>(stream);
   int r;
