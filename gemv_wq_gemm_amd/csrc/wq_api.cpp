@@ -136,9 +136,11 @@ int scratch_address(float** out) {
 
 // io (inside the library only): bit 0, x holds bf16 bit patterns; bit 1, y receives them. Both
 // take bf16 weights on the bf16 matrix-core path (which rounds X to bf16 anyway), and a bf16 y
-// takes no residual and no dual outputs.
+// takes no residual and no dual outputs. dry: run the checks only (a caller that launches several
+// steps checks them all before its first launch).
 int gemm_checked(const float* x, const void* w, int wtype, const float* bias, unsigned flags, float alpha,
-                 float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream, int io = 0) {
+                 float* y, int64_t n, int64_t m, int64_t k, int64_t dual, int path, void* stream, int io = 0,
+                 bool dry = false) {
   clear_error();
   if (int r = check_wtype(wtype)) return r;
   constexpr unsigned kActs = WQ_GELU | WQ_SILU | WQ_RELU | WQ_TANH;
@@ -175,6 +177,7 @@ int gemm_checked(const float* x, const void* w, int wtype, const float* bias, un
   if (overlap(y, ybytes, x, n * k * ((io & 1) ? 2 : 4)) || overlap(y, ybytes, w, wbytes) ||
       overlap(y, ybytes, bias, (m + dual) * 4))
     return fail(WQ_ERR_ALIAS, "y overlaps x, w or bias");
+  if (dry) return WQ_OK;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
@@ -581,8 +584,39 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   const bool b16 = wtype == WQ_W_BF16 && gpath == WQ_PATH_MFMA && d % 64 == 0 && inter % 64 == 0 &&
                    n * std::max(d, inter) * 2 < (int64_t(1) << 32) && 3 * d * d * 2 < (int64_t(1) << 32) &&
                    inter * d * 2 < (int64_t(1) << 32);
-  hipStream_t hs = static_cast<hipStream_t>(stream);
+  // Every step's checks run here, before the first launch, so a refused call leaves h as it was
+  // (only a launch that fails returns with h partly updated). The steps write h and the
+  // workspace; nothing they read may lie there.
+  const int64_t hbytes = n * d * 4;
+  auto outside = [&](const void* p, int64_t bytes) {
+    return !overlap(p, bytes, h, hbytes) && !overlap(p, bytes, workspace, w.total);
+  };
+  const float* vecs[] = {l->ln1, l->ln2, l->qkv_b, l->qn, l->kn, l->out_b, l->fc1_b, l->fc2_b};
+  const int64_t vbytes[] = {2 * d * 4, 2 * d * 4, 3 * d * 4, 2 * hd * 4, 2 * hd * 4, d * 4, inter * 4, d * 4};
+  for (int i = 0; i < 8; ++i) {
+    if (vecs[i] && !aligned(vecs[i], 4)) return fail(WQ_ERR_ALIGN, "the layer's vectors must be 4-byte aligned");
+    if (!outside(vecs[i], vbytes[i])) return fail(WQ_ERR_ALIAS, "a layer vector overlaps h or the workspace");
+  }
+  const void* mats[] = {l->qkv_w, l->out_w, l->fc1_w, l->fc2_w};
+  const int64_t mbytes[] = {wq_weight_bytes(wtype, 3 * d, d), wq_weight_bytes(wtype, d, d),
+                            wq_weight_bytes(wtype, inter, d), wq_weight_bytes(wtype, d, inter)};
+  for (int i = 0; i < 4; ++i)
+    if (!outside(mats[i], mbytes[i])) return fail(WQ_ERR_ALIAS, "a layer weight overlaps h or the workspace");
+  if (!outside(valid, n * 4) || (rot > 0 && !outside(cs, n * rot * 4)))
+    return fail(WQ_ERR_ALIAS, "valid or cs overlaps h or the workspace");
+  const int io_in = b16 ? 1 : 0;
   int r;
+  if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, gpath, stream,
+                        io_in, true)) ||
+      (r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, gpath, stream, io_in,
+                        true)) ||
+      (r = gemm_checked(a, l->fc1_w, wtype, l->fc1_b, WQ_BIAS | WQ_GELU, 1.0f, f, n, inter, d, 0, gpath, stream,
+                        b16 ? 3 : 0, true)) ||
+      (r = gemm_checked(f, l->fc2_w, wtype, l->fc2_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, inter, 0, gpath, stream,
+                        io_in, true)))
+    return r;
+
+  hipStream_t hs = static_cast<hipStream_t>(stream);
   auto norm = [&](const float* wb) -> int {
     if (!b16) return wq_layer_norm(h, wb, a, n, d, stream);
     clear_error();
@@ -592,7 +626,7 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
   };
   if ((r = norm(l->ln1))) return r;
   if ((r = gemm_checked(a, l->qkv_w, wtype, l->qkv_b, l->qkv_b ? WQ_BIAS : 0u, 1.0f, qkv, n, 3 * d, d, 0, gpath, stream,
-                        b16 ? 1 : 0)))
+                        io_in)))
     return r;
   // The q/k norm + rotation runs fused with the attention's pack: k goes to the workspace in bf16
   // only (the f32 rows are not needed after), q is rewritten in place as wq_qk_norm_rope would.
@@ -602,14 +636,14 @@ int wq_encoder_layer(const wq_encoder_layer_t* l, int wtype, float* h, const int
                                           hs, b16 ? 1 : 0);
   if (he != hipSuccess) return hip_fail(he, "q/k norm + attention launch");
   if ((r = gemm_checked(att, l->out_w, wtype, l->out_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, d, 0, gpath, stream,
-                        b16 ? 1 : 0)))
+                        io_in)))
     return r;
   if ((r = norm(l->ln2))) return r;
   if ((r = gemm_checked(a, l->fc1_w, wtype, l->fc1_b, WQ_BIAS | WQ_GELU, 1.0f, f, n, inter, d, 0, gpath, stream,
                         b16 ? 3 : 0)))
     return r;
   return gemm_checked(f, l->fc2_w, wtype, l->fc2_b, WQ_BIAS | WQ_RESIDUAL, 1.0f, h, n, d, inter, 0, gpath, stream,
-                      b16 ? 1 : 0);
+                      io_in);
 }
 
 const char* wq_last_error(void) { return g_err; }

@@ -392,7 +392,9 @@ int64_t wq_encoder_workspace_bytes(int64_t n, int64_t d, int64_t heads, int64_t 
  *   workspace  device, 256-byte aligned, >= wq_encoder_workspace_bytes(n, d, heads, inter).
  *   d % 32 == 0, inter % 32 == 0, d % heads == 0 with hd = d / heads <= 128, rot as for
  *   wq_qk_norm_rope, 0 <= n <= 2^22.
- * Returns the first failing step's code; h is then partly updated.
+ * Every step's argument checks run before the first launch, so a refused call leaves h as it
+ * was. The layer's weights and vectors, valid and cs must not overlap h or the workspace
+ * (WQ_ERR_ALIAS). Only a launch that fails (WQ_ERR_HIP) returns with h partly updated.
  */
 int wq_encoder_layer(const wq_encoder_layer_t* layer, int wtype, float* h, const int32_t* valid,
                      const float* cs, void* workspace, int64_t workspace_bytes, int64_t n, int64_t d,

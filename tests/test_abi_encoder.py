@@ -126,6 +126,29 @@ def test_encoder_layer_weight_checks():
     assert _layer(n=0, h=NULL, valid=NULL, ws=NULL, cs=NULL) == 0
 
 
+@pytest.mark.parametrize("desc_kw,kw,code", [
+    (dict(fc2_w=0x80000 + 8), {}, -5),        # the last product's weight, misaligned
+    (dict(qkv_b=0xA0002), {}, -5),            # a vector, misaligned
+    (dict(fc1_w=0x200000), {}, -6),           # a weight on h
+    (dict(out_b=0x1000000 + 1024), {}, -6),   # a vector inside the workspace
+    ({}, dict(valid=0x200000 + 8), -6),       # valid inside h
+    ({}, dict(cs=0x1000000), -6),             # cs on the workspace
+    ({}, dict(wtype=wq.W_Q4_K, d=256, inter=512), -3),  # Q4_K at n = 100: the products take n <= 16 only
+])
+def test_encoder_layer_checks_every_step_before_launching(desc_kw, kw, code):
+    """Each of these would be refused only at a later step if the steps were checked one at a
+    time; here the call is refused before the first launch (without a GPU a launch would return
+    WQ_ERR_HIP, -7), so h is left as it was."""
+    assert _layer(_layer_ptrs(**desc_kw), **kw) == code
+    assert wq.lib().wq_last_error().decode()
+
+
+def test_encoder_layer_valid_call_reaches_the_launch():
+    # Every check passes; the first launch then fails for want of a GPU.
+    assert _layer() == -7
+    assert "launch" in wq.lib().wq_last_error().decode().lower()
+
+
 def test_rope_table_argument_errors():
     buf = (ctypes.c_float * 16)()
     assert wq.lib().wq_rope_table(buf, 4, 3) == -2
