@@ -345,6 +345,27 @@ def _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic):
         others["encoder_chain_f32_accurate"] = {**st, "ms": round(st["median_us"] / 1e3, 4),
                                                 "TFLOP/s": round(flop_step / (st["median_us"] * 1e-6) / 1e12, 1),
                                                 "frac": round(flop_step / (st["median_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        # Calibration on the same GPU: the vendor GEMM (torch's bf16 linear, hipBLASLt) on the four
+        # layer shapes over the same 24 weights, given the easier problem: X already in bf16, no
+        # bias, activation or residual.
+        vendor = {}
+        for nm in ("qkv", "out", "fc1", "fc2"):
+            x_, m_, k_, _, _ = shapes[nm]
+            xv = x_.to(torch.bfloat16)
+            wv = [W_[nm][0].view(torch.bfloat16).view(m_, k_) for W_ in layers]
+            vendor[nm] = _stats(timer.runs(lambda i: torch.nn.functional.linear(xv, wv[i % len(wv)]), len(wv),
+                                           args.reps))
+            del xv, wv
+        vsum = sum(v["median_us"] for v in vendor.values())
+        others["vendor_gemm_bf16_same_shapes"] = {
+            "layers_us": {nm: v["median_us"] for nm, v in vendor.items()},
+            "layer_sum_us": round(vsum, 3),
+            "TFLOP/s": round(flop_layer / (vsum * 1e-6) / 1e12, 1),
+            "frac": round(flop_layer / (vsum * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "this_chain_layer_sum_us": round(sum(v["median_us"] for v in layer_us.values()), 3),
+            "note": "torch.nn.functional.linear in bf16 (hipBLASLt) with X converted to bf16 beforehand and no "
+                    "epilogue; this library's layers take f32 X and fuse bias, GELU and the residual",
+        }
     del layers, qkv, f, h
     torch.cuda.empty_cache()
 
