@@ -32,9 +32,12 @@ The same JSON line carries:
                 The rest of the encoder block adds LayerNorm 1500x1024, the q/k norm + rotation over
                 8 heads of 128 and attention (1500 frames, 100 masked) to rooflines, each with a CPU
                 baseline;
-  others        the chain on the f32-accurate matrix-core path, f16 weights at 4096x4096 n = 1,
-                the MLP-up shape with f16 / f32 / Q8_0 / Q4_0 weights, and the whole 24-block
-                encoder forward (every kernel of the block; CPU baseline: one block).
+  others        the chain on the f32-accurate matrix-core path, the vendor bf16 GEMM (torch's linear)
+                on the chain's four layer shapes as a same-GPU calibration, f16 weights at 4096x4096
+                n = 1, the MLP-up shape with f16 / f32 / Q8_0 / Q4_0 weights, and the whole 24-block
+                encoder forward (every kernel of the block; CPU baseline: one block);
+  context       the shader clock measured under load, the device's maximum clock attribute, and a
+                device-to-device copy rate.
 Weights of the matvec and MoE workloads rotate over copies of at least 600 MB, so the 256 MB
 Infinity Cache cannot serve them; the floors read the same amounts from rotating windows.
 """
@@ -222,6 +225,8 @@ def main():
         others.update(_others(torch, wq, synth, dev, timer, to_dev, args))
     if others:
         line["others"] = others
+    if not args.no_others and "others" in legs:
+        line["context"] = _context(torch, timer, dev, args)
 
     if not args.no_cpu_baseline:
         if acts is not None:
@@ -233,6 +238,42 @@ def main():
                 others[key]["cpu_baseline"] = cpu
 
     print(json.dumps(line), flush=True)
+
+
+def _context(torch, timer, dev, args):
+    """Secondary context for the figures above: the shader clock measured under load (libwq_bench.so's
+    probe: shader-clock cycles over wall-counter ticks on 4 workgroups per CU), the device's maximum
+    clock attribute, and a device-to-device copy rate."""
+    path = os.path.join(ROOT, "gemv_wq_gemm_amd", "libwq_bench.so")
+    lib = ctypes.CDLL(path)
+    lib.wq_bench_clock_probe.restype = ctypes.c_int
+    lib.wq_bench_clock_probe.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p]
+    wall_khz, max_khz = ctypes.c_int(0), ctypes.c_int(0)
+    lib.wq_bench_clock_rates(ctypes.byref(wall_khz), ctypes.byref(max_khz))
+    blocks = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    counts = torch.zeros(2 * blocks, dtype=torch.int64, device=dev)
+    sink = torch.zeros(256, dtype=torch.float32, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    for _ in range(3):  # the last run is read; the first ones bring the clock up
+        r = lib.wq_bench_clock_probe(200000, ctypes.c_void_p(counts.data_ptr()), ctypes.c_void_p(sink.data_ptr()),
+                                     blocks, stream)
+        if r != 0:
+            raise RuntimeError(f"clock probe launch failed: {r}")
+    c = counts.view(blocks, 2).cpu().numpy().astype(np.float64)
+    mhz = float(np.median(c[:, 0] / c[:, 1])) * wall_khz.value / 1e3 if wall_khz.value > 0 else None
+
+    nbytes = 512 * 2 ** 20
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    ms = timer.runs(lambda i: dst.copy_(src), 4, args.reps)
+    del src, dst
+    return {
+        "sclk_mhz_under_load": None if mhz is None else round(mhz, 1),
+        "sclk_mhz_max_attribute": round(max_khz.value / 1e3, 1),
+        "peaks_assume_mhz": 2400.0,
+        "d2d_copy_GBps": round(2 * nbytes / (float(np.median(ms)) * 1e-3) / 1e9, 1),
+        "d2d_copy_note": "torch copy_ of 512 MiB, read + written bytes over the median time",
+    }
 
 
 def _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic):

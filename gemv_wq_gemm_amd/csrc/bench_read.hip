@@ -76,9 +76,48 @@ __global__ __launch_bounds__(64 * kWaves) void stream_read_lds_kernel(const uint
   if (threadIdx.x == 0) out[blockIdx.x] = reinterpret_cast<const uint32_t*>(ring)[0];
 }
 
+// The shader clock under load: every workgroup runs `iters` dependent FMAs per lane between two
+// readings of the shader-clock counter (s_memtime) and of the constant-rate wall counter
+// (s_memrealtime); the bench turns each workgroup's cycle and tick counts into a clock rate.
+__global__ __launch_bounds__(kThreads) void clock_probe_kernel(int iters, float seed, unsigned long long* __restrict__ out,
+                                                                float* __restrict__ sink) {
+  const unsigned long long c0 = clock64();
+  const unsigned long long w0 = wall_clock64();
+  float a = seed + static_cast<float>(threadIdx.x);
+  for (int i = 0; i < iters; ++i) a = __builtin_fmaf(a, 1.0000001f, 1e-7f);
+  asm volatile("" ::"v"(a));  // the chain is done before the second reading
+  const unsigned long long c1 = clock64();
+  const unsigned long long w1 = wall_clock64();
+  if (threadIdx.x == 0) {
+    out[2 * blockIdx.x] = c1 - c0;
+    out[2 * blockIdx.x + 1] = w1 - w0;
+  }
+  if (a == -1.f) sink[threadIdx.x] = a;  // never true for these inputs; keeps the chain live
+}
+
 }  // namespace
 
 extern "C" {
+
+// Runs the clock probe on `blocks` workgroups: out receives 2 * blocks counts (shader-clock
+// cycles, wall-counter ticks per workgroup), sink 256 floats that stay unwritten.
+int wq_bench_clock_probe(int iters, uint64_t* out, float* sink, int blocks, void* stream) {
+  if (iters <= 0 || blocks <= 0 || !out || !sink) return static_cast<int>(hipErrorInvalidValue);
+  hipLaunchKernelGGL(clock_probe_kernel, dim3(blocks), dim3(kThreads), 0, static_cast<hipStream_t>(stream), iters, 1.f,
+                     reinterpret_cast<unsigned long long*>(out), sink);
+  return static_cast<int>(hipGetLastError());
+}
+
+// Rates of the wall counter and the device's maximum shader clock, in kHz (0 if unknown).
+int wq_bench_clock_rates(int* wall_khz, int* max_khz) {
+  int dev = 0;
+  *wall_khz = 0;
+  *max_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 1;
+  if (hipDeviceGetAttribute(wall_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) *wall_khz = 0;
+  if (hipDeviceGetAttribute(max_khz, hipDeviceAttributeClockRate, dev) != hipSuccess) *max_khz = 0;
+  return 0;
+}
 
 // The direct-to-LDS read of `bytes` (a multiple of 1024, buf 16-byte aligned); `blocks` workgroups.
 int wq_bench_stream_read_lds(const void* buf, int64_t bytes, uint32_t* out, int blocks, void* stream) {
