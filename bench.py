@@ -509,8 +509,17 @@ def _c3(torch, wq, synth, dev, timer, to_dev, R, out, floor, read_traffic):
     y = torch.empty((1, m), device=dev)
     gs = [wq.bind_gemm(x, W[i], wq.W_Q4_0, m=m, k=k, out=y) for i in range(nc)]
     st = _stats(timer.runs(lambda i: gs[i % nc](), 100, R))
-    out["C3_q4_0_14336x4096_n1"] = _hbm_entry(st, wb, floor.us(wb, R), read_traffic(COUNTERS, "q4_0_n1"),
-                                              extra={"copies": nc})
+    fl = floor.us(wb, R)
+    out["C3_q4_0_14336x4096_n1"] = _hbm_entry(st, wb, fl, read_traffic(COUNTERS, "q4_0_n1"), extra={"copies": nc})
+    # One GPU's share of the MoE workload split expert-parallel over 8 GPUs: one expert with its
+    # routed tokens (32 slots over 8 experts: 4 on average), the same matvec at n = 4.
+    x4 = to_dev(synth.normal_f32(synth.rng(0, 4, 7), (4, k), 1.0))
+    y4 = torch.empty((4, m), device=dev)
+    g4 = [wq.bind_gemm(x4, W[i], wq.W_Q4_0, m=m, k=k, out=y4) for i in range(nc)]
+    st4 = _stats(timer.runs(lambda i: g4[i % nc](), 100, R))
+    out["C3_q4_0_14336x4096_n4_expert_share"] = _hbm_entry(
+        st4, wb, fl, None, extra={"copies": nc, "note": "one expert with the 4 tokens it receives on average: "
+                                                          "the per-GPU share of the MoE workload split over 8 GPUs"})
     del W
 
 

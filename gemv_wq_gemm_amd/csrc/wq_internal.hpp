@@ -61,6 +61,9 @@ hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tokens
 // The matrix-core kernel for 2..16 tokens per pass and MoE (Q8_0 / Q4_0, k a multiple of 512
 // in 2048..4096), which launch_matvec prefers when it applies.
 bool matvec_mfma_supports(int wtype, int k);
+// Whether a plain call (no ids) of n tokens on m rows goes to the matrix-core kernel: from 9
+// tokens, and from 5 when the weight has at least two 16-row tiles per CU.
+bool matvec_mfma_takes_plain(int m, int n);
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream);
 
 // Q4_K weights (k a multiple of 256): the sliced kernel where it applies (no dual outputs), else

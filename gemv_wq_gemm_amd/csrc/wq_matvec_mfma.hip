@@ -500,6 +500,19 @@ bool matvec_mfma_supports(int wtype, int k) {
   return (wtype == kQ8_0 || wtype == kQ4_0) && k % 512 == 0 && k >= 2048 && k <= kMaxK;
 }
 
+// From 5 to 8 tokens the f32 FMA kernel runs its 8-token variant, which spends more per weight
+// than the matrix cores once every CU has two or more 16-row tiles to walk (the activation parts
+// are then built once for several tiles). Measured on MI355X, plain calls at n = 5 and 8,
+// matrix cores against the FMA kernel: Q4_0 14336 x 4096 18.8 / 19.7 against 25.8 / 27.8 us,
+// Q4_0 8192 x 4096 14.7 / 15.7 against 16.9 / 18.0, Q8_0 8192 x 4096 14.4 / 15.2 against
+// 19.2 / 19.7, Q8_0 8192 x 2048 10.1 / 10.5 against 12.3 / 12.5, Q4_0 14336 x 2048 13.4 / 14.1
+// against 17.1 / 18.4. With one tile per CU (4096 rows), or up to 4 tokens on the larger weights,
+// the FMA kernels were as fast or faster (Q4_0 14336 x 4096 at n = 4: 18.6 against 18.9 us).
+bool matvec_mfma_takes_plain(int m, int n) {
+  if (n > 8) return true;
+  return n >= 5 && (m + kTileRows - 1) / kTileRows >= 2 * mfma_device_cus();
+}
+
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream) {
   if (!matvec_mfma_supports(wtype, p.k) || (p.ids == nullptr && p.n_exp != 1)) return hipErrorInvalidValue;
   // Both run a 2-slot ring (one tile in flight behind the one in use). For Q4_0 a third slot

@@ -105,6 +105,21 @@ def test_matvec_matrix_core_route_every_flag(wtype, n, flags):
     assert_within(got, y_ref, tol, f"matrix-core matvec wtype={wtype} n={n} flags={flags}")
 
 
+@pytest.mark.parametrize("wtype", [wq.W_Q8_0, wq.W_Q4_0])
+@pytest.mark.parametrize("n,m", [(5, 8192), (8, 8192), (5, 8176), (4, 8192)])
+def test_matvec_route_boundary_on_wide_weights(wtype, n, m):
+    """Plain calls of 5-8 tokens on weights with at least two 16-row tiles per CU (8192 rows on
+    256 CUs) take the matrix-core kernel; 8176 rows (one tile short) and 4 tokens stay on the f32
+    FMA kernel. Both sides of the boundary, every output, against the oracle."""
+    k = 2048
+    flags = 7 if n == 8 else 1
+    print(f"wide-weight route wtype={wtype} n={n} m={m}", flush=True)
+    x, w, bias, y_old = _inputs(17, wtype, n, m, k, flags)
+    got = _run(x, w, wtype, m, k, bias, flags, y_old, wq.PATH_AUTO)
+    y_ref, tol = oracle_with_tol(x, w, wtype, m, k, bias, flags, y_old, B_F32)
+    assert_within(got, y_ref, tol, f"wide-weight route wtype={wtype} n={n} m={m}")
+
+
 # ---------------------------------------------------------------- MFMA path (bf16 x, exact w)
 
 GEMM_SHAPES = [(17, 1, 32), (64, 37, 96), (130, 128, 256), (200, 288, 160), (257, 130, 1024)]
