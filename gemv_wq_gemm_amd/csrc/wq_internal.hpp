@@ -62,8 +62,8 @@ hipError_t launch_matvec_sliced(int wtype, const MatvecParams& p, int max_tokens
 // in 2048..4096), which launch_matvec prefers when it applies.
 bool matvec_mfma_supports(int wtype, int k);
 // Whether a plain call (no ids) of n tokens on m rows goes to the matrix-core kernel: from 9
-// tokens, and from 5 when the weight has at least two 16-row tiles per CU.
-bool matvec_mfma_takes_plain(int m, int n);
+// tokens, and from 5 when the weight has at least two 16-row tiles per CU (three for Q4_K).
+bool matvec_mfma_takes_plain(int wtype, int m, int n);
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream);
 
 // Q4_K weights (k a multiple of 256): the sliced kernel where it applies (no dual outputs), else

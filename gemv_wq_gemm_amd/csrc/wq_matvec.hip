@@ -394,14 +394,14 @@ hipError_t launch_matvec(int wtype, const MatvecParams& p, int max_tok, hipStrea
   // or more slots per expert the matrix cores win, 4 tokens 52.8 against 56.7 us). The plain layer
   // takes the matrix cores from 9 tokens, where the f32 FMA kernels would stream the weights twice
   // (one pass for up to 16, measured 20.9 -> 16.3 us for Q8_0 4096 x 4096 at n = 16), and from 5
-  // tokens on weights with at least two 16-row tiles per CU (matvec_mfma_takes_plain).
+  // tokens on weights with at least two (Q4_K three) 16-row tiles per CU (matvec_mfma_takes_plain).
   // Dual outputs (wavo `Linear.dual`) are stored by this file's general kernel only: the sliced
   // and matrix-core kernels keep one output per row, since even a skipped second store in their
   // flush measured 12% slower on Q4_0 14336 x 4096 at n = 1.
   if (wtype == kQ4_K) return launch_matvec_q4k(p, max_tok, stream);
   const bool dual = p.dual > 0;
   if (!dual && matvec_mfma_supports(wtype, p.k) &&
-      (p.ids != nullptr ? max_tok > 1 : matvec_mfma_takes_plain(p.m, max_tok)))
+      (p.ids != nullptr ? max_tok > 1 : matvec_mfma_takes_plain(wtype, p.m, max_tok)))
     return launch_matvec_mfma(wtype, p, stream);
   if (!dual && matvec_sliced_supports(p.k)) return launch_matvec_sliced(wtype, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;

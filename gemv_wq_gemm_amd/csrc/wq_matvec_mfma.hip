@@ -508,9 +508,13 @@ bool matvec_mfma_supports(int wtype, int k) {
 // 19.2 / 19.7, Q8_0 8192 x 2048 10.1 / 10.5 against 12.3 / 12.5, Q4_0 14336 x 2048 13.4 / 14.1
 // against 17.1 / 18.4. With one tile per CU (4096 rows), or up to 4 tokens on the larger weights,
 // the FMA kernels were as fast or faster (Q4_0 14336 x 4096 at n = 4: 18.6 against 18.9 us).
-bool matvec_mfma_takes_plain(int m, int n) {
+// Q4_K's decode costs the matrix-core kernel more (a scale, a min and an activation sum per
+// sub-block), so it needs three tiles per CU: 14336 x 4096 at n = 5 / 8 21.6 / 23.8 against
+// 25.9 / 26.6 us, but 8192 x 4096 17.0 / 19.2 against 16.9 / 17.7 us.
+bool matvec_mfma_takes_plain(int wtype, int m, int n) {
   if (n > 8) return true;
-  return n >= 5 && (m + kTileRows - 1) / kTileRows >= 2 * mfma_device_cus();
+  const int per_cu = wtype == kQ4_K ? 3 : 2;
+  return n >= 5 && (m + kTileRows - 1) / kTileRows >= per_cu * mfma_device_cus();
 }
 
 hipError_t launch_matvec_mfma(int wtype, const MatvecParams& p, hipStream_t stream) {

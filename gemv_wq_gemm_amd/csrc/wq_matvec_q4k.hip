@@ -248,10 +248,11 @@ __global__ __launch_bounds__(256) void dequantize_q4k_kernel(const uint8_t* w, f
 
 hipError_t launch_matvec_q4k(const MatvecParams& p, int max_tok, hipStream_t stream) {
   if (p.k % kQ4KElems != 0) return hipErrorInvalidValue;
-  // As for the other quantized types: the matrix cores for MoE with two or more slots per expert
-  // and for 9 to 16 tokens (every weight decoded once for up to 16 slots), the sliced f32 kernel
-  // for 1 to 8 tokens.
-  if (p.dual == 0 && matvec_mfma_supports(kQ4_K, p.k) && ((p.ids != nullptr && max_tok > 1) || max_tok > 8))
+  // As for the other quantized types: the matrix cores for MoE with two or more slots per expert,
+  // for 9 to 16 tokens (every weight decoded once for up to 16 slots) and for 5 to 8 on weights
+  // with three or more 16-row tiles per CU (matvec_mfma_takes_plain); else the sliced f32 kernel.
+  if (p.dual == 0 && matvec_mfma_supports(kQ4_K, p.k) &&
+      (p.ids != nullptr ? max_tok > 1 : matvec_mfma_takes_plain(kQ4_K, p.m, max_tok)))
     return launch_matvec_mfma(kQ4_K, p, stream);
   if (p.dual == 0 && matvec_sliced_supports(p.k)) return launch_matvec_sliced(kQ4_K, p, max_tok, stream);
   const int n_exp_rows = p.ids ? p.n_exp + 1 : 1;

@@ -82,6 +82,24 @@ def test_q4k_layer_parity(n, k):
     print(f"Q4_K n={n} k={k}: err/tol {r:.3f}, err/(1e-5 S) {literal_ratio(got, y_ref, S, B_F32):.3f}")
 
 
+@pytest.mark.parametrize("n,m", [(5, 12288), (8, 12288), (5, 12272), (4, 12288)])
+def test_q4k_route_boundary_on_wide_weights(n, m):
+    """Plain calls of 5-8 tokens on Q4_K weights with at least three 16-row tiles per CU (12288
+    rows on 256 CUs) take the matrix-core kernel; 12272 rows (one tile short) and 4 tokens stay on
+    the sliced kernel. Both sides, every output, against the oracle."""
+    k = 2048
+    print(f"Q4_K wide-weight route n={n} m={m}", flush=True)
+    g = synth.rng(79, n, m)
+    x = synth.normal_f32(g, (n, k), 1.0)
+    w = _weight(80, m, k)
+    bias = synth.normal_f32(g, (m,), 0.1)
+    buf, out = guarded_out(n, m)
+    wq.gemm(dev(x), dev(w), wq.W_Q4_K, m=m, k=k, bias=dev(bias), out=out)
+    got = read_guarded(buf, n, m)
+    y_ref, _, tol = _ref_tol(x, w, m, k, bias, wq.BIAS)
+    assert_within(got, y_ref, tol, f"Q4_K wide-weight route n={n} m={m}")
+
+
 @pytest.mark.parametrize("k", [2560, 4096])
 @pytest.mark.parametrize("flags", [wq.BIAS, wq.BIAS | wq.GELU, wq.RESIDUAL, wq.BIAS | wq.GELU | wq.RESIDUAL])
 @pytest.mark.parametrize("n", [1, 4, 13])
