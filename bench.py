@@ -334,8 +334,10 @@ def _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic):
     x_, m_, k_, _, kw_ = shapes[dom]
     dom_flop = 2 * n * m_ * k_
     dom_tflops = dom_flop / (layer_us[dom]["median_us"] * 1e-6) / 1e12
-    dom_kernels = {"qkv": "gemm_bf16_kernel<64, 192, 2, 2, 2, 64, false, false, false>", "out": "gemm_bf16_kernel<64, 64, 2, 2, 3, 64, false, false, false>",
-                   "fc1": "gemm_bf16_kernel<64, 128, 2, 4, 2, 64, false, false, false>", "fc2": "gemm_bf16_kernel<64, 128, 2, 4, 4, 64, false, false, false>"}
+    dom_kernels = {"qkv": "gemm_bf16_kernel<64, 192, 2, 2, 2, 64, false, false, false, false>",
+                   "out": "gemm_bf16_kernel<64, 64, 2, 2, 3, 64, false, false, false, false>",
+                   "fc1": "gemm_bf16_kernel<64, 128, 2, 4, 2, 64, false, false, false, true>",
+                   "fc2": "gemm_bf16_kernel<64, 128, 2, 4, 4, 64, false, false, false, false>"}
     traffic = read_traffic(COUNTERS, f"gemm_{dom}")
 
     line = {

@@ -499,22 +499,31 @@ __device__ __forceinline__ int w_swizzle(int r) {
 // XB: X arrives as bf16 bit patterns (a producer already rounded it), staged like W. YB: outputs
 // are stored as bf16 bit patterns, rounded to nearest even (no residual, no dual outputs): the
 // encoder block hands activations from one product to the next that way, since the next product
-// rounds them to bf16 anyway.
-template <int BM, int BN, int WM, int WN, int NSTAGE, int BK, bool SPLIT, bool XB = false, bool YB = false>
+// rounds them to bf16 anyway. XR: f32 X arrives by register loads and is rounded to bf16 (nearest
+// even, as at fragment reads) once per element as it is written to LDS, in XB's layout; W keeps
+// its direct-to-LDS loads. Half the LDS bytes and reads of X, no rounding in every reading wave,
+// the same products and sums as the f32 staging (2-slot ring only).
+template <int BM, int BN, int WM, int WN, int NSTAGE, int BK, bool SPLIT, bool XB = false, bool YB = false,
+          bool XR = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, int tiles_m, int tiles_n, int band) {
   static_assert(BK == 32 || BK == 64, "k step");
   static_assert(!(SPLIT && (XB || YB)), "the f32-accurate path takes f32 X and Y");
+  static_assert(!XR || (!XB && !SPLIT && NSTAGE == 2 && BK == 64), "X rounded once: f32 X, 2-slot ring");
   constexpr int kXC = BK / 4, kWC = BK / 8;  // 16-byte chunks per X row and per W row
   constexpr int kWaves = WM * WN;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
-  constexpr int kABytes = BM * BK * (XB ? 2 : 4);  // f32 (bf16 when XB)
+  constexpr bool kXb16 = XB || XR;                  // X sits in LDS as bf16
+  constexpr int kABytes = BM * BK * (kXb16 ? 2 : 4);  // f32 (bf16 when XB or XR)
   constexpr int kBBytes = BN * BK * 2;  // bf16
   constexpr int kStageBytes = kABytes + kBBytes;
-  constexpr int kAInst = kABytes / 1024 / kWaves;  // direct-to-LDS loads per wave per step
+  // XR: X arrives by register loads (kXI 16-byte f32 chunks per thread per step), rounded once.
+  constexpr int kXI = XR ? BM * BK * 4 / 16 / (64 * kWaves) : 0;
+  static_assert(!XR || (BM * BK * 4 / 16) % (64 * kWaves) == 0, "X chunks must split evenly");
+  constexpr int kAInst = XR ? 0 : kABytes / 1024 / kWaves;  // direct-to-LDS loads per wave per step
   constexpr int kBInst = kBBytes / 1024 / kWaves;
   constexpr int kInst = kAInst + kBInst;
   constexpr int P = NSTAGE - 1;  // steps in flight
-  static_assert(kABytes % (1024 * kWaves) == 0 && kBBytes % (1024 * kWaves) == 0, "step must split evenly");
+  static_assert((XR || kABytes % (1024 * kWaves) == 0) && kBBytes % (1024 * kWaves) == 0, "step must split evenly");
   static_assert(kInst * (P - 1) < 64, "vmcnt range");
 
   __shared__ __attribute__((aligned(1024))) uint8_t ring[NSTAGE * kStageBytes];
@@ -543,7 +552,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
   const int nk = p.k / BK;
 
   // Per-lane source offsets (bytes) of this wave's direct-to-LDS loads, for k step 0.
-  uint32_t aoff[kAInst], boff[kBInst];
+  uint32_t aoff[kAInst > 0 ? kAInst : 1], boff[kBInst];
 #pragma unroll
   for (int i = 0; i < kAInst; ++i) {
     const int L = (wave * kAInst + i) * 64 + lane;  // 16-byte chunk index in a step's X region
@@ -565,6 +574,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
     boff[i] = static_cast<uint32_t>(min(m0 + r, p.m - 1)) * static_cast<uint32_t>(p.rowbytes) + c * 16u;
   }
   const uint32_t ring_lds = lds_address(ring);
+  // XR: chunk L = i * threads + tid of a step's BM x BK f32 block (row L / kXC, four values at
+  // column 4 (L % kXC)); its bf16 goes to the XB layout (rows of 2 BK bytes, swizzled as W's).
+  uint32_t xoff[kXI > 0 ? kXI : 1];
+  int xdst[kXI > 0 ? kXI : 1];
+#pragma unroll
+  for (int i = 0; i < kXI; ++i) {
+    const int L = i * 64 * kWaves + tid;
+    const int r = L / kXC, c4 = L % kXC;
+    xoff[i] = static_cast<uint32_t>(min(n0 + r, p.n - 1)) * static_cast<uint32_t>(p.k) * 4u + c4 * 16u;
+    xdst[i] = r * BK * 2 + (((c4 >> 1) ^ w_swizzle<BK>(r)) << 4) + (c4 & 1) * 8;
+  }
 
   auto issue = [&](int s) {
     const uint32_t lst = ring_lds + (s % NSTAGE) * kStageBytes;
@@ -594,17 +614,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
     bias_v[j] = (p.flags & kEpiBias) ? p.bias[col] : 0.f;
   }
 
-  // Prologue: steps 0..P-1 in flight.
-#pragma unroll
-  for (int s = 0; s < P; ++s)
-    if (s < nk) issue(s);
-
-  for (int s = 0; s < nk; ++s) {
-    // Wait for this wave's loads of step s: those of the later steps issued so far stay outstanding.
-    wait_groups<kInst, P - 1>(min(P - 1, nk - 1 - s));
-    __syncthreads();  // every wave's step-s data is in LDS; the slot of step s-1 is free
-    if (s + P < nk) issue(s + P);
-
+  // The k step s from ring slot s % NSTAGE.
+  auto compute = [&](int s) {
     const uint8_t* st = ring + (s % NSTAGE) * kStageBytes;
     const float* sa = reinterpret_cast<const float*>(st);
     const __bf16* sb = reinterpret_cast<const __bf16*>(st + kABytes);
@@ -616,7 +627,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int r = wm * TM + i * 32 + frow;
-        if constexpr (XB) {
+        if constexpr (kXb16) {
           const int c = 2 * ks + khalf;
           fa[slot][i] = *reinterpret_cast<const bf16x8*>(sab + r * BK + ((c ^ w_swizzle<BK>(r)) << 3));
         } else {
@@ -650,7 +661,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
           a[i] = __builtin_bit_cast(bf16x8, make_uint4(l1.x, l1.y, h1.x, h1.y));
           am[i] = __builtin_bit_cast(bf16x8, make_uint4(l2.x, l2.y, h2.x, h2.y));
           al[i] = __builtin_bit_cast(bf16x8, make_uint4(l3.x, l3.y, h3.x, h3.y));
-        } else if constexpr (XB) {
+        } else if constexpr (kXb16) {
           a[i] = fa[slot][i];
         } else {
           const uint2 l2 = round_bf16x4(ra[slot][i][0]), h2 = round_bf16x4(ra[slot][i][1]);
@@ -672,6 +683,53 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(GemmParams p, i
           }
       }
       if (ks + 2 < BK / 16) read_frags(ks + 2, slot);
+    }
+  };
+
+  if constexpr (XR) {
+    // X by register loads, rounded to bf16 once per element as it is written to LDS; W by
+    // direct-to-LDS loads. Iteration s: wait for this wave's W of step s (only the X loads of step
+    // s + 1, issued after it, stay outstanding), barrier, write X of step s + 1 (its loads are then
+    // the only ones in flight, so the compiler's wait for them is exact) and issue W of step s + 1
+    // into the slot step s - 1 used, load X of step s + 2 into registers, compute step s.
+    float4 xr[kXI > 0 ? kXI : 1];
+    auto xload = [&](int s) {
+#pragma unroll
+      for (int i = 0; i < kXI; ++i)
+        xr[i] = *reinterpret_cast<const float4*>(reinterpret_cast<const uint8_t*>(p.x) + xoff[i] + s * (BK * 4u));
+    };
+    auto xstore = [&](int s) {
+      uint8_t* dst = ring + (s % NSTAGE) * kStageBytes;
+#pragma unroll
+      for (int i = 0; i < kXI; ++i) *reinterpret_cast<uint2*>(dst + xdst[i]) = round_bf16x4(xr[i]);
+    };
+    issue(0);
+    xload(0);
+    xstore(0);
+    if (nk > 1) xload(1);
+    for (int s = 0; s < nk; ++s) {
+      if (s + 1 < nk) wait_vmcnt<kXI>();
+      else wait_vmcnt<0>();
+      __syncthreads();  // X and W of step s are in LDS; the slot of step s - 1 is free
+      if (s + 1 < nk) {
+        xstore(s + 1);
+        issue(s + 1);
+      }
+      if (s + 2 < nk) xload(s + 2);
+      compute(s);
+    }
+  } else {
+    // Prologue: steps 0..P-1 in flight.
+#pragma unroll
+    for (int s = 0; s < P; ++s)
+      if (s < nk) issue(s);
+
+    for (int s = 0; s < nk; ++s) {
+      // Wait for this wave's loads of step s: those of the later steps issued so far stay outstanding.
+      wait_groups<kInst, P - 1>(min(P - 1, nk - 1 - s));
+      __syncthreads();  // every wave's step-s data is in LDS; the slot of step s-1 is free
+      if (s + P < nk) issue(s + P);
+      compute(s);
     }
   }
 
@@ -860,8 +918,22 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t stream) {
   const int per_xcd = (tiles_m * tiles_n + 7) / 8;
   auto kernel = p.x_parts == 3 ? gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK, true>
                                : gemm_bf16_kernel<BM, BN, WM, WN, NSTAGE, BK, false>;
+
   hipLaunchKernelGGL(kernel, dim3(per_xcd * 8), dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n,
                      tile_band(tiles_m, per_xcd));
+  return hipGetLastError();
+}
+
+// The same tiles with X rounded once as it is staged (XR, 2-slot ring) on the plain path; the
+// f32-accurate path keeps the direct-to-LDS kernel.
+template <int BM, int BN, int WM, int WN>
+hipError_t launch_bf16_xr(const GemmParams& p, hipStream_t stream) {
+  if (p.x_parts == 3) return launch_bf16<BM, BN, WM, WN, 2, 64>(p, stream);
+  const int tiles_m = (p.n + BM - 1) / BM;
+  const int tiles_n = (p.m + BN - 1) / BN;
+  const int per_xcd = (tiles_m * tiles_n + 7) / 8;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, 2, 64, false, false, false, true>), dim3(per_xcd * 8),
+                     dim3(64 * WM * WN), 0, stream, p, tiles_m, tiles_n, tile_band(tiles_m, per_xcd));
   return hipGetLastError();
 }
 
@@ -921,7 +993,11 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
       //    tile's epilogue and stores overlap the other's k loop. A round is two tiles per CU:
       //    64 x 128 tiles when they fit one round or 64 x 192 tiles do not either, else 64 x 192
       //    tiles of 4 waves (one round instead of a thin second one: 1500 x 3072 x 1024
-      //    26.5 -> 19.1 us);
+      //    26.5 -> 19.1 us). With more than two 64 x 128 tiles per CU, X is rounded once as it
+      //    is staged (XR): 48 KB of LDS per workgroup instead of 64 KB, so three fit on a CU
+      //    (1500 x 4096 x 1024 + GELU 30.5 -> 27.0 us, 1500 x 4096 x 4096 91.5 -> 82.9 us); with
+      //    up to two per CU the f32 staging was as fast or faster (2048^3 31.4 both,
+      //    1500 x 2048 x 1024 15.6 against 17.4 us);
       //  * fewer: 64 x 64 tiles of 4 waves when the tiles are very few or k is short (more
       //    tiles in flight), else 64 x 128 tiles with a 4-slot ring.
       const int cus = device_cus();
@@ -929,6 +1005,7 @@ hipError_t launch_wt(const GemmParams& p, hipStream_t stream) {
       const long long tall_tiles = static_cast<long long>((p.n + 63) / 64) * ((p.m + 191) / 192);
       if (wide_tiles >= cus) return launch_bf16<128, 256, 2, 4, 2, 64>(p, stream);
       if (small_tiles > 2LL * cus && tall_tiles <= 2LL * cus) return launch_bf16<64, 192, 2, 2, 2, 64>(p, stream);
+      if (small_tiles > 2LL * cus) return launch_bf16_xr<64, 128, 2, 4>(p, stream);
       if (small_tiles > cus) return launch_bf16<64, 128, 2, 4, 2, 64>(p, stream);
       if (small_tiles <= cus / 2 || p.k <= 1024) {
         // At most four k steps: a 2-slot ring (64 x 256 x 256 + bias + GELU 5.4 -> 5.0 us). At
