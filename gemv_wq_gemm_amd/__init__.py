@@ -177,13 +177,14 @@ def gemm(x, w, wtype: int, *, m: int, k: int, bias=None, gelu: bool = False, res
 
 
 class BoundGemm:
-    """One ``wq_linear`` call with every argument resolved up front.
+    """One ``wq_linear`` (or ``wq_layer_norm``) call with every argument resolved up front.
 
     For loops that call the same layer on the same buffers again and again (a
     timing loop, a decode step): calling the object costs one ctypes call, with
-    no tensor inspection. The tensors given to :func:`bind_gemm` must stay alive
-    and in place for as long as the object is used, and the stream it was bound
-    to must still be the one to launch on.
+    no tensor inspection. The tensors given to :func:`bind_gemm` or
+    :func:`bind_layer_norm` must stay alive and in place for as long as the
+    object is used, and the stream it was bound to must still be the one to
+    launch on.
     """
 
     def __init__(self, fn, args):
@@ -287,6 +288,15 @@ def layer_norm(x, wb, *, d: int, out=None):
         out = torch.empty((n, d), dtype=torch.float32, device=x.device)
     _check(lib().wq_layer_norm(_f32(x, "x"), _f32(wb, "wb", 2 * d), _f32(out, "out", n * d), n, d, _stream()))
     return out
+
+
+def bind_layer_norm(x, wb, *, d: int, out) -> BoundGemm:
+    """Checks the arguments as :func:`layer_norm` does and returns the bound call."""
+    n = x.numel() // d
+    if x.numel() != n * d:
+        raise ValueError("x must hold n*d elements")
+    args = (_f32(x, "x"), _f32(wb, "wb", 2 * d), _f32(out, "out", n * d), n, d, _stream())
+    return BoundGemm(lib().wq_layer_norm, args)
 
 
 def rope_table(n: int, rot: int):

@@ -62,6 +62,23 @@ def test_layer_norm_in_place_and_unaligned(n, d):
     assert math.isnan(o[0].item())
 
 
+def test_bound_layer_norm_equals_the_plain_call():
+    """The bound call (arguments marshalled once) launches the same kernel on the same buffers."""
+    n, d = 1500, 1024
+    g = synth.rng(402, n, d)
+    x = _rows(g, n, d)
+    wb = synth.layer_norm_weights(g, d)
+    xt, wbt = dev(x), dev(wb)
+    buf, out = guarded_out(n, d)
+    call = wq.bind_layer_norm(xt, wbt, d=d, out=out)
+    for _ in range(3):
+        call()
+    got = read_guarded(buf, n, d)
+    plain = wq.layer_norm(xt, wbt, d=d).cpu().numpy()
+    assert np.array_equal(got, plain)
+    assert_within(got, enc.layer_norm(x, wb), eb.ln_tol(x, wb), "bound layer norm")
+
+
 # ---------------------------------------------------------------- q/k norm + rotation
 
 QK_CASES = [  # n, heads, hd, rot, norm
