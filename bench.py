@@ -83,12 +83,22 @@ class Timer:
         self.torch = torch
         self.stream = torch.cuda.current_stream()
 
-    def runs(self, fn, calls, reps, warm=2):
-        """ms per call of each of `reps` runs of `calls` back-to-back calls."""
+    def runs(self, fn, calls, reps, warm=2, warm_ms=30.0):
+        """ms per call of each of `reps` runs of `calls` back-to-back calls, after `warm` calls and
+        then whole runs until the GPU has been busy for `warm_ms`: after the host-side set-up of a
+        workload, memory-bound calls run up to 20% slower for their first few milliseconds (the MoE
+        workload: 80-90 us for about 100 calls, then 72-75 us)."""
         torch = self.torch
         for i in range(warm):
             fn(i)
         torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        i = warm
+        while (time.perf_counter() - t0) * 1e3 < warm_ms:
+            for _ in range(calls):
+                fn(i)
+                i += 1
+            torch.cuda.synchronize()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         i = 0
         ev[0].record(self.stream)
