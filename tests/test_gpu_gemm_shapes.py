@@ -20,6 +20,10 @@ SHAPES = [
     (300, 700, 4096),     # few tiles, long k, ragged in both
     (129, 257, 8192),     # one tile row and column past a tile edge, longest k
     (700, 520, 2048),
+    (1500, 4096, 1024),   # the MLP up projection: X rounded to bf16 once as it is staged
+    (1480, 4200, 512),    # the same route, ragged in n and m
+    (1500, 1024, 4096),   # the MLP down projection: 64 x 128 tiles with a 4-slot ring
+    (1500, 2048, 1024),   # 64 x 128 tiles two per CU, 2-slot ring
 ]
 
 FLAGS = [wq.BIAS, wq.BIAS | wq.GELU, wq.BIAS | wq.RESIDUAL, wq.RESIDUAL, wq.BIAS | wq.SILU | wq.RESIDUAL,
