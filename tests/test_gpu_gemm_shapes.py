@@ -80,9 +80,8 @@ def test_gemm_shape_f32_accurate(n, m, k):
     assert_within(got[:, cols], y_ref, tol, f"f32-accurate {n}x{m}x{k}")
 
 
-def test_bf16_gemm_is_deterministic():
-    n, m, k = 1500, 1024, 4096
-    flags = wq.BIAS | wq.RESIDUAL
+@pytest.mark.parametrize("n,m,k,flags", [(1500, 1024, 4096, wq.BIAS | wq.RESIDUAL), (1500, 4096, 1024, wq.BIAS | wq.GELU)])
+def test_bf16_gemm_is_deterministic(n, m, k, flags):
     x, w, bias, y_old = _inputs(n, m, k, flags, seed=2)
     first = _run(x, w, m, k, bias, flags, y_old, wq.PATH_MFMA)
     for _ in range(3):
