@@ -361,7 +361,8 @@ def _chain(torch, wq, synth, dev, timer, to_dev, args, props, read_traffic):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 x bf16 -> f32 (f32 activations rounded to bf16, bf16 weights as stored)",
+        "dtype": "bf16",
+        "arithmetic": "bf16 x bf16 -> f32 on the matrix cores (f32 activations rounded to bf16, bf16 weights as stored)",
         "data": "synthetic",
         "config": {
             "workload": "encoder GEMM chain: 24 layers x {QKV 1500x3072x1024 +bias, out 1500x1024x1024 +bias+residual, "
